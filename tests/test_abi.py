@@ -1,0 +1,149 @@
+"""CPU-only checks of the C-ABI library: it loads, exports every symbol the header
+declares, and its synchronous validation returns the documented status codes
+without launching anything (all calls below fail validation, or have nothing to
+do, before any HIP call is made; the pointers are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_attention_sequence_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, NULL, SHAPE, DTYPE, UNSUP, ALIAS, WS, LAUNCH, ALIGN = range(9)
+
+
+def header_symbols():
+    with open(os.path.join(ROOT, "include", "gdn.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(gdn_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gdn.LIB_PATH):
+        from linear_attention_sequence_amd import build
+        build.build()
+    return gdn.load()
+
+
+def test_header_lists_the_binding_exports():
+    assert header_symbols() == sorted(gdn.EXPORTS)
+
+
+def test_library_exports_every_header_symbol(lib):
+    for name in header_symbols():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version(lib):
+    for code in range(9):
+        assert lib.gdn_status_string(code)
+    assert lib.gdn_version() >= 10000
+
+
+def P(**kw):
+    d = dict(num_k_heads=16, num_v_heads=32, head_k_dim=128, head_v_dim=128, conv_kernel=4,
+             use_qk_l2norm=True, l2norm_eps=1e-6, in_dtype=gdn.GDN_BF16)
+    d.update(kw)
+    return ctypes.byref(gdn.GdnParams(**d).c())
+
+
+# fake, well-separated, 256-byte aligned device addresses: never dereferenced
+def A(i):
+    return ctypes.c_void_p(0x7f0000000000 + i * 0x100000000)
+
+
+def decode(lib, p, B=4, **over):
+    args = dict(qkv=A(1), gate=A(2), beta=A(3), w=A(4), cin=A(5), cout=A(6), S=A(7), o=A(8))
+    args.update(over)
+    return lib.gdn_decode_step(p, B, args["qkv"], args["gate"], args["beta"], args["w"],
+                               args["cin"], args["cout"], args["S"], args["o"], None)
+
+
+def test_param_validation(lib):
+    assert decode(lib, None) == NULL
+    assert decode(lib, P(in_dtype=7)) == DTYPE
+    assert decode(lib, P(num_k_heads=0)) == SHAPE
+    assert decode(lib, P(num_k_heads=3, num_v_heads=32)) == SHAPE      # Hv % Hk != 0
+    assert decode(lib, P(use_qk_l2norm=2)) == SHAPE
+    assert decode(lib, P(l2norm_eps=-1.0)) == SHAPE
+    assert decode(lib, P(l2norm_eps=float("nan"))) == SHAPE
+    assert decode(lib, P(head_k_dim=64, head_v_dim=64)) == UNSUP
+    assert decode(lib, P(head_k_dim=128, head_v_dim=16)) == UNSUP
+    assert decode(lib, P(conv_kernel=3)) == UNSUP
+
+
+def test_decode_validation(lib):
+    p = P()
+    assert decode(lib, p, B=-1) == SHAPE
+    assert decode(lib, p, B=0) == OK                  # nothing to do, nothing launched
+    for k in ("qkv", "gate", "beta", "w", "cin", "cout", "S", "o"):
+        assert decode(lib, p, **{k: None}) == NULL, k
+    assert decode(lib, p, cout=A(5)) == ALIAS          # conv_state_out == conv_state_in
+    assert decode(lib, p, o=A(7)) == ALIAS             # o inside S
+    assert decode(lib, p, S=ctypes.c_void_p(0x7f0000000004)) == ALIGN
+
+
+def test_verify_and_commit_validation(lib):
+    p = P()
+
+    def verify(B=4, T=4, S_in=A(7), S_snap=A(9), o=A(8)):
+        return lib.gdn_verify_block(p, B, T, A(1), A(2), A(3), A(4), A(5), S_in, S_snap, o, None)
+
+    assert verify(T=0) == SHAPE
+    assert verify(T=17) == UNSUP
+    assert verify(S_in=None) == NULL
+    assert verify(S_snap=A(7)) == ALIAS
+    assert verify(B=0) == OK
+
+    def commit(B=4, T=4, acc=A(10), cin=A(5), snap=A(9), cout=A(6), S_out=A(7)):
+        return lib.gdn_verify_commit(p, B, T, acc, A(1), cin, snap, cout, S_out, None)
+
+    assert commit(T=0) == SHAPE
+    assert commit(acc=None) == NULL
+    assert commit(cout=A(5)) == ALIAS
+    assert commit(S_out=A(9)) == ALIAS
+    assert commit(B=0) == OK
+
+
+def test_conv_validation(lib):
+    p = P()
+
+    def conv(B=2, L=8, cu=None, N=2, cin=A(5), cout=A(6), y=A(8)):
+        return lib.gdn_conv1d_silu(p, B, L, A(1), A(4), cin, cout, y, cu, N, None)
+
+    assert conv(N=3) == SHAPE                  # without cu_seqlens N must equal B
+    assert conv(cu=A(11), B=2) == SHAPE        # with cu_seqlens B must be 1
+    assert conv(L=-1) == SHAPE
+    assert conv(y=None) == NULL
+    assert conv(cout=A(5)) == ALIAS
+    assert conv(B=0, N=0) == OK
+
+
+def test_prefill_validation(lib):
+    p = P()
+    need = lib.gdn_prefill_workspace_size(p, 1, 4096, 1, 64)
+    assert need > 0
+    assert lib.gdn_prefill_workspace_size(p, 1, 4096, 1, 32) == 0   # chunk 32 unsupported
+    assert lib.gdn_prefill_workspace_size(None, 1, 4096, 1, 64) == 0
+
+    def prefill(B=1, L=4096, N=1, cu=None, chunk=64, ws=A(12), ws_bytes=need, S=A(7), o=A(8)):
+        return lib.gdn_prefill(p, B, L, A(1), A(2), A(3), A(4), A(5), A(6), S, o, cu, N, chunk,
+                               ws, ws_bytes, None)
+
+    assert prefill(chunk=32) == UNSUP
+    assert prefill(chunk=0) == SHAPE
+    assert prefill(N=2) == SHAPE
+    assert prefill(ws=None) == WS
+    assert prefill(ws_bytes=need - 1) == WS
+    assert prefill(ws=ctypes.c_void_p(0x7f0000000010 + 12 * 0x100000000)) == ALIGN
+    assert prefill(o=A(7)) == ALIAS
+    assert prefill(ws=A(8)) == ALIAS
+    assert prefill(B=2, N=2, cu=A(11)) == SHAPE
+    # ragged: B == 1 with N sequences; the workspace bound covers both packings
+    need_r = lib.gdn_prefill_workspace_size(p, 1, 4096, 8, 64)
+    assert need_r >= need
+    assert prefill(N=0, cu=A(11)) == OK

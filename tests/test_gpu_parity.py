@@ -1,0 +1,352 @@
+"""GPU parity: every entry point of libgdn.so against the fp64 oracle on the same
+seeded inputs, plus bit-exact GPU invariants. Needs an MI355X."""
+from __future__ import annotations
+
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import gdn_inputs as gi
+import linear_attention_sequence_amd as gdn
+import oracle
+from gpu_cases import TOL, dev, layer_inputs, oparams, params, rel_err, run_prefill
+
+pytestmark = pytest.mark.gpu
+
+SMALL128 = gi.Shape(Hk=2, Hv=4, dk=128, dv=128, K=4)   # d = 128 tiles, GQA factor 2
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gdn.load()
+    oracle.build_oracle(force=False)
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# conv1d + SiLU
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("shape,dtype,B,L", [(gi.TINY, "f32", 1, 64), (SMALL128, "bf16", 2, 300),
+                                             (gi.TINY_GQA, "f32", 3, 1)])
+def test_conv1d_silu(shape, dtype, B, L):
+    _say(f"conv1d_silu {shape} {dtype} B={B} L={L}")
+    inp = layer_inputs(shape, B, L, 7, dtype, conv_std=1.0)
+    p = params(shape, dtype)
+    y = torch.full((B, shape.D, L), float("nan"), device="cuda")
+    cout = torch.zeros_like(dev(inp["conv0"], dtype))
+    gdn.gdn_conv1d_silu(p, dev(inp["qkv"], dtype), dev(inp["w"], dtype), dev(inp["conv0"], dtype), cout, y)
+    torch.cuda.synchronize()
+    y_ref, c_ref = oracle.conv1d_silu(oparams(shape), inp["qkv"], inp["w"], inp["conv0"])
+    assert rel_err(y, y_ref) <= TOL[dtype]
+    assert np.array_equal(cout.float().cpu().numpy(), c_ref)
+
+
+def test_conv1d_silu_ragged():
+    shape, dtype = SMALL128, "bf16"
+    lens = [5, 0, 300, 1, 2]
+    cu = gi.cu_seqlens(lens)
+    Lt = int(cu[-1]) + 7   # 7 trailing tokens owned by no sequence stay untouched
+    inp = layer_inputs(shape, 1, Lt, 8, dtype, N=len(lens), conv_std=1.0)
+    p = params(shape, dtype)
+    y = torch.full((1, shape.D, Lt), 12345.0, device="cuda")
+    cout = torch.zeros_like(dev(inp["conv0"], dtype))
+    gdn.gdn_conv1d_silu(p, dev(inp["qkv"], dtype), dev(inp["w"], dtype), dev(inp["conv0"], dtype),
+                        cout, y, cu_seqlens=dev(cu))
+    torch.cuda.synchronize()
+    y_ref, c_ref = oracle.conv1d_silu(oparams(shape), inp["qkv"][:, :, :int(cu[-1])], inp["w"],
+                                      inp["conv0"], cu_seqlens=cu)
+    assert rel_err(y[:, :, :int(cu[-1])], y_ref) <= TOL[dtype]
+    assert torch.all(y[:, :, int(cu[-1]):] == 12345.0)
+    assert np.array_equal(cout.float().cpu().numpy(), c_ref)
+
+
+# ---------------------------------------------------------------------------
+# prefill, full comparison at small sizes (several chunks and a ragged tail)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("shape,dtype,B,L,s0", [
+    (gi.TINY, "f32", 1, 64, 0.0),
+    (gi.TINY_GQA, "f32", 2, 150, 0.1),
+    (SMALL128, "bf16", 1, 200, 0.1),
+    (SMALL128, "bf16", 2, 1, 0.1),
+    (SMALL128, "f32", 1, 129, 0.1),
+])
+def test_prefill_small(shape, dtype, B, L, s0):
+    _say(f"prefill {shape} {dtype} B={B} L={L}")
+    inp = layer_inputs(shape, B, L, 11, dtype, s0_std=s0, conv_std=1.0 if s0 else 0.0)
+    got = run_prefill(shape, dtype, inp)
+    ref = oracle.gdn_forward(oparams(shape), inp["qkv"], inp["gate"], inp["beta"], inp["w"],
+                             inp["conv0"], inp["S0"])
+    assert rel_err(got["o"], ref["o"]) <= TOL[dtype]
+    assert rel_err(got["S"], ref["S"]) <= TOL[dtype]
+    assert np.array_equal(got["conv_out"].float().cpu().numpy(), ref["conv_out"])
+
+
+def test_prefill_ragged_small():
+    shape, dtype = SMALL128, "bf16"
+    lens = [70, 0, 130, 1, 64]
+    cu = gi.cu_seqlens(lens)
+    inp = layer_inputs(shape, 1, int(cu[-1]), 12, dtype, N=len(lens), s0_std=0.1, conv_std=1.0)
+    got = run_prefill(shape, dtype, inp, cu=cu)
+    ref = oracle.gdn_forward(oparams(shape), inp["qkv"], inp["gate"], inp["beta"], inp["w"],
+                             inp["conv0"], inp["S0"], cu_seqlens=cu)
+    assert rel_err(got["o"], ref["o"]) <= TOL[dtype]
+    assert rel_err(got["S"], ref["S"]) <= TOL[dtype]
+    assert np.array_equal(got["conv_out"].float().cpu().numpy(), ref["conv_out"])
+
+
+def test_prefill_long_memory():
+    """Weak decay (gate scaled by 0.01) so early errors do not fade; beta near 1."""
+    shape, dtype = SMALL128, "bf16"
+    inp = layer_inputs(shape, 1, 512, 13, dtype, s0_std=0.1, conv_std=1.0)
+    inp["gate"] = gi.round_to(0.01 * inp["gate"].astype(np.float64), dtype)
+    inp["beta"] = gi.round_to(0.5 + 0.5 * inp["beta"].astype(np.float64), dtype)
+    got = run_prefill(shape, dtype, inp)
+    ref = oracle.gdn_forward(oparams(shape), inp["qkv"], inp["gate"], inp["beta"], inp["w"],
+                             inp["conv0"], inp["S0"])
+    assert rel_err(got["o"], ref["o"]) <= TOL[dtype]
+    assert rel_err(got["S"], ref["S"]) <= TOL[dtype]
+
+
+# ---------------------------------------------------------------------------
+# decode and verify, small
+# ---------------------------------------------------------------------------
+def _decode_steps(shape, dtype, inp, steps):
+    p = params(shape, dtype)
+    B = inp["qkv"].shape[0]
+    S = dev(inp["S0"])
+    cs = dev(inp["conv0"], dtype)
+    w = dev(inp["w"], dtype)
+    outs = []
+    for t in range(steps):
+        o = torch.empty((B, 1, shape.Hv, shape.dv), device="cuda")
+        cnew = torch.empty_like(cs)
+        gdn.gdn_decode_step(p, dev(inp["qkv"][:, :, t:t + 1], dtype), dev(inp["gate"][:, t:t + 1], dtype),
+                            dev(inp["beta"][:, t:t + 1], dtype), w, cs, cnew, S, o)
+        cs = cnew
+        outs.append(o)
+    torch.cuda.synchronize()
+    return torch.cat(outs, dim=1), S, cs
+
+
+@pytest.mark.parametrize("shape,dtype,B,steps", [(gi.TINY, "f32", 1, 64), (gi.TINY_GQA, "f32", 2, 16),
+                                                 (SMALL128, "bf16", 3, 20)])
+def test_decode_small(shape, dtype, B, steps):
+    _say(f"decode {shape} {dtype} B={B} steps={steps}")
+    inp = layer_inputs(shape, B, steps, 21, dtype, s0_std=0.1, conv_std=1.0)
+    o, S, cs = _decode_steps(shape, dtype, inp, steps)
+    ref = oracle.gdn_forward(oparams(shape), inp["qkv"], inp["gate"], inp["beta"], inp["w"],
+                             inp["conv0"], inp["S0"])
+    assert rel_err(o, ref["o"]) <= TOL[dtype]
+    assert rel_err(S, ref["S"]) <= TOL[dtype]
+    assert np.array_equal(cs.float().cpu().numpy(), ref["conv_out"])
+
+
+def _verify(shape, dtype, inp, S_in, cs, T):
+    p = params(shape, dtype)
+    B = inp["qkv"].shape[0]
+    snap = torch.empty((B, T, shape.Hv, shape.dk, shape.dv), device="cuda")
+    o = torch.empty((B, T, shape.Hv, shape.dv), device="cuda")
+    gdn.gdn_verify_block(p, dev(inp["qkv"], dtype), dev(inp["gate"], dtype), dev(inp["beta"], dtype),
+                         dev(inp["w"], dtype), cs, S_in, snap, o)
+    return snap, o
+
+
+@pytest.mark.parametrize("shape,dtype,B,blocks,T", [(gi.TINY, "f32", 1, 16, 4), (SMALL128, "bf16", 4, 3, 4),
+                                                    (gi.TINY_GQA, "f32", 3, 4, 1), (SMALL128, "bf16", 2, 2, 16)])
+def test_verify_commit_chain(shape, dtype, B, blocks, T):
+    """Blocks of T tokens; after each, commit a random accepted prefix and carry on
+    from it. The oracle replays exactly the committed tokens."""
+    _say(f"verify chain {shape} {dtype} B={B} blocks={blocks} T={T}")
+    p = params(shape, dtype)
+    op = oparams(shape)
+    base = layer_inputs(shape, B, 1, 31, dtype, s0_std=0.1, conv_std=1.0)
+    S = dev(base["S0"])
+    cs = dev(base["conv0"], dtype)
+    S_ref = base["S0"].astype(np.float64)
+    c_ref = base["conv0"].astype(np.float64)
+    for blk in range(blocks):
+        inp = layer_inputs(shape, B, T, 31, dtype, step=blk)
+        inp["w"] = base["w"]
+        snap, o = _verify(shape, dtype, inp, S, cs, T)
+        acc = gi.accept_len(B, T, 31 + blk)
+        S_new = torch.empty_like(S)
+        c_new = torch.empty_like(cs)
+        gdn.gdn_verify_commit(p, dev(acc), dev(inp["qkv"], dtype), cs, snap, c_new, S_new)
+        torch.cuda.synchronize()
+        ref = oracle.gdn_forward(op, inp["qkv"], inp["gate"], inp["beta"], inp["w"], c_ref, S_ref,
+                                 snapshots=True)
+        assert rel_err(o, ref["o"]) <= TOL[dtype]
+        assert rel_err(snap, ref["snap"]) <= TOL[dtype]
+        S_ref, c_ref = oracle.verify_commit(op, acc, inp["qkv"], c_ref, ref["snap"])
+        assert rel_err(S_new, S_ref) <= TOL[dtype]
+        assert np.array_equal(c_new.float().cpu().numpy(), c_ref)
+        S, cs = S_new, c_new
+
+
+def test_gqa_mapping_probe_exact():
+    """One token from a zero state, identity conv, beta = 1, gate = 0: o_h = (k.q) v_h
+    with k, q from K head h // f. K head j's key makes angle theta_j with its query, so
+    round(o_h / v_h) read back as an integer must name h // f for every h, exactly."""
+    shape, dtype = gi.Shape(Hk=4, Hv=16, dk=128, dv=128), "f32"
+    Hk, Hv, dk, dv, K, D = shape.Hk, shape.Hv, shape.dk, shape.dv, shape.K, shape.D
+    x = np.zeros((1, D, 1), np.float32)
+    for j in range(Hk):
+        x[0, j * dk, 0] = 4.0                    # q of head j along e0
+        x[0, Hk * dk + j * dk, 0] = 4.0          # k of head j: direction (1, j+1) scaled
+        x[0, Hk * dk + j * dk + 1, 0] = 4.0 * (j + 1)
+    x[0, 2 * Hk * dk:, 0] = 1.0                  # v = silu(1) everywhere
+    w = np.zeros((D, 1, K), np.float32)
+    w[:, 0, K - 1] = 1.0
+    p = params(shape, dtype)
+    inp = {"qkv": x, "gate": np.zeros((1, 1, Hv), np.float32), "beta": np.ones((1, 1, Hv), np.float32),
+           "w": w, "conv0": np.zeros((1, D, K - 1), np.float32), "S0": np.zeros((1, Hv, dk, dv), np.float32)}
+    got = run_prefill(shape, dtype, inp)
+    ref = oracle.gdn_forward(oparams(shape), inp["qkv"], inp["gate"], inp["beta"], inp["w"],
+                             inp["conv0"], inp["S0"])
+    silu1 = 1.0 / (1.0 + np.exp(-1.0))
+    # (k.q) sqrt(dk) = cos(theta_j) identifies head j; map it back to j
+    cos = got["o"][0, 0, :, 0].double().cpu().numpy() * np.sqrt(dk) / silu1
+    cos_ref = ref["o"][0, 0, :, 0] * np.sqrt(dk) / silu1
+
+    def head_of(c):
+        # silu(4 (j+1)) / silu(4) ~ (j+1): the k direction is (1, ~j+1) up to SiLU
+        return np.rint(np.sqrt(np.maximum(1.0 / np.maximum(c, 1e-9) ** 2 - 1.0, 0.0)) - 1.0).astype(int)
+    assert np.array_equal(head_of(cos), np.arange(Hv) // (Hv // Hk))
+    assert np.array_equal(head_of(cos), head_of(cos_ref))
+    # decode and verify use their own indexing: same probe through both
+    o_dec = torch.empty((1, 1, Hv, dv), device="cuda")
+    S = torch.zeros((1, Hv, dk, dv), device="cuda")
+    cz = torch.zeros((1, D, K - 1), device="cuda")
+    gdn.gdn_decode_step(p, dev(x), dev(inp["gate"]), dev(inp["beta"]), dev(w), cz, torch.empty_like(cz), S, o_dec)
+    torch.cuda.synchronize()
+    assert np.array_equal(head_of(o_dec[0, 0, :, 0].double().cpu().numpy() * np.sqrt(dk) / silu1),
+                          np.arange(Hv) // (Hv // Hk))
+
+
+# ---------------------------------------------------------------------------
+# bit-exact GPU invariants
+# ---------------------------------------------------------------------------
+def test_verify_snapshots_equal_decode_steps_bitexact():
+    shape, dtype, B, T = SMALL128, "bf16", 5, 6
+    inp = layer_inputs(shape, B, T, 41, dtype, s0_std=0.1, conv_std=1.0)
+    S0 = dev(inp["S0"])
+    snap, o_v = _verify(shape, dtype, inp, S0, dev(inp["conv0"], dtype), T)
+    o_d, S_d, _ = _decode_steps(shape, dtype, inp, T)
+    torch.cuda.synchronize()
+    assert torch.equal(o_v, o_d)
+    assert torch.equal(snap[:, -1], S_d)
+    # every intermediate snapshot too
+    S = dev(inp["S0"])
+    cs = dev(inp["conv0"], dtype)
+    p = params(shape, dtype)
+    for t in range(T):
+        o = torch.empty((B, 1, shape.Hv, shape.dv), device="cuda")
+        cn = torch.empty_like(cs)
+        gdn.gdn_decode_step(p, dev(inp["qkv"][:, :, t:t + 1], dtype), dev(inp["gate"][:, t:t + 1], dtype),
+                            dev(inp["beta"][:, t:t + 1], dtype), dev(inp["w"], dtype), cs, cn, S, o)
+        cs = cn
+        torch.cuda.synchronize()
+        assert torch.equal(snap[:, t], S)
+
+
+def test_beta0_gate0_keeps_state_bitexact():
+    shape, dtype, B = SMALL128, "bf16", 3
+    inp = layer_inputs(shape, B, 1, 42, dtype, s0_std=0.1, conv_std=1.0)
+    p = params(shape, dtype)
+    S = dev(inp["S0"])
+    S_before = S.clone()
+    o = torch.empty((B, 1, shape.Hv, shape.dv), device="cuda")
+    z = torch.zeros((B, 1, shape.Hv), device="cuda", dtype=torch.bfloat16)
+    cs = dev(inp["conv0"], dtype)
+    gdn.gdn_decode_step(p, dev(inp["qkv"], dtype), z, z, dev(inp["w"], dtype), cs, torch.empty_like(cs), S, o)
+    torch.cuda.synchronize()
+    assert torch.equal(S, S_before)
+    ref = oracle.gdn_forward(oparams(shape), inp["qkv"], np.zeros((B, 1, shape.Hv)), np.zeros((B, 1, shape.Hv)),
+                             inp["w"], inp["conv0"], inp["S0"])
+    assert rel_err(o, ref["o"]) <= TOL[dtype]
+
+
+def test_prefill_deterministic_and_ragged_equals_separate():
+    shape, dtype = SMALL128, "bf16"
+    lens = [100, 3, 64, 0, 65]
+    cu = gi.cu_seqlens(lens)
+    inp = layer_inputs(shape, 1, int(cu[-1]), 43, dtype, N=len(lens), s0_std=0.1, conv_std=1.0)
+    a = run_prefill(shape, dtype, inp, cu=cu)
+    b = run_prefill(shape, dtype, inp, cu=cu)
+    for k in ("o", "S", "conv_out"):
+        assert torch.equal(a[k], b[k]), k
+    for n in range(len(lens)):
+        s, e = int(cu[n]), int(cu[n + 1])
+        one = {"qkv": inp["qkv"][:, :, s:e], "gate": inp["gate"][:, s:e], "beta": inp["beta"][:, s:e],
+               "w": inp["w"], "conv0": inp["conv0"][n:n + 1], "S0": inp["S0"][n:n + 1]}
+        r = run_prefill(shape, dtype, one)
+        assert torch.equal(r["o"][0], a["o"][0, s:e])
+        assert torch.equal(r["S"][0], a["S"][n])
+        assert torch.equal(r["conv_out"][0], a["conv_out"][n])
+
+
+def test_prefill_split_carry():
+    """prefill(L) == prefill(L1) then prefill(L - L1) with both states carried."""
+    shape, dtype = SMALL128, "bf16"
+    inp = layer_inputs(shape, 1, 300, 44, dtype, s0_std=0.1, conv_std=1.0)
+    full = run_prefill(shape, dtype, inp)
+    first = {k: v for k, v in inp.items()}
+    first.update(qkv=inp["qkv"][:, :, :77], gate=inp["gate"][:, :77], beta=inp["beta"][:, :77])
+    r1 = run_prefill(shape, dtype, first)
+    second = {"qkv": inp["qkv"][:, :, 77:], "gate": inp["gate"][:, 77:], "beta": inp["beta"][:, 77:],
+              "w": inp["w"], "conv0": r1["conv_out"].float().cpu().numpy(), "S0": r1["S"].cpu().numpy()}
+    r2 = run_prefill(shape, dtype, second)
+    ref_o = full["o"].double().cpu().numpy()
+    assert rel_err(torch.cat([r1["o"], r2["o"]], dim=1), ref_o) <= TOL[dtype]
+    assert rel_err(r2["S"], full["S"].double().cpu().numpy()) <= TOL[dtype]
+    assert torch.equal(r2["conv_out"], full["conv_out"])
+
+
+def test_empty_calls_launch_nothing():
+    shape, dtype = SMALL128, "bf16"
+    p = params(shape, dtype)
+    inp = layer_inputs(shape, 1, 0, 45, dtype, s0_std=0.1)
+    got = run_prefill(shape, dtype, inp)   # L = 0: S and the conv window come back unchanged
+    assert torch.equal(got["S"].cpu(), torch.from_numpy(inp["S0"]))
+    assert torch.equal(got["conv_out"].float().cpu(), torch.from_numpy(inp["conv0"]))
+    e = torch.empty(0, device="cuda")
+    gdn.gdn_decode_step(p, e.reshape(0, shape.D, 1).bfloat16(), e.reshape(0, 1, 4).bfloat16(),
+                        e.reshape(0, 1, 4).bfloat16(), torch.zeros((shape.D, 1, 4), device="cuda").bfloat16(),
+                        e.reshape(0, shape.D, 3).bfloat16(), e.reshape(0, shape.D, 3).bfloat16(),
+                        e.reshape(0, 4, 128, 128), e.reshape(0, 1, 4, 128))
+
+
+def test_calls_never_synchronise():
+    """Enqueue a long chain of matmuls, then the library calls: each must return
+    while the chain is still running (it only enqueues)."""
+    shape, dtype, B = SMALL128, "bf16", 4
+    inp = layer_inputs(shape, B, 64, 46, dtype, s0_std=0.1, conv_std=1.0)
+    p = params(shape, dtype)
+    args = {k: dev(v, dtype if k not in ("S0",) else None) for k, v in inp.items()}
+    ws = gdn.prefill_workspace(p, B, 64, B)
+    o = torch.empty((B, 64, shape.Hv, shape.dv), device="cuda")
+    cout = torch.empty_like(args["conv0"])
+    snap = torch.empty((B, 4, shape.Hv, 128, 128), device="cuda")
+    a = torch.randn(4096, 4096, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(60):
+        a = a @ a
+        a = a / a.norm()
+    t0 = time.perf_counter()
+    gdn.gdn_prefill(p, args["qkv"], args["gate"], args["beta"], args["w"], args["conv0"], cout,
+                    args["S0"], o, ws)
+    gdn.gdn_verify_block(p, args["qkv"][:, :, :4].contiguous(), args["gate"][:, :4].contiguous(),
+                         args["beta"][:, :4].contiguous(), args["w"], args["conv0"], args["S0"], snap,
+                         o[:, :4].contiguous())
+    t1 = time.perf_counter()
+    pending = not torch.cuda.current_stream().query()
+    torch.cuda.synchronize()
+    assert pending, "the matmul chain drained before the library calls returned"
+    assert t1 - t0 < 0.05
