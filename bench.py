@@ -1,0 +1,332 @@
+"""Benchmark of the Gated DeltaNet layer on one MI355X.
+
+Default workload: the decode step at B = 64 sequences, 16 K/Q heads expanded to
+32 V heads, d_k = d_v = 128, conv K = 4, bf16 inputs, fp32 state [64,32,128,128]
+(~N(0, 0.1)) and conv state, 256 consecutive steps with fresh inputs per step.
+A "step" is one gdn_decode_step call (conv + SiLU, split, GQA, L2 norm, scale,
+one recurrence step for every (sequence, V head)).
+
+Timing: W untimed warm-up steps, then exactly K steps bracketed by
+torch.cuda.synchronize(); inputs are resident in HBM before the clock starts.
+Cold-cache mode: 4 independent state replicas rotate, so the 128 MiB state a
+step reads was last touched 4 steps (512 MiB of state) earlier and cannot sit
+in the 256 MB Infinity Cache; this is the reported value. With --warm the
+warm-cache rate (one replica) is timed too. Every kernel launch in the timed region is
+bracketed by HIP events on the launch stream for the per-kernel duration used
+by the roofline.
+
+Other workloads (--workload verify | prefill | ragged | commit) time the other
+entry points on their configurations; they print the same kind of JSON line.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Gated DeltaNet tokens/s + % roofline (decode HBM GB/s; prefill MFMA util)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "linear_attention_sequence_amd", "csrc")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_digest(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_counters(name, digest, launches_bytes_unit=1):
+    """HBM bytes per launch from committed rocprofv3 --pmc counters, scaled by the
+    copy-kernel calibration taken in the same runs; None when absent or stale."""
+    path = os.path.join(PROFILES, f"{name}_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        c = json.load(f)
+    if c.get("source_digest") != digest:
+        return None
+    fetch = c["fetch_kib_per_dispatch"] * 1024.0 * c["copy_read_bytes"] / (c["copy_fetch_kib"] * 1024.0)
+    write = c["write_kib_per_dispatch"] * 1024.0 * c["copy_write_bytes"] / (c["copy_write_kib"] * 1024.0)
+    return fetch + write
+
+
+def run_timed(torch, step_fn, steps, warmup):
+    """W untimed steps, then K timed steps launched back to back. A HIP event
+    pair on the launch stream brackets the K launches (no event between them,
+    so nothing is inserted into the pipeline); the per-launch duration is the
+    bracketed time / K. Wall time comes from the host clock around the same
+    region, with a synchronize on both sides."""
+    for i in range(warmup):
+        step_fn(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(steps):
+        step_fn(warmup + i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, e0.elapsed_time(e1) / steps
+
+
+# ---------------------------------------------------------------------------
+# decode (default)
+# ---------------------------------------------------------------------------
+def bench_decode(args, torch, gdn, gi):
+    sh, w_ = gi.QWEN, gi.WORKLOADS[1]
+    seed, B, NSTEP = w_.seed, gi.DECODE_B, gi.DECODE_STEPS
+    p = gdn.GdnParams(sh.Hk, sh.Hv, sh.dk, sh.dv, sh.K, True, 1e-6, gdn.GDN_BF16)
+    dev = lambda a, bf=True: (torch.from_numpy(a).cuda().to(torch.bfloat16) if bf else torch.from_numpy(a).cuda())
+    log("generating decode inputs ...")
+    xs = [dev(gi.qkv(sh, B, 1, seed, "bf16", step=s)) for s in range(NSTEP)]
+    gs = [dev(gi.gate(sh, B, 1, seed, "bf16", step=s)) for s in range(NSTEP)]
+    bs = [dev(gi.beta(sh, B, 1, seed, "bf16", step=s)) for s in range(NSTEP)]
+    w = dev(gi.conv_weight(sh, seed, "bf16"))
+    S0 = dev(gi.state0(sh, B, seed, 0.1), bf=False)
+    c0 = dev(gi.conv_state0(sh, B, seed, 1.0, "bf16"))
+    o = torch.empty((B, 1, sh.Hv, sh.dv), device="cuda")
+
+    def make(replicas):
+        S = [S0.clone() for _ in range(replicas)]
+        conv = [[c0.clone(), torch.empty_like(c0)] for _ in range(replicas)]
+        par = [0] * replicas
+
+        def step(i):
+            r = i % replicas
+            ci, co = conv[r][par[r]], conv[r][1 - par[r]]
+            j = i % NSTEP
+            gdn.gdn_decode_step(p, xs[j], gs[j], bs[j], w, ci, co, S[r], o)
+            par[r] ^= 1
+        return step
+
+    wall, kms = run_timed(torch, make(4), args.steps, args.warmup)
+    bytes_step = (B * sh.Hv * sh.dk * sh.dv * 4 * 2          # S read + write
+                  + B * sh.D * 2                              # qkv
+                  + B * sh.D * (sh.K - 1) * 2 * 2             # conv state read + write
+                  + sh.D * sh.K * 2                           # conv weight
+                  + B * sh.Hv * 2 * 2                         # gate, beta
+                  + B * sh.Hv * sh.dv * 4)                    # o
+    achieved = bytes_step / (kms * 1e-3) / 1e9
+    digest = source_digest(["gdn_recurrent.hip", "gdn_common.hpp"])
+    traffic = traffic_from_counters("decode_B64_d128", digest)
+    res = {
+        "metric": METRIC, "value": B * args.steps / wall, "unit": "tokens/s",
+        "ms_per_step": 1e3 * wall / args.steps,
+        "config": {"workload": w_.name, "B": B, "Hk": sh.Hk, "Hv": sh.Hv, "dk": sh.dk, "dv": sh.dv,
+                   "conv_K": sh.K, "inputs": "bf16", "state": "fp32",
+                   "cache": "cold: 4 rotating state replicas"},
+        "dtype": "f32",
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "recurrent_kernel (decode)", "algorithmic_bytes_per_launch": bytes_step,
+                     "avg_kernel_us": kms * 1e3},
+    }
+    if args.warm:
+        wall_w, kms_w = run_timed(torch, make(1), args.steps, args.warmup)
+        res["warm"] = {"value": B * args.steps / wall_w, "ms_per_step": 1e3 * wall_w / args.steps,
+                       "avg_kernel_us": kms_w * 1e3,
+                       "achieved_GBs": bytes_step / (kms_w * 1e-3) / 1e9}
+    if args.cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_decode(gi, sh, seed, B)
+    return res
+
+
+def cpu_baseline_decode(gi, sh, seed, B, budget_s=12.0):
+    """The fp64 oracle, unmodified, on decode steps of the same workload (all 64
+    sequences, all heads), one step per call with both states carried, until
+    about budget_s seconds of CPU work have run."""
+    import oracle
+    op = oracle.OracleParams.of(sh)
+    nthreads = min(oracle.default_threads(), 16)
+    S = gi.state0(sh, B, seed, 0.1).astype(np.float64)
+    c = gi.conv_state0(sh, B, seed, 1.0, "bf16").astype(np.float64)
+    w = gi.conv_weight(sh, seed, "bf16")
+    done, el = 0, 0.0
+    while el < budget_s and done < gi.DECODE_STEPS:
+        x = gi.qkv(sh, B, 1, seed, "bf16", step=done)
+        g = gi.gate(sh, B, 1, seed, "bf16", step=done)
+        b = gi.beta(sh, B, 1, seed, "bf16", step=done)
+        t0 = time.perf_counter()
+        r = oracle.gdn_forward(op, x, g, b, w, c, S, nthreads=nthreads)
+        el += time.perf_counter() - t0
+        S, c = r["S"], r["conv_out"]
+        done += 1
+    return {"value": B * done / el, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"{done} consecutive decode steps of the same workload (B={B}, all 32 V heads), "
+                      f"{el:.1f} s of oracle time"}
+
+
+# ---------------------------------------------------------------------------
+# verify (B = 128, T = 4) and commit
+# ---------------------------------------------------------------------------
+def bench_verify(args, torch, gdn, gi, commit=False):
+    sh, w_ = gi.QWEN, gi.WORKLOADS[4]
+    seed, B, T = w_.seed, gi.VERIFY_B, gi.VERIFY_T
+    p = gdn.GdnParams(sh.Hk, sh.Hv, sh.dk, sh.dv, sh.K, True, 1e-6, gdn.GDN_BF16)
+    dev = lambda a, bf=True: (torch.from_numpy(a).cuda().to(torch.bfloat16) if bf else torch.from_numpy(a).cuda())
+    x = dev(gi.qkv(sh, B, T, seed, "bf16"))
+    g = dev(gi.gate(sh, B, T, seed, "bf16"))
+    b = dev(gi.beta(sh, B, T, seed, "bf16"))
+    w = dev(gi.conv_weight(sh, seed, "bf16"))
+    S_in = dev(gi.state0(sh, B, seed, 0.1), bf=False)
+    c0 = dev(gi.conv_state0(sh, B, seed, 1.0, "bf16"))
+    acc = torch.from_numpy(gi.accept_len(B, T, seed)).cuda()
+    snap = torch.empty((B, T, sh.Hv, sh.dk, sh.dv), device="cuda")
+    o = torch.empty((B, T, sh.Hv, sh.dv), device="cuda")
+    S_out = torch.empty_like(S_in)
+    c_out = torch.empty_like(c0)
+    gdn.gdn_verify_block(p, x, g, b, w, c0, S_in, snap, o)
+
+    def step(i):
+        if commit:
+            gdn.gdn_verify_commit(p, acc, x, c0, snap, c_out, S_out)
+        else:
+            gdn.gdn_verify_block(p, x, g, b, w, c0, S_in, snap, o)
+
+    wall, kms = run_timed(torch, step, args.steps, args.warmup)
+    tile = sh.dk * sh.dv * 4
+    if commit:
+        nbytes = B * sh.Hv * tile * 2 + B * 4 + B * sh.D * (sh.K - 1) * 2 * 2 + B * sh.D * T * 2
+        name, kern = "verify_commit_B128_T4_d128", "commit_kernel"
+    else:
+        nbytes = (B * sh.Hv * tile * (1 + T) + B * sh.D * T * 2 + B * sh.D * (sh.K - 1) * 2
+                  + sh.D * sh.K * 2 + B * T * sh.Hv * 2 * 2 + B * T * sh.Hv * sh.dv * 4)
+        name, kern = w_.name, "recurrent_kernel (verify, T=4)"
+    achieved = nbytes / (kms * 1e-3) / 1e9
+    return {
+        "metric": METRIC, "value": (B if commit else B * T) * args.steps / wall, "unit": "tokens/s",
+        "ms_per_step": 1e3 * wall / args.steps,
+        "config": {"workload": name, "B": B, "T": T, "Hk": sh.Hk, "Hv": sh.Hv, "dk": sh.dk, "dv": sh.dv,
+                   "cache": "single working set of >1.3 GB (no rotation needed)"},
+        "dtype": "f32",
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": kern,
+                     "algorithmic_bytes_per_launch": nbytes, "avg_kernel_us": kms * 1e3},
+    }
+
+
+# ---------------------------------------------------------------------------
+# prefill (L = 4096) and ragged prefill (8 sequences)
+# ---------------------------------------------------------------------------
+PREFILL_FLOP_PER_TOKEN_HEAD = 163840   # bf16-MFMA-shaped work of the chunked form, C = 64, d = 128
+
+
+def bench_prefill(args, torch, gdn, gi, ragged=False):
+    sh = gi.QWEN
+    w_ = gi.WORKLOADS[3 if ragged else 2]
+    seed = w_.seed
+    if ragged:
+        lens = gi.seq_lens(gi.RAGGED_N, gi.RAGGED_LO, gi.RAGGED_HI, seed)
+        cu_np = gi.cu_seqlens(lens)
+        L, N = int(cu_np[-1]), gi.RAGGED_N
+    else:
+        L, N = gi.PREFILL_L, 1
+    p = gdn.GdnParams(sh.Hk, sh.Hv, sh.dk, sh.dv, sh.K, True, 1e-6, gdn.GDN_BF16)
+    dev = lambda a: torch.from_numpy(a).cuda().to(torch.bfloat16)
+    reps = 1 if ragged else 4   # 64 MiB of qkv per call: 4 replicas exceed the 256 MB cache
+    xs = [dev(gi.qkv(sh, 1, L, seed + 100 * r, "bf16")) for r in range(reps)]
+    g = dev(gi.gate(sh, 1, L, seed, "bf16"))
+    b = dev(gi.beta(sh, 1, L, seed, "bf16"))
+    w = dev(gi.conv_weight(sh, seed, "bf16"))
+    c0 = torch.zeros((N, sh.D, sh.K - 1), device="cuda", dtype=torch.bfloat16)
+    c_out = torch.empty_like(c0)
+    S = torch.zeros((N, sh.Hv, sh.dk, sh.dv), device="cuda")
+    o = torch.empty((1, L, sh.Hv, sh.dv), device="cuda")
+    cu = torch.from_numpy(cu_np).cuda() if ragged else None
+    ws = gdn.prefill_workspace(p, 1, L, N)
+
+    def step(i):
+        # the state is carried in place, so each call continues from the last one's
+        # final state: the work per call is the same whatever S holds
+        gdn.gdn_prefill(p, xs[i % reps], g, b, w, c0, c_out, S, o, ws, cu_seqlens=cu)
+
+    wall, kms = run_timed(torch, step, args.steps, args.warmup)
+    flops = PREFILL_FLOP_PER_TOKEN_HEAD * L * sh.Hv
+    achieved = flops / (kms * 1e-3) / 1e12
+    return {
+        "metric": METRIC, "value": L * args.steps / wall, "unit": "tokens/s",
+        "ms_per_step": 1e3 * wall / args.steps,
+        "config": {"workload": w_.name, "L_total": L, "N": N, "Hk": sh.Hk, "Hv": sh.Hv, "dk": sh.dk,
+                   "dv": sh.dv, "chunk": 64, "cache": f"{reps} input replicas"},
+        "dtype": "f32",
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "gdn_prefill (all kernels of one call)",
+                     "algorithmic_flops_per_call": flops, "avg_call_us": kms * 1e3},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "verify", "commit", "prefill", "ragged"])
+    ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
+    ap.add_argument("--warm", action="store_true",
+                    help="decode: also time the warm-cache rate (one state replica)")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="first run one plain 256 MiB device copy (reads and writes 268435456 B), "
+                         "so that HBM counters can be scaled by a kernel of known traffic")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the layer's path is built and measured on a single "
+              f"MI355X (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    defaults = {"decode": (256, 32), "verify": (50, 5), "commit": (50, 5), "prefill": (20, 3),
+                "ragged": (10, 2)}[args.workload]
+    args.steps = defaults[0] if args.steps is None else args.steps
+    args.warmup = defaults[1] if args.warmup is None else args.warmup
+    if args.workload != "decode":
+        args.cpu_baseline = False
+
+    import torch
+    import gdn_inputs as gi
+    import linear_attention_sequence_amd as gdn
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    gdn.load()
+    if args.calibration_copy:
+        src = torch.ones(64 << 20, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    fn = {"decode": bench_decode, "verify": bench_verify,
+          "commit": lambda a, t, g, i: bench_verify(a, t, g, i, commit=True),
+          "prefill": bench_prefill,
+          "ragged": lambda a, t, g, i: bench_prefill(a, t, g, i, ragged=True)}[args.workload]
+    res = fn(args, torch, gdn, gi)
+    out = {"metric": res.pop("metric"), "value": res.pop("value"), "unit": res.pop("unit"),
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": res.pop("ms_per_step"), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": res.pop("dtype"), "data": "synthetic (seeded)",
+           "config": res.pop("config")}
+    out.update(res)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

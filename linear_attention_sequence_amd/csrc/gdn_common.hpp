@@ -9,6 +9,9 @@ namespace gdn {
 constexpr int kConvK = 4;   // conv taps supported by the kernels
 constexpr int kWave = 64;   // CDNA wavefront width
 
+// Native 4 x fp32 vector (the form the nontemporal builtins accept).
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 // Input storage types. bf16 is carried as raw bits; widening to fp32 is exact.
 struct bf16_t { uint16_t bits; };
 
