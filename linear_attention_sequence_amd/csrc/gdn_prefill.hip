@@ -1,5 +1,8 @@
 // Chunked prefill of the Gated DeltaNet layer ("MNN Model Support: Qwen3.5",
 // §1.2 steps 1-5 over a whole prompt, §1.3 reverse GQA, §1.4 carried states).
+// This file holds the fp32 vector-ALU version, used for fp32 inputs and for
+// head dim 16; bf16 inputs at head dim 128 run on MFMA (gdn_prefill_mfma.hip)
+// with the same chunk algebra.
 //
 // Step 5 is evaluated chunk by chunk (chunk length C). Inside a chunk, with
 // Gam_t the inclusive cumulative sum of the log-decays g and S0 the state on
@@ -75,10 +78,16 @@ static PrefillWs ws_layout(void* base, int B, int L, int N, int Hk, int Hv, int 
 }
 
 size_t prefill_workspace_bytes(int B, int L, int N, int Hk, int Hv, int d, int chunk) {
-    // sized for the ragged layout, which bounds the plain one too
+    // sized for the ragged layout and the plain one, and at d = 128 for both the
+    // MFMA path (bf16 inputs) and the fp32 path (fp32 inputs)
     const size_t a = ws_layout(nullptr, B, L, N, Hk, Hv, d, chunk, true).bytes;
     const size_t b = ws_layout(nullptr, B, L, N, Hk, Hv, d, chunk, false).bytes;
-    return a > b ? a : b;
+    size_t m = a > b ? a : b;
+    if (d == 128) {
+        const size_t c = prefill_mfma_workspace_bytes(B, L, N, Hk, Hv);
+        m = c > m ? c : m;
+    }
+    return m;
 }
 
 // Number of chunks of sequence n.
@@ -407,9 +416,12 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, int in_dtype, hipStream
 
 hipError_t launch_prefill(const PrefillArgs& a, int in_dtype, int d, hipStream_t stream) {
     if (a.chunk != 64) return hipErrorInvalidValue;
-    if (d == 128)
-        return in_dtype == 1 ? launch_prefill_t<bf16_t, 128>(a, in_dtype, stream)
+    // bf16 inputs run the dense products on fp16 MFMA (within the bf16 error
+    // budget); fp32 inputs keep every operation in fp32 on the vector ALUs.
+    if (d == 128) {
+        return in_dtype == 1 ? launch_prefill_mfma(a, in_dtype, stream)
                              : launch_prefill_t<float, 128>(a, in_dtype, stream);
+    }
     return in_dtype == 1 ? launch_prefill_t<bf16_t, 16>(a, in_dtype, stream)
                          : launch_prefill_t<float, 16>(a, in_dtype, stream);
 }

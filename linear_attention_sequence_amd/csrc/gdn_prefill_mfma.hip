@@ -1,0 +1,847 @@
+// Chunked prefill of the Gated DeltaNet layer on MFMA, d_k = d_v = 128
+// ("MNN Model Support: Qwen3.5", §1.2 steps 1-5 over whole prompts, §1.3
+// reverse GQA, §1.4 carried states).
+//
+// The chunk algebra is the one stated in gdn_prefill.hip (an exact rewrite of
+// step 5 over chunks of C = 64 tokens). Here the dense products run on
+// v_mfma_f32_16x16x32_f16 (fp16 operands, fp32 accumulation); the state S,
+// the triangular solve and every accumulation stay fp32. Operands whose scale
+// is set by the data (the state S, the values v, U and the deltas) are brought
+// into fp16's range with a power-of-two scale chosen per wave or per chunk
+// (exact to apply and to undo); q and k are unit-norm and P, W are bounded by
+// them.
+//
+//   front_kernel   steps 1-4 on a (64-token, 128-channel) tile: coalesced
+//                  channel-major loads, conv + SiLU, transpose through LDS,
+//                  per-token L2 norms and the q scale; fp16 token-major q, k, v.
+//   chunk_kernel   per (chunk, V head), all chunks in parallel: Gam (cumulative
+//                  log-decay), the Gram matrices K K^T and Q K^T on MFMA,
+//                  A and P, T = (I + A)^-1 by a blocked fp32 inverse (16 x 16
+//                  diagonal blocks by substitution, off-diagonal blocks by
+//                  block products), then W = T diag(beta exp(Gam)) K and
+//                  U = T diag(beta) V on MFMA. Writes W, U, P, Gam and a
+//                  transposed copy of the chunk's keys.
+//   carry_kernel   per (sequence, V head): the state lives in registers in MFMA
+//                  accumulator layout (each of the 4 waves owns 32 of the 128
+//                  columns; the columns of S evolve independently); chunk by
+//                  chunk it forms Delta = U - W S, O = diag(exp(Gam)) Q S +
+//                  P Delta and S = exp(Gam_last) S + K^T diag(exp(Gam_last -
+//                  Gam)) Delta. The next chunk's operands stream into the other
+//                  half of a double-buffered LDS stage with global_load_lds
+//                  while the current chunk computes. Accumulator tiles are fed
+//                  back as B operands without data movement by pairing the k
+//                  slots of the MFMA with the accumulator rows they hold.
+#include "gdn_common.hpp"
+#include "gdn_launch.hpp"
+#include "gdn_mfma.hpp"
+
+namespace gdn {
+namespace pf2 {
+
+constexpr int C = 64;      // chunk length
+constexpr int D = 128;     // head dim (dk == dv)
+constexpr int TT = 64;     // front-end tile (tokens)
+constexpr int RAW = TT + 5;  // raw tile row stride (floats): 67 used, odd-ish stride against bank conflicts
+// per (chunk, V head) coefficients: [0, C) exp(Gam_t); [C, 2C) exp(Gam_last - Gam_t);
+// 2C: exp(Gam_last); 2C + 1: 2^uexp, the scale of the stored U; padded to 40 granules
+constexpr int COEF = 160;
+
+struct Ws {
+    _Float16* qh;   // [Ttot, Hk, D] q_hat (normalised, scaled)
+    _Float16* kh;   // [Ttot, Hk, D] k_hat
+    _Float16* vh;   // [Ttot, Hv, D] v
+    _Float16* W;    // [NC, Hv, C, D]
+    _Float16* U;    // [NC, Hv, C, D] scaled by 2^-uexp
+    _Float16* P;    // [NC, Hv, C, C]
+    _Float16* KT;   // [NC, Hk, D, C]  keys of the chunk, transposed
+    float* coef;    // [NC, Hv, COEF]: exp(Gam_t), exp(Gam_last - Gam_t), exp(Gam_last), 2^uexp
+    int nc_max;
+    size_t bytes;
+};
+
+static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+static int max_chunks(int B, int L, int N, bool ragged) {
+    const int per = (L + C - 1) / C;
+    return ragged ? per + N : B * per;
+}
+
+static Ws layout(void* base, int B, int L, int N, int Hk, int Hv, bool ragged) {
+    Ws w;
+    const size_t T = static_cast<size_t>(B) * L;
+    const size_t nc = static_cast<size_t>(max_chunks(B, L, N, ragged));
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        void* r = base ? static_cast<char*>(base) + off : nullptr;
+        off = align256(off + bytes);
+        return r;
+    };
+    w.qh = static_cast<_Float16*>(take(T * Hk * D * 2));
+    w.kh = static_cast<_Float16*>(take(T * Hk * D * 2));
+    w.vh = static_cast<_Float16*>(take(T * Hv * D * 2));
+    w.W = static_cast<_Float16*>(take(nc * Hv * C * D * 2));
+    w.U = static_cast<_Float16*>(take(nc * Hv * C * D * 2));
+    w.P = static_cast<_Float16*>(take(nc * Hv * C * C * 2));
+    w.KT = static_cast<_Float16*>(take(nc * Hk * D * C * 2));
+    w.coef = static_cast<float*>(take(nc * Hv * COEF * 4));
+    w.nc_max = static_cast<int>(nc);
+    w.bytes = off;
+    return w;
+}
+
+__device__ __forceinline__ int chunks_of(const Seg& s) { return (s.len + C - 1) / C; }
+
+__device__ __forceinline__ bool find_chunk(int id, const PrefillArgs& a, int* n_out, int* c_out, Seg* seg) {
+    int acc = 0;
+    for (int n = 0; n < a.N; ++n) {
+        const Seg s = segment_of(n, a.L, a.cu);
+        const int nc = chunks_of(s);
+        if (id < acc + nc) { *n_out = n; *c_out = id - acc; *seg = s; return true; }
+        acc += nc;
+    }
+    return false;
+}
+
+// Sequence owning token p of a row (clamped cu_seqlens), or -1.
+__device__ __forceinline__ int owner_of(int p, int row, const PrefillArgs& a, int* start) {
+    if (a.cu == nullptr) { *start = 0; return row; }
+    int lo = 0, hi = a.N - 1, n = -1;
+    while (lo <= hi) {
+        const int mid = (lo + hi) >> 1;
+        int st = a.cu[mid];
+        st = st < 0 ? 0 : (st > a.L ? a.L : st);
+        if (st <= p) { n = mid; lo = mid + 1; } else { hi = mid - 1; }
+    }
+    if (n < 0) return -1;
+    const Seg sg = segment_of(n, a.L, a.cu);
+    if (p >= sg.start + sg.len) return -1;
+    *start = sg.start;
+    return n;
+}
+
+// SiLU with the hardware exp2 and reciprocal (about 1e-6 relative): the result is
+// rounded to fp16 (2^-11) right after, so the accurate library forms would buy nothing.
+__device__ __forceinline__ float fast_silu(float x) {
+    return x * __frcp_rn(1.0f + __expf(-x));
+}
+
+// ---- steps 1-4 ------------------------------------------------------------------
+template <typename Tin>
+__global__ __launch_bounds__(256) void front_kernel(PrefillArgs a, Ws ws) {
+    __shared__ float buf[D * RAW];           // raw[c][m] (window of 67 tokens), then ys[t][c] (stride 129)
+    __shared__ int s_n[TT], s_start[TT];
+    const int units = 2 * a.Hk + a.Hv;
+    const int tiles = (a.L + TT - 1) / TT;
+    long long blk = blockIdx.x;
+    const int u = static_cast<int>(blk % units); blk /= units;
+    const int tile = static_cast<int>(blk % tiles);
+    const int row = static_cast<int>(blk / tiles);
+    const int p0 = tile * TT;
+    const int ch0 = u * D;   // [Q | K | V] blocks of D channels
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const Tin* x = static_cast<const Tin*>(a.qkv) + (static_cast<size_t>(row) * a.D + ch0) * a.L;
+
+    if (tid < TT) {
+        const int p = p0 + tid;
+        int start = 0, n = -1;
+        if (p < a.L) n = owner_of(p, row, a, &start);
+        s_n[tid] = n;
+        s_start[tid] = start;
+    }
+    // a wave loads 64 consecutive tokens of one channel per instruction (coalesced);
+    // all of a wave's rows are issued before the first one is used
+    {
+        constexpr int ROWS = D / 4;
+        // unconditional loads from clamped positions, masked afterwards, so that
+        // every row is in flight at once (a load under a branch is waited for
+        // inside the branch)
+        float v[ROWS], hv[ROWS];
+        const int p = p0 + lane, ph = p0 - 3 + lane;
+        const bool pv = p < a.L, hvld = lane < 3 && ph >= 0 && ph < a.L;
+        const int pc = pv ? p : a.L - 1, phc = hvld ? ph : pc;
+#pragma unroll
+        for (int i = 0; i < ROWS; ++i) {
+            const Tin* xc = x + static_cast<size_t>(wave * ROWS + i) * a.L;
+            const float lv = to_f32(xc[pc]), lh = to_f32(xc[phc]);
+            v[i] = pv ? lv : 0.f;
+            hv[i] = hvld ? lh : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < ROWS; ++i) {
+            const int c = wave * ROWS + i;
+            buf[c * RAW + 3 + lane] = v[i];
+            if (lane < 3) buf[c * RAW + lane] = hv[i];
+        }
+    }
+    __syncthreads();
+    const int c = tid & (D - 1), th = tid >> 7;   // channel, token half
+    const Tin* w = static_cast<const Tin*>(a.w) + static_cast<size_t>(ch0 + c) * kConvK;
+    float wv[kConvK];
+#pragma unroll
+    for (int j = 0; j < kConvK; ++j) wv[j] = to_f32(w[j]);
+    const Tin* cin = static_cast<const Tin*>(a.conv_in);
+    float y[TT / 2];
+    const int t0 = th * (TT / 2);
+    // fast path: all 32 tokens of this half belong to one sequence whose start is at
+    // least K-1 tokens before the first of them, so every window lies in the tile
+    const bool clean = s_n[t0] >= 0 && s_n[t0] == s_n[t0 + TT / 2 - 1] && p0 + t0 - s_start[t0] >= kConvK - 1;
+    if (clean) {
+        float x0 = buf[c * RAW + t0], x1 = buf[c * RAW + t0 + 1], x2 = buf[c * RAW + t0 + 2];
+#pragma unroll
+        for (int j = 0; j < TT / 2; ++j) {
+            const float x3 = buf[c * RAW + t0 + j + 3];
+            float acc = wv[0] * x0;
+            acc = __fmaf_rn(wv[1], x1, acc);
+            acc = __fmaf_rn(wv[2], x2, acc);
+            acc = __fmaf_rn(wv[3], x3, acc);
+            y[j] = fast_silu(acc);
+            x0 = x1; x1 = x2; x2 = x3;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < TT / 2; ++j) {
+            const int t = t0 + j;
+            const int n = s_n[t];
+            float win[kConvK];
+            if (n < 0) { y[j] = 0.f; continue; }
+            const int uu = p0 + t - s_start[t];  // index inside the sequence
+#pragma unroll
+            for (int q = 0; q < kConvK; ++q) {
+                const int m = uu + q;            // position in concat(state, x[seq])
+                win[q] = (m < kConvK - 1) ? to_f32(cin[(static_cast<size_t>(n) * a.D + ch0 + c) * (kConvK - 1) + m])
+                                          : buf[c * RAW + t + q];
+            }
+            float acc = wv[0] * win[0];
+            acc = __fmaf_rn(wv[1], win[1], acc);
+            acc = __fmaf_rn(wv[2], win[2], acc);
+            acc = __fmaf_rn(wv[3], win[3], acc);
+            y[j] = fast_silu(acc);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < TT / 2; ++j) buf[(th * (TT / 2) + j) * (D + 1) + c] = y[j];
+    __syncthreads();
+    const bool is_q = u < a.Hk, is_k = !is_q && u < 2 * a.Hk;
+    // per-token sum of squares: thread (token tid % 64, channel quarter tid / 64)
+    // reads its quarter column-wise (lanes run along tokens: conflict-free)
+    __shared__ float s_part[4][TT];
+    __shared__ float s_scale[TT];
+    if (is_q || is_k) {
+        const int t = tid & (TT - 1), qq = tid >> 6;
+        float ss = 0.f;
+#pragma unroll 8
+        for (int cc = 0; cc < D / 4; ++cc) {
+            const float v = buf[t * (D + 1) + qq * (D / 4) + cc];
+            ss = __fmaf_rn(v, v, ss);
+        }
+        s_part[qq][t] = ss;
+    }
+    __syncthreads();
+    if (tid < TT) {
+        float r = 1.f;
+        if (is_q || is_k) {
+            const float ss = (s_part[0][tid] + s_part[1][tid]) + (s_part[2][tid] + s_part[3][tid]);
+            if (a.use_l2) r = 1.0f / sqrtf(ss + a.eps);
+            if (is_q) r *= 1.0f / sqrtf(static_cast<float>(D));
+        }
+        s_scale[tid] = r;
+    }
+    __syncthreads();
+    // one wave per token: lane writes channels 2*lane, 2*lane+1 (256 contiguous bytes)
+    for (int i = 0; i < TT / 4; ++i) {
+        const int t = wave * (TT / 4) + i;
+        if (s_n[t] < 0) continue;            // uniform across the wave
+        const float r = s_scale[t];
+        const size_t tok = static_cast<size_t>(row) * a.L + p0 + t;
+        _Float16* dst = is_q ? ws.qh + (tok * a.Hk + u) * D
+                      : is_k ? ws.kh + (tok * a.Hk + (u - a.Hk)) * D
+                             : ws.vh + (tok * a.Hv + (u - 2 * a.Hk)) * D;
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        const h2 v = {static_cast<_Float16>(buf[t * (D + 1) + 2 * lane] * r),
+                      static_cast<_Float16>(buf[t * (D + 1) + 2 * lane + 1] * r)};
+        *reinterpret_cast<h2*>(dst + 2 * lane) = v;
+    }
+}
+
+// ---- chunk phase --------------------------------------------------------------------
+constexpr int KS = D + 8;    // row stride (halfs) of the chunk's keys in LDS
+constexpr int TS = C + 8;    // row stride (halfs) of the transposed operands (16-byte aligned rows)
+constexpr int AS = C + 1;    // row stride (floats) of A and T
+
+template <typename Tin>
+__global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a, Ws ws) {
+    // region: {Kc [C][KS] halfs, Am [C][AS] floats} during the Gram/solve phases,
+    //         {KbT [D][TS], VbT [D][TS] halfs} during the W/U phase
+    constexpr int REGION = 2 * D * TS * 2;  // 36864 B >= 64*136*2 + 64*65*4 = 34048 B
+    __shared__ __align__(16) unsigned char region[REGION];
+    __shared__ float Tm[C * AS];
+    __shared__ float Mt[3][16][17];
+    __shared__ float s_g[C], s_b[C], s_gam[C], s_red[4];
+    _Float16* Kc = reinterpret_cast<_Float16*>(region);
+    float* Am = reinterpret_cast<float*>(region + C * KS * 2);
+    _Float16* KbT = reinterpret_cast<_Float16*>(region);
+    _Float16* VbT = reinterpret_cast<_Float16*>(region + D * TS * 2);
+
+    const int h = blockIdx.x % a.Hv;
+    const int id = blockIdx.x / a.Hv;
+    int n, c;
+    Seg seg;
+    if (id >= ws.nc_max || !find_chunk(id, a, &n, &c, &seg)) return;
+    const int f = a.Hv / a.Hk, hk = h / f;
+    const int nt = min(C, seg.len - c * C);
+    const size_t tok0 = static_cast<size_t>(seg.row) * a.L + seg.start + static_cast<size_t>(c) * C;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, r16 = lane & 15;
+    const Tin* gate = static_cast<const Tin*>(a.gate);
+    const Tin* beta = static_cast<const Tin*>(a.beta);
+
+    // 1. keys of the chunk (zero rows past the end), gate, beta
+    {
+        uint4 v[C * (D / 8) / 256];
+#pragma unroll
+        for (int q = 0; q < C * (D / 8) / 256; ++q) {
+            const int it = tid + 256 * q, r = it >> 4, j = it & 15;
+            const int rc = r < nt ? r : nt - 1;   // clamped row, masked below
+            v[q] = *reinterpret_cast<const uint4*>(ws.kh + ((tok0 + rc) * a.Hk + hk) * D + 8 * j);
+        }
+#pragma unroll
+        for (int q = 0; q < C * (D / 8) / 256; ++q) {
+            const int it = tid + 256 * q, r = it >> 4, j = it & 15;
+            *reinterpret_cast<uint4*>(Kc + r * KS + 8 * j) = r < nt ? v[q] : make_uint4(0, 0, 0, 0);
+        }
+    }
+    if (tid < C) {
+        s_g[tid] = tid < nt ? to_f32(gate[(tok0 + tid) * a.Hv + h]) : 0.f;
+        s_b[tid] = tid < nt ? to_f32(beta[(tok0 + tid) * a.Hv + h]) : 0.f;
+    }
+    // q rows of this wave's 16-token tile, straight into registers (A operands)
+    f16x8 aq[4];
+    {
+        const int t = 16 * wave + r16;
+        const int tc = t < nt ? t : nt - 1;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const f16x8 v = *reinterpret_cast<const f16x8*>(ws.qh + ((tok0 + tc) * a.Hk + hk) * D + 32 * ks + 8 * g);
+            aq[ks] = t < nt ? v : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {   // Gam = inclusive cumulative sum of g (wave scan)
+        float v = s_g[lane];
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float o = __shfl_up(v, off, 64);
+            if (lane >= off) v += o;
+        }
+        s_gam[lane] = v;
+    }
+    if ((h % f) == 0) {   // transposed keys for the carry: KT[i][s]
+        _Float16* kt = ws.KT + (static_cast<size_t>(id) * a.Hk + hk) * D * C;
+        for (int it = tid; it < D * (C / 8); it += 256) {
+            const int i = it >> 3, sg = it & 7;
+            f16x8 v;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] = Kc[(8 * sg + q) * KS + i];
+            *reinterpret_cast<f16x8*>(kt + i * C + 8 * sg) = v;
+        }
+    }
+    __syncthreads();
+
+    // 2. Gram matrices on MFMA: wave w owns rows 16w..16w+15
+    {
+        f32x4v kk[4], qk[4];
+#pragma unroll
+        for (int ntile = 0; ntile < 4; ++ntile) { kk[ntile] = f32x4v{0, 0, 0, 0}; qk[ntile] = kk[ntile]; }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const f16x8 ak = *reinterpret_cast<const f16x8*>(Kc + (16 * wave + r16) * KS + 32 * ks + 8 * g);
+#pragma unroll
+            for (int ntile = 0; ntile < 4; ++ntile) {
+                const f16x8 bk = *reinterpret_cast<const f16x8*>(Kc + (16 * ntile + r16) * KS + 32 * ks + 8 * g);
+                kk[ntile] = mfma16x16x32(ak, bk, kk[ntile]);
+                qk[ntile] = mfma16x16x32(aq[ks], bk, qk[ntile]);
+            }
+        }
+        _Float16* P = ws.P + (static_cast<size_t>(id) * a.Hv + h) * C * C;
+#pragma unroll
+        for (int ntile = 0; ntile < 4; ++ntile) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 16 * wave + 4 * g + e, s = 16 * ntile + r16;
+                const float dec = (s <= t && t < nt) ? expf(s_gam[t] - s_gam[s]) : 0.f;
+                Am[t * AS + s] = (s < t) ? s_b[t] * dec * kk[ntile][e] : 0.f;
+                P[t * C + s] = static_cast<_Float16>(dec * qk[ntile][e]);
+            }
+        }
+    }
+    __syncthreads();
+
+    // 3. T = (I + A)^-1, fp32. Diagonal 16x16 blocks by forward substitution
+    //    (lane = (block, column)); off-diagonal blocks by
+    //    T_ij = -T_ii * sum_{k=j}^{i-1} A_ik T_kj, block row by block row.
+    if (wave == 0) {
+        const int blk = lane >> 4, j = lane & 15;
+        float xcol[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            float acc = (t == j) ? 1.f : 0.f;
+#pragma unroll
+            for (int s = 0; s < t; ++s) acc = __fmaf_rn(-Am[(16 * blk + t) * AS + 16 * blk + s], xcol[s], acc);
+            xcol[t] = acc;
+        }
+#pragma unroll
+        for (int t = 0; t < 16; ++t) Tm[(16 * blk + t) * AS + 16 * blk + j] = xcol[t];
+    } else {
+        for (int e = tid - 64; e < C * C; e += 192) {
+            const int t = e >> 6, s = e & 63;
+            if ((s >> 4) > (t >> 4)) Tm[t * AS + s] = 0.f;
+        }
+    }
+    __syncthreads();
+    {
+        const int r = tid >> 4, cc = tid & 15;
+        for (int bi = 1; bi < 4; ++bi) {
+            for (int bj = 0; bj < bi; ++bj) {
+                float m = 0.f;
+                for (int bk = bj; bk < bi; ++bk)
+#pragma unroll
+                    for (int q = 0; q < 16; ++q)
+                        m = __fmaf_rn(Am[(16 * bi + r) * AS + 16 * bk + q], Tm[(16 * bk + q) * AS + 16 * bj + cc], m);
+                Mt[bj][r][cc] = m;
+            }
+            __syncthreads();
+            for (int bj = 0; bj < bi; ++bj) {
+                float v = 0.f;
+#pragma unroll
+                for (int q = 0; q < 16; ++q) v = __fmaf_rn(Tm[(16 * bi + r) * AS + 16 * bi + q], Mt[bj][q][cc], v);
+                Tm[(16 * bi + r) * AS + 16 * bj + cc] = -v;
+            }
+            __syncthreads();
+        }
+    }
+
+    // 4. operands of W and U, transposed (k = token): KbT[i][s] = beta_s exp(Gam_s) k_s[i],
+    //    VbT[j][s] = beta_s v_s[j] 2^-eV
+    // lanes run along tokens, so the transposed LDS writes of a wave hit
+    // consecutive halfs (no bank conflicts); item (s, j) = granule j of token s
+    float vmax = 0.f;
+    f16x8 vreg[4];
+    const int s = lane;
+    const float fk = s_b[s] * expf(s_gam[s]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int j = wave + 4 * q;
+        const int sc = s < nt ? s : nt - 1;
+        const f16x8 z = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        const f16x8 kl = *reinterpret_cast<const f16x8*>(ws.kh + ((tok0 + sc) * a.Hk + hk) * D + 8 * j);
+        const f16x8 vl = *reinterpret_cast<const f16x8*>(ws.vh + ((tok0 + sc) * a.Hv + h) * D + 8 * j);
+        const f16x8 kv = s < nt ? kl : z;
+        vreg[q] = s < nt ? vl : z;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            KbT[(8 * j + e) * TS + s] = static_cast<_Float16>(fk * static_cast<float>(kv[e]));
+            vmax = fmaxf(vmax, fabsf(s_b[s] * static_cast<float>(vreg[q][e])));
+        }
+    }
+    vmax = wave_max(vmax);
+    if (lane == 0) s_red[wave] = vmax;
+    __syncthreads();
+    const int eV = pow2_exponent(fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3])));
+    const float sV = ldexpf(1.f, -eV);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int j = wave + 4 * q;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            VbT[(8 * j + e) * TS + s] = static_cast<_Float16>(s_b[s] * static_cast<float>(vreg[q][e]) * sV);
+    }
+    __syncthreads();
+
+    // 5. W = T KbT^T and U = T VbT^T on MFMA: wave w owns token rows 16w..16w+15
+    f16x8 at[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) at[ks][e] = static_cast<_Float16>(Tm[(16 * wave + r16) * AS + 32 * ks + 8 * g + e]);
+    _Float16* Wout = ws.W + (static_cast<size_t>(id) * a.Hv + h) * C * D;
+    f32x4v uacc[8];
+#pragma unroll
+    for (int ntile = 0; ntile < 8; ++ntile) {
+        f32x4v wacc = f32x4v{0, 0, 0, 0};
+        uacc[ntile] = wacc;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const f16x8 bk = *reinterpret_cast<const f16x8*>(KbT + (16 * ntile + r16) * TS + 32 * ks + 8 * g);
+            const f16x8 bv = *reinterpret_cast<const f16x8*>(VbT + (16 * ntile + r16) * TS + 32 * ks + 8 * g);
+            wacc = mfma16x16x32(at[ks], bk, wacc);
+            uacc[ntile] = mfma16x16x32(at[ks], bv, uacc[ntile]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            Wout[(16 * wave + 4 * g + e) * D + 16 * ntile + r16] = static_cast<_Float16>(wacc[e]);
+    }
+    float umax = 0.f;
+#pragma unroll
+    for (int ntile = 0; ntile < 8; ++ntile)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) umax = fmaxf(umax, fabsf(uacc[ntile][e]));
+    umax = wave_max(umax);
+    __syncthreads();   // every wave has read s_red
+    if (lane == 0) s_red[wave] = umax;
+    __syncthreads();
+    const int eU = pow2_exponent(fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3])));
+    const float sU = ldexpf(1.f, -eU);
+    _Float16* Uout = ws.U + (static_cast<size_t>(id) * a.Hv + h) * C * D;
+#pragma unroll
+    for (int ntile = 0; ntile < 8; ++ntile)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            Uout[(16 * wave + 4 * g + e) * D + 16 * ntile + r16] = static_cast<_Float16>(uacc[ntile][e] * sU);
+    float* cf = ws.coef + (static_cast<size_t>(id) * a.Hv + h) * COEF;
+    if (tid < C) {
+        const float glast = s_gam[nt - 1];
+        cf[tid] = expf(s_gam[tid]);
+        cf[C + tid] = expf(glast - s_gam[tid]);   // rows past the end multiply zero deltas
+    }
+    if (tid == 0) {
+        cf[2 * C] = expf(s_gam[nt - 1]);
+        cf[2 * C + 1] = ldexpf(1.f, eV + eU);
+    }
+}
+
+// ---- state carry ----------------------------------------------------------------------
+// A workgroup of 4 waves owns NTW * 64 columns of one head's state: wave w owns
+// the 16-column tiles [col0, col0 + 16 * NTW). With NTW = 1 a head is split
+// over two workgroups (more CUs for few sequences), with NTW = 2 one
+// workgroup holds the whole head.
+//
+// One LDS stage holds, for one chunk and head, in 16-byte granules:
+//   W [64][16 granules]  Q [64][16]  KT [128][8]  P [64][8]  U [64][8*NTW] (this
+//   workgroup's columns)  coefficients [40]
+// Granule j of row r of W, Q, KT and P sits at position j ^ (r mod rowgranules) of its
+// row, which spreads the 16 rows one MFMA operand read touches over the banks.
+template <int NTW>
+struct Stage {
+    static constexpr int W = 0, Q = 1024, KT = 2048, P = 3072, U = 3584;
+    static constexpr int UG = 8 * NTW;                 // U granules per row
+    static constexpr int CF = U + 64 * UG;
+    static constexpr int END = CF + COEF / 4;
+    static constexpr int INSTR = (END + 63) / 64;      // wave-wide 1 KB loads
+    static constexpr int BYTES = INSTR * 1024;
+};
+
+// Eight halfs of an A operand whose k slots (g, e) hold logical columns
+// 32ks + 4g + e (e < 4) and 32ks + 16 + 4g + (e - 4) (e >= 4), from a swizzled row.
+template <int RG>   // granules per row (16 or 8)
+__device__ __forceinline__ f16x8 lds_a(const _Float16* base, int row, int ks, int g) {
+    const int j1 = 4 * ks + (g >> 1), j2 = j1 + 2;
+    const int sw = row & (RG - 1);
+    const _Float16* r = base + row * RG * 8 + 4 * (g & 1);
+    const f16x4 lo = *reinterpret_cast<const f16x4*>(r + (j1 ^ sw) * 8);
+    const f16x4 hi = *reinterpret_cast<const f16x4*>(r + (j2 ^ sw) * 8);
+    return f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+extern __shared__ __align__(1024) unsigned char g_stage[];   // 2 stages
+
+// Issue the wave-wide 1 KB global->LDS loads of one stage. `wave` must be
+// wave-uniform (readfirstlane'd): each load lies wholly inside one region, so
+// the region choice is a scalar branch and only the row/granule arithmetic is
+// per lane.
+template <int NTW>
+__device__ __forceinline__ void issue_stage(const PrefillArgs& a, const Ws& ws, int id, size_t tok0, int nt,
+                                            int h, int hk, int ucol0, int buf, int wave, int lane) {
+    using SG = Stage<NTW>;
+    const size_t wbase = (static_cast<size_t>(id) * a.Hv + h) * C * D;
+    const size_t ktbase = (static_cast<size_t>(id) * a.Hk + hk) * D * C;
+    const size_t pbase = (static_cast<size_t>(id) * a.Hv + h) * C * C;
+    const size_t cfbase = (static_cast<size_t>(id) * a.Hv + h) * COEF;
+    unsigned char* stage = g_stage + buf * SG::BYTES;
+    for (int q = wave; q < SG::INSTR; q += 4) {
+        const int item = 64 * q + lane;
+        const void* src;
+        if (64 * q < SG::Q) {                     // W rows, swizzled granules
+            const int r = item >> 4, j = (item & 15) ^ (r & 15);
+            src = ws.W + wbase + r * D + 8 * j;
+        } else if (64 * q < SG::KT) {             // q rows of the K head (rows past the end: a finite row)
+            const int it = item - SG::Q, r = it >> 4, j = (it & 15) ^ (r & 15);
+            const int rr = r < nt ? r : nt - 1;
+            src = ws.qh + ((tok0 + rr) * a.Hk + hk) * D + 8 * j;
+        } else if (64 * q < SG::P) {              // keys transposed
+            const int it = item - SG::KT, i = it >> 3, j = (it & 7) ^ (i & 7);
+            src = ws.KT + ktbase + i * C + 8 * j;
+        } else if (64 * q < SG::U) {              // P
+            const int it = item - SG::P, t = it >> 3, j = (it & 7) ^ (t & 7);
+            src = ws.P + pbase + t * C + 8 * j;
+        } else if (64 * q < SG::CF) {             // this workgroup's columns of U
+            const int it = item - SG::U, t = it / SG::UG, j = it % SG::UG;
+            src = ws.U + wbase + t * D + ucol0 + 8 * j;
+        } else {                                  // coefficients; lanes past the end land in padding
+            const int it = item - SG::CF;
+            src = ws.coef + cfbase + 4 * (it < COEF / 4 ? it : 0);
+        }
+        __builtin_amdgcn_global_load_lds(src, stage + q * 1024, 16, 0, 0);
+    }
+}
+
+template <int NTW>
+__global__ __launch_bounds__(256) void carry_kernel(PrefillArgs a, Ws ws) {
+    using SG = Stage<NTW>;
+    const int nh = a.N * a.Hv;
+    const int cs = blockIdx.x / nh;                      // the CS workgroups of a head share blockIdx % 8 (XCD)
+    const int h = (blockIdx.x % nh) % a.Hv;
+    const int n = (blockIdx.x % nh) / a.Hv;
+    const int f = a.Hv / a.Hk, hk = h / f;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, r16 = lane & 15;
+    const int ucol0 = cs * 64 * NTW;                     // first column of this workgroup
+    const int lcol0 = wave * 16 * NTW;                   // first column of this wave, inside the workgroup
+    const int col0 = ucol0 + lcol0;
+    const Seg seg = segment_of(n, a.L, a.cu);
+    int base = 0;
+    for (int m = 0; m < n; ++m) base += chunks_of(segment_of(m, a.L, a.cu));
+    int nch = chunks_of(seg);
+    if (base + nch > ws.nc_max) nch = ws.nc_max - base;   // only malformed cu_seqlens get here
+    if (nch <= 0) return;
+
+    float* Sg = a.S + (static_cast<size_t>(n) * a.Hv + h) * D * D;
+    float S[8][NTW][4];
+    float smax = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                S[mt][nt][e] = Sg[(16 * mt + 4 * g + e) * D + col0 + 16 * nt + r16];
+                smax = fmaxf(smax, fabsf(S[mt][nt][e]));
+            }
+
+    const size_t row_tok = static_cast<size_t>(seg.row) * a.L + seg.start;
+    // outputs of the previous chunk, stored one iteration late so that the wait
+    // for the next stage never waits on freshly issued stores
+    float opend[4][NTW][4];
+    size_t otok = 0;
+    int ont = 0;
+    issue_stage<NTW>(a, ws, base, row_tok, min(C, seg.len), h, hk, ucol0, 0, wave, lane);
+    for (int c = 0; c <= nch; ++c) {
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's share of the stage has landed
+        __syncthreads();                 // ... and every wave's; the other stage is free
+        if (c > 0) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = 16 * mt + 4 * g + e;
+                    if (t < ont) {
+                        float* orow = a.o + ((otok + t) * a.Hv + h) * D + col0 + r16;
+#pragma unroll
+                        for (int nt = 0; nt < NTW; ++nt) orow[16 * nt] = opend[mt][nt][e];
+                    }
+                }
+        }
+        if (c == nch) break;
+        const int id = base + c;
+        const int ntc = min(C, seg.len - c * C);
+        const size_t tok0 = row_tok + static_cast<size_t>(c) * C;
+        if (c + 1 < nch)
+            issue_stage<NTW>(a, ws, id + 1, tok0 + C, min(C, seg.len - (c + 1) * C), h, hk, ucol0, (c + 1) & 1,
+                             wave, lane);
+        const unsigned char* st = g_stage + (c & 1) * SG::BYTES;
+        const _Float16* Wl = reinterpret_cast<const _Float16*>(st + SG::W * 16);
+        const _Float16* Ql = reinterpret_cast<const _Float16*>(st + SG::Q * 16);
+        const _Float16* KTl = reinterpret_cast<const _Float16*>(st + SG::KT * 16);
+        const _Float16* Pl = reinterpret_cast<const _Float16*>(st + SG::P * 16);
+        const _Float16* Ul = reinterpret_cast<const _Float16*>(st + SG::U * 16);
+        const float* cf = reinterpret_cast<const float*>(st + SG::CF * 16);   // exp(Gam_t)
+        const float* cfr = cf + C;                                            // exp(Gam_last - Gam_t)
+        const float egl = cf[2 * C], uscale = cf[2 * C + 1];
+
+        // S as B operands (k = rows of S), scaled into fp16 range
+        const int eS = pow2_exponent(wave_max(smax));
+        const float sS = ldexpf(1.f, -eS), iS = ldexpf(1.f, eS);
+        f16x8 sb[NTW][4];
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    sb[nt][ks][e] = static_cast<_Float16>(S[2 * ks][nt][e] * sS);
+                    sb[nt][ks][4 + e] = static_cast<_Float16>(S[2 * ks + 1][nt][e] * sS);
+                }
+
+        // Delta = U - W S (rows past the end of the sequence are zero)
+        float dl[4][NTW][4];
+        float dmax = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            f32x4v acc[NTW];
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) acc[nt] = f32x4v{0, 0, 0, 0};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const f16x8 aw = lds_a<16>(Wl, 16 * mt + r16, ks, g);
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt) acc[nt] = mfma16x16x32(aw, sb[nt][ks], acc[nt]);
+            }
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = 16 * mt + 4 * g + e;
+                    const float u = static_cast<float>(Ul[t * 8 * SG::UG + lcol0 + 16 * nt + r16]);
+                    const float d = (t < ntc) ? __fmaf_rn(u, uscale, -iS * acc[nt][e]) : 0.f;
+                    dl[mt][nt][e] = d;
+                    dmax = fmaxf(dmax, fabsf(d));
+                }
+        }
+        const int eD = pow2_exponent(wave_max(dmax));
+        const float sD = ldexpf(1.f, -eD), iD = ldexpf(1.f, eD);
+        f16x8 db[NTW][2], dp[NTW][2];   // Delta and diag(exp(Gam_last - Gam)) Delta as B operands (k = token)
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int mt = 2 * ks + (e >> 2), ee = e & 3;
+                    const int t = 16 * mt + 4 * g + ee;
+                    const float v = dl[mt][nt][ee] * sD;
+                    db[nt][ks][e] = static_cast<_Float16>(v);
+                    dp[nt][ks][e] = static_cast<_Float16>(v * cfr[t]);
+                }
+
+        // O = diag(exp(Gam)) Q S + P Delta (stored at the next iteration)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            f32x4v a1[NTW], a2[NTW];
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) { a1[nt] = f32x4v{0, 0, 0, 0}; a2[nt] = a1[nt]; }
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const f16x8 aq = lds_a<16>(Ql, 16 * mt + r16, ks, g);
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt) a1[nt] = mfma16x16x32(aq, sb[nt][ks], a1[nt]);
+            }
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const f16x8 ap = lds_a<8>(Pl, 16 * mt + r16, ks, g);
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt) a2[nt] = mfma16x16x32(ap, db[nt][ks], a2[nt]);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float eg = cf[16 * mt + 4 * g + e] * iS;
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt) opend[mt][nt][e] = __fmaf_rn(eg, a1[nt][e], iD * a2[nt][e]);
+            }
+        }
+        otok = tok0;
+        ont = ntc;
+
+        // S = exp(Gam_last) S + K^T diag(exp(Gam_last - Gam)) Delta; max|S| for the next chunk
+        smax = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+            f32x4v acc[NTW];
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) acc[nt] = f32x4v{0, 0, 0, 0};
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const f16x8 ak = lds_a<8>(KTl, 16 * mt + r16, ks, g);
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt) acc[nt] = mfma16x16x32(ak, dp[nt][ks], acc[nt]);
+            }
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    S[mt][nt][e] = __fmaf_rn(egl, S[mt][nt][e], iD * acc[nt][e]);
+                    smax = fmaxf(smax, fabsf(S[mt][nt][e]));
+                }
+        }
+    }
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Sg[(16 * mt + 4 * g + e) * D + col0 + 16 * nt + r16] = S[mt][nt][e];
+}
+
+}  // namespace pf2
+
+size_t prefill_mfma_workspace_bytes(int B, int L, int N, int Hk, int Hv) {
+    const size_t a = pf2::layout(nullptr, B, L, N, Hk, Hv, true).bytes;
+    const size_t b = pf2::layout(nullptr, B, L, N, Hk, Hv, false).bytes;
+    return a > b ? a : b;
+}
+
+// Compute units of the current device (queried once per device).
+static int device_cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+// Dynamic LDS above 64 KB must be allowed per kernel before the first launch.
+static hipError_t allow_stage_lds() {
+    static hipError_t st = [] {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pf2::carry_kernel<1>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, 2 * pf2::Stage<1>::BYTES);
+        if (e != hipSuccess) return e;
+        return hipFuncSetAttribute(reinterpret_cast<const void*>(&pf2::carry_kernel<2>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, 2 * pf2::Stage<2>::BYTES);
+    }();
+    return st;
+}
+
+template <typename Tin>
+static hipError_t launch_mfma_t(const PrefillArgs& a, int in_dtype, hipStream_t stream) {
+    const bool ragged = a.cu != nullptr;
+    pf2::Ws ws = pf2::layout(a.ws, a.B, a.L, a.N, a.Hk, a.Hv, ragged);
+    void* args[] = {const_cast<PrefillArgs*>(&a), &ws};
+    hipError_t e = allow_stage_lds();
+    if (e != hipSuccess) return e;
+    const long long fblocks = static_cast<long long>(a.B) * ((a.L + pf2::TT - 1) / pf2::TT) * (2 * a.Hk + a.Hv);
+    if (fblocks > 0) {
+        e = hipLaunchKernel(reinterpret_cast<const void*>(&pf2::front_kernel<Tin>), dim3(static_cast<unsigned>(fblocks)),
+                            dim3(256), args, 0, stream);
+        if (e != hipSuccess) return e;
+    }
+    const long long cblocks = static_cast<long long>(ws.nc_max) * a.Hv;
+    if (cblocks > 0) {
+        e = hipLaunchKernel(reinterpret_cast<const void*>(&pf2::chunk_kernel<Tin>), dim3(static_cast<unsigned>(cblocks)),
+                            dim3(256), args, 0, stream);
+        if (e != hipSuccess) return e;
+    }
+    const long long heads = static_cast<long long>(a.N) * a.Hv;
+    if (heads > 0) {
+        // split each head over two workgroups when that still fits one round of the CUs
+        if (2 * heads <= device_cu_count()) {
+            e = hipLaunchKernel(reinterpret_cast<const void*>(&pf2::carry_kernel<1>), dim3(static_cast<unsigned>(2 * heads)),
+                                dim3(256), args, 2 * pf2::Stage<1>::BYTES, stream);
+        } else {
+            e = hipLaunchKernel(reinterpret_cast<const void*>(&pf2::carry_kernel<2>), dim3(static_cast<unsigned>(heads)),
+                                dim3(256), args, 2 * pf2::Stage<2>::BYTES, stream);
+        }
+        if (e != hipSuccess) return e;
+    }
+    ConvArgs ca{a.B, a.L, a.D, a.N, a.qkv, a.w, a.conv_in, a.conv_out, nullptr, a.cu};
+    return launch_conv_state(ca, in_dtype, stream);
+}
+
+hipError_t launch_prefill_mfma(const PrefillArgs& a, int in_dtype, hipStream_t stream) {
+    return in_dtype == 1 ? launch_mfma_t<bf16_t>(a, in_dtype, stream) : launch_mfma_t<float>(a, in_dtype, stream);
+}
+
+}  // namespace gdn
