@@ -28,6 +28,21 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
+// max over the wave of non-negative values, returned wave-uniform. Non-negative
+// IEEE floats order like their bit patterns, so the reduction runs on integers:
+// DPP within quads (lanes ^1, ^2) and rows (rotate by 4, 8), then the four row
+// results are read out to scalars.
+__device__ __forceinline__ float wave_max_nonneg(float x) {
+    int v = __float_as_int(x);
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x124, 0xF, 0xF, false));  // row_ror:4
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false));  // row_ror:8
+    const int r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+    const int r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+    return __int_as_float(max(max(r0, r1), max(r2, r3)));
+}
+
 // Power-of-two scale that brings max|x| into [2^14, 2^15): inside fp16's range
 // with room to spare. Returns the exponent e; values are stored as x * 2^-e and
 // results multiplied back by 2^e (both exact).

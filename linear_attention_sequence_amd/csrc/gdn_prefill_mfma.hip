@@ -511,20 +511,19 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a, Ws ws) {
 }
 
 // ---- state carry ----------------------------------------------------------------------
-// A workgroup of 4 waves owns NTW * 64 columns of one head's state: wave w owns
-// the 16-column tiles [col0, col0 + 16 * NTW). With NTW = 1 a head is split
-// over two workgroups (more CUs for few sequences), with NTW = 2 one
-// workgroup holds the whole head.
+// A workgroup of NW waves owns CPW = NW * NTW * 16 columns of one head's state:
+// wave w owns the 16-column tiles [col0, col0 + 16 * NTW). A head is split over
+// 128 / CPW workgroups (more CUs when there are few sequences).
 //
 // One LDS stage holds, for one chunk and head, in 16-byte granules:
-//   W [64][16 granules]  Q [64][16]  KT [128][8]  P [64][8]  U [64][8*NTW] (this
+//   W [64][16 granules]  Q [64][16]  KT [128][8]  P [64][8]  U [64][CPW/8] (this
 //   workgroup's columns)  coefficients [40]
 // Granule j of row r of W, Q, KT and P sits at position j ^ (r mod rowgranules) of its
 // row, which spreads the 16 rows one MFMA operand read touches over the banks.
-template <int NTW>
+template <int CPW>
 struct Stage {
     static constexpr int W = 0, Q = 1024, KT = 2048, P = 3072, U = 3584;
-    static constexpr int UG = 8 * NTW;                 // U granules per row
+    static constexpr int UG = CPW / 8;                 // U granules per row
     static constexpr int CF = U + 64 * UG;
     static constexpr int END = CF + COEF / 4;
     static constexpr int INSTR = (END + 63) / 64;      // wave-wide 1 KB loads
@@ -549,16 +548,16 @@ extern __shared__ __align__(1024) unsigned char g_stage[];   // 2 stages
 // wave-uniform (readfirstlane'd): each load lies wholly inside one region, so
 // the region choice is a scalar branch and only the row/granule arithmetic is
 // per lane.
-template <int NTW>
+template <int CPW, int NW>
 __device__ __forceinline__ void issue_stage(const PrefillArgs& a, const Ws& ws, int id, size_t tok0, int nt,
                                             int h, int hk, int ucol0, int buf, int wave, int lane) {
-    using SG = Stage<NTW>;
+    using SG = Stage<CPW>;
     const size_t wbase = (static_cast<size_t>(id) * a.Hv + h) * C * D;
     const size_t ktbase = (static_cast<size_t>(id) * a.Hk + hk) * D * C;
     const size_t pbase = (static_cast<size_t>(id) * a.Hv + h) * C * C;
     const size_t cfbase = (static_cast<size_t>(id) * a.Hv + h) * COEF;
     unsigned char* stage = g_stage + buf * SG::BYTES;
-    for (int q = wave; q < SG::INSTR; q += 4) {
+    for (int q = wave; q < SG::INSTR; q += NW) {
         const int item = 64 * q + lane;
         const void* src;
         if (64 * q < SG::Q) {                     // W rows, swizzled granules
@@ -585,9 +584,10 @@ __device__ __forceinline__ void issue_stage(const PrefillArgs& a, const Ws& ws, 
     }
 }
 
-template <int NTW>
-__global__ __launch_bounds__(256) void carry_kernel(PrefillArgs a, Ws ws) {
-    using SG = Stage<NTW>;
+template <int NTW, int NW>
+__global__ __launch_bounds__(NW * 64) void carry_kernel(PrefillArgs a, Ws ws) {
+    constexpr int CPW = NW * NTW * 16;
+    using SG = Stage<CPW>;
     const int nh = a.N * a.Hv;
     const int cs = blockIdx.x / nh;                      // the CS workgroups of a head share blockIdx % 8 (XCD)
     const int h = (blockIdx.x % nh) % a.Hv;
@@ -596,7 +596,7 @@ __global__ __launch_bounds__(256) void carry_kernel(PrefillArgs a, Ws ws) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, r16 = lane & 15;
-    const int ucol0 = cs * 64 * NTW;                     // first column of this workgroup
+    const int ucol0 = cs * CPW;                          // first column of this workgroup
     const int lcol0 = wave * 16 * NTW;                   // first column of this wave, inside the workgroup
     const int col0 = ucol0 + lcol0;
     const Seg seg = segment_of(n, a.L, a.cu);
@@ -625,7 +625,7 @@ __global__ __launch_bounds__(256) void carry_kernel(PrefillArgs a, Ws ws) {
     float opend[4][NTW][4];
     size_t otok = 0;
     int ont = 0;
-    issue_stage<NTW>(a, ws, base, row_tok, min(C, seg.len), h, hk, ucol0, 0, wave, lane);
+    issue_stage<CPW, NW>(a, ws, base, row_tok, min(C, seg.len), h, hk, ucol0, 0, wave, lane);
     for (int c = 0; c <= nch; ++c) {
         __builtin_amdgcn_s_waitcnt(0);   // this wave's share of the stage has landed
         __syncthreads();                 // ... and every wave's; the other stage is free
@@ -647,8 +647,8 @@ __global__ __launch_bounds__(256) void carry_kernel(PrefillArgs a, Ws ws) {
         const int ntc = min(C, seg.len - c * C);
         const size_t tok0 = row_tok + static_cast<size_t>(c) * C;
         if (c + 1 < nch)
-            issue_stage<NTW>(a, ws, id + 1, tok0 + C, min(C, seg.len - (c + 1) * C), h, hk, ucol0, (c + 1) & 1,
-                             wave, lane);
+            issue_stage<CPW, NW>(a, ws, id + 1, tok0 + C, min(C, seg.len - (c + 1) * C), h, hk, ucol0, (c + 1) & 1,
+                                 wave, lane);
         const unsigned char* st = g_stage + (c & 1) * SG::BYTES;
         const _Float16* Wl = reinterpret_cast<const _Float16*>(st + SG::W * 16);
         const _Float16* Ql = reinterpret_cast<const _Float16*>(st + SG::Q * 16);
@@ -660,7 +660,7 @@ __global__ __launch_bounds__(256) void carry_kernel(PrefillArgs a, Ws ws) {
         const float egl = cf[2 * C], uscale = cf[2 * C + 1];
 
         // S as B operands (k = rows of S), scaled into fp16 range
-        const int eS = pow2_exponent(wave_max(smax));
+        const int eS = pow2_exponent(wave_max_nonneg(smax));
         const float sS = ldexpf(1.f, -eS), iS = ldexpf(1.f, eS);
         f16x8 sb[NTW][4];
 #pragma unroll
@@ -698,7 +698,7 @@ __global__ __launch_bounds__(256) void carry_kernel(PrefillArgs a, Ws ws) {
                     dmax = fmaxf(dmax, fabsf(d));
                 }
         }
-        const int eD = pow2_exponent(wave_max(dmax));
+        const int eD = pow2_exponent(wave_max_nonneg(dmax));
         const float sD = ldexpf(1.f, -eD), iD = ldexpf(1.f, eD);
         f16x8 db[NTW][2], dp[NTW][2];   // Delta and diag(exp(Gam_last - Gam)) Delta as B operands (k = token)
 #pragma unroll
@@ -780,6 +780,14 @@ size_t prefill_mfma_workspace_bytes(int B, int L, int N, int Hk, int Hv) {
     return a > b ? a : b;
 }
 
+// Whole-head carry workgroups: 8 waves of one 16-column tile each (two waves per
+// SIMD hide each other's LDS and MFMA latencies; on the 8-sequence ragged prefill
+// this beat 4 waves of two tiles by 10%).
+#ifndef CARRY_NTW
+#define CARRY_NTW 1
+#define CARRY_NW 8
+#endif
+
 // Compute units of the current device (queried once per device).
 static int device_cu_count() {
     static int cached[64] = {0};
@@ -793,16 +801,16 @@ static int device_cu_count() {
     return cached[dev];
 }
 
-// Dynamic LDS above 64 KB must be allowed per kernel before the first launch.
-static hipError_t allow_stage_lds() {
-    static hipError_t st = [] {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pf2::carry_kernel<1>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, 2 * pf2::Stage<1>::BYTES);
-        if (e != hipSuccess) return e;
-        return hipFuncSetAttribute(reinterpret_cast<const void*>(&pf2::carry_kernel<2>),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, 2 * pf2::Stage<2>::BYTES);
-    }();
-    return st;
+// The carry configurations: (tiles per wave, waves per workgroup).
+template <int NTW, int NW>
+static hipError_t launch_carry(void** args, long long heads, hipStream_t stream) {
+    constexpr int CPW = NW * NTW * 16;
+    constexpr size_t lds = 2 * pf2::Stage<CPW>::BYTES;
+    const void* k = reinterpret_cast<const void*>(&pf2::carry_kernel<NTW, NW>);
+    // dynamic LDS above 64 KB must be allowed per kernel before its first launch
+    static const hipError_t allowed = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (allowed != hipSuccess) return allowed;
+    return hipLaunchKernel(k, dim3(static_cast<unsigned>(heads * (128 / CPW))), dim3(NW * 64), args, lds, stream);
 }
 
 template <typename Tin>
@@ -810,8 +818,7 @@ static hipError_t launch_mfma_t(const PrefillArgs& a, int in_dtype, hipStream_t 
     const bool ragged = a.cu != nullptr;
     pf2::Ws ws = pf2::layout(a.ws, a.B, a.L, a.N, a.Hk, a.Hv, ragged);
     void* args[] = {const_cast<PrefillArgs*>(&a), &ws};
-    hipError_t e = allow_stage_lds();
-    if (e != hipSuccess) return e;
+    hipError_t e;
     const long long fblocks = static_cast<long long>(a.B) * ((a.L + pf2::TT - 1) / pf2::TT) * (2 * a.Hk + a.Hv);
     if (fblocks > 0) {
         e = hipLaunchKernel(reinterpret_cast<const void*>(&pf2::front_kernel<Tin>), dim3(static_cast<unsigned>(fblocks)),
@@ -827,13 +834,8 @@ static hipError_t launch_mfma_t(const PrefillArgs& a, int in_dtype, hipStream_t 
     const long long heads = static_cast<long long>(a.N) * a.Hv;
     if (heads > 0) {
         // split each head over two workgroups when that still fits one round of the CUs
-        if (2 * heads <= device_cu_count()) {
-            e = hipLaunchKernel(reinterpret_cast<const void*>(&pf2::carry_kernel<1>), dim3(static_cast<unsigned>(2 * heads)),
-                                dim3(256), args, 2 * pf2::Stage<1>::BYTES, stream);
-        } else {
-            e = hipLaunchKernel(reinterpret_cast<const void*>(&pf2::carry_kernel<2>), dim3(static_cast<unsigned>(heads)),
-                                dim3(256), args, 2 * pf2::Stage<2>::BYTES, stream);
-        }
+        e = (2 * heads <= device_cu_count()) ? launch_carry<1, 4>(args, heads, stream)
+                                             : launch_carry<CARRY_NTW, CARRY_NW>(args, heads, stream);
         if (e != hipSuccess) return e;
     }
     ConvArgs ca{a.B, a.L, a.D, a.N, a.qkv, a.w, a.conv_in, a.conv_out, nullptr, a.cu};

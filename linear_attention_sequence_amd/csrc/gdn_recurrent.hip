@@ -28,48 +28,88 @@
 
 namespace gdn {
 
-template <typename Tin, int DK, int DV, int NT, int CW, bool NT_STORE, bool NT_LOAD>
-__global__ __launch_bounds__(NT) void recurrent_kernel(RecArgs a) {
+// Tile geometry: NT threads own a DK x CW slice (columns j0..j0+CW) of one
+// (sequence, V head) state tile.
+template <int DK, int DV, int NT, int CW>
+struct RecGeom {
     static_assert(CW % 4 == 0 && DV % CW == 0, "column split must divide dv");
-    constexpr int NSPLIT = DV / CW;
-    constexpr int CG = CW / 4;
-    constexpr int RG = NT / CG;
-    constexpr int RPT = DK / RG;
-    constexpr int NW = NT / kWave;
+    static constexpr int NSPLIT = DV / CW;
+    static constexpr int CG = CW / 4;
+    static constexpr int RG = NT / CG;
+    static constexpr int RPT = DK / RG;
+    static constexpr int NW = NT / kWave;
+    static constexpr int NCH = 2 * DK + CW;
     static_assert(NT % CG == 0 && DK % RG == 0, "tile does not divide the workgroup");
     static_assert(kWave % CG == 0, "a column group set must fit in one wave");
-    constexpr int NCH = 2 * DK + CW;
+};
 
-    extern __shared__ float lds[];
-    const int T = a.T;
-    float* sq = lds;                       // [T][DK] q_hat
-    float* sk = sq + T * DK;               // [T][DK] k_hat
-    float* sv = sk + T * DK;               // [T][CW] v (this workgroup's columns)
-    float* s_alpha = sv + T * CW;          // [T] exp(gate)
-    float* s_beta = s_alpha + T;           // [T]
-    float* s_kq = s_beta + T;              // [T] k_hat . q_hat
-    float* red = s_kq + T;                 // [NW][CG][8] partial dot products
-    float* s_delta = red + NW * CG * 8;    // [CW]
+struct RecLds {
+    float *sq, *sk, *sv, *s_alpha, *s_beta, *s_kq, *red, *s_delta;
+};
 
-    const int bh = blockIdx.x / NSPLIT;
-    const int split = blockIdx.x - bh * NSPLIT;
-    const int j0 = split * CW;
-    const int b = bh / a.Hv;
-    const int h = bh - b * a.Hv;
+template <int DK, int CW, int NW>
+__device__ __forceinline__ RecLds rec_lds(float* lds, int T) {
+    RecLds L;
+    L.sq = lds;                          // [T][DK] q_hat
+    L.sk = L.sq + T * DK;                // [T][DK] k_hat
+    L.sv = L.sk + T * DK;                // [T][CW] v (this workgroup's columns)
+    L.s_alpha = L.sv + T * CW;           // [T] exp(gate)
+    L.s_beta = L.s_alpha + T;            // [T]
+    L.s_kq = L.s_beta + T;               // [T] k_hat . q_hat
+    L.red = L.s_kq + T;                  // [NW][CG][8] partial dot products
+    L.s_delta = L.red + NW * (CW / 4) * 8;  // [CW]
+    return L;
+}
+
+template <int DK, int CW, int NT>
+size_t recurrent_lds_bytes(int T) {
+    constexpr int CG = CW / 4;
+    constexpr int NW = NT / kWave;
+    return sizeof(float) * (static_cast<size_t>(T) * (2 * DK + CW) + 3 * T + NW * CG * 8 + CW);
+}
+
+// Which (sequence, V head, column slice) a unit index names.
+struct Unit {
+    int bh, b, h, hk, j0;
+    bool qk_owner;   // writes the q/k conv-state channels (one of the GQA group, slice 0)
+};
+
+template <int NSPLIT, int CW>
+__device__ __forceinline__ Unit unit_of(const RecArgs& a, int unit) {
+    Unit u;
+    u.bh = unit / NSPLIT;
+    const int split = unit - u.bh * NSPLIT;
+    u.j0 = split * CW;
+    u.b = u.bh / a.Hv;
+    u.h = u.bh - u.b * a.Hv;
     const int f = a.Hv / a.Hk;
-    const int hk = h / f;                  // reverse GQA: repeat_interleave
-    const int tid = threadIdx.x;
-    const int cg = tid % CG;
-    const int rg = tid / CG;
-    const int lane = tid % kWave;
-    const int wave = tid / kWave;
+    u.hk = u.h / f;                      // reverse GQA: repeat_interleave
+    u.qk_owner = (u.h % f) == 0 && split == 0;
+    return u;
+}
 
-    // 1. state tile -> registers
-    const float* Sin = a.S_in + static_cast<size_t>(bh) * DK * DV + j0;
-    float4 s[RPT];
+// Conv channel c (0 <= c < 2*DK + CW) of a unit: global channel, LDS row and
+// stride, and whether this unit writes its conv-state window.
+template <int DK, int DV, int CW>
+__device__ __forceinline__ void fe_channel(const RecArgs& a, const Unit& u, const RecLds& L, int c, int* ch,
+                                           float** dst, int* stride, bool* owner) {
+    if (c < DK) {                        // q channels of K head hk
+        *ch = u.hk * DK + c; *dst = L.sq + c; *owner = u.qk_owner; *stride = DK;
+    } else if (c < 2 * DK) {             // k channels of K head hk
+        *ch = a.Hk * DK + u.hk * DK + (c - DK); *dst = L.sk + (c - DK); *owner = u.qk_owner; *stride = DK;
+    } else {                             // v channels j0.. of V head h
+        *ch = 2 * a.Hk * DK + u.h * DV + u.j0 + (c - 2 * DK); *dst = L.sv + (c - 2 * DK); *owner = true; *stride = CW;
+    }
+}
+
+template <int DK, int DV, int NT, int CW, bool NT_LOAD>
+__device__ __forceinline__ void load_tile(const RecArgs& a, const Unit& u, float4 (&s)[RecGeom<DK, DV, NT, CW>::RPT]) {
+    using G = RecGeom<DK, DV, NT, CW>;
+    const int cg = threadIdx.x % G::CG, rg = threadIdx.x / G::CG;
+    const float* Sin = a.S_in + static_cast<size_t>(u.bh) * DK * DV + u.j0;
 #pragma unroll
-    for (int r = 0; r < RPT; ++r) {
-        const float* src = Sin + static_cast<size_t>(rg + r * RG) * DV + 4 * cg;
+    for (int r = 0; r < G::RPT; ++r) {
+        const float* src = Sin + static_cast<size_t>(rg + r * G::RG) * DV + 4 * cg;
         if constexpr (NT_LOAD) {
             const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src));
             s[r] = make_float4(v[0], v[1], v[2], v[3]);
@@ -77,58 +117,26 @@ __global__ __launch_bounds__(NT) void recurrent_kernel(RecArgs a) {
             s[r] = *reinterpret_cast<const float4*>(src);
         }
     }
+}
 
-    // 2. conv + SiLU of this unit's channels for every token of the block
-    const Tin* x = static_cast<const Tin*>(a.qkv);
-    const Tin* w = static_cast<const Tin*>(a.w);
-    const Tin* cin = static_cast<const Tin*>(a.conv_in);
-    Tin* cout = static_cast<Tin*>(a.conv_out);
-    const bool qk_owner = (h % f) == 0 && split == 0;
-    for (int c = tid; c < NCH; c += NT) {
-        int ch, stride;
-        float* dst;
-        bool owner;
-        if (c < DK) {                       // q channels of K head hk
-            ch = hk * DK + c; dst = sq + c; owner = qk_owner; stride = DK;
-        } else if (c < 2 * DK) {            // k channels of K head hk
-            ch = a.Hk * DK + hk * DK + (c - DK); dst = sk + (c - DK); owner = qk_owner; stride = DK;
-        } else {                            // v channels j0.. of V head h
-            ch = 2 * a.Hk * DK + h * DV + j0 + (c - 2 * DK); dst = sv + (c - 2 * DK); owner = true; stride = CW;
-        }
-        float wv[kConvK];
-#pragma unroll
-        for (int j = 0; j < kConvK; ++j) wv[j] = to_f32(w[static_cast<size_t>(ch) * kConvK + j]);
-        const Tin* st = cin + (static_cast<size_t>(b) * a.D + ch) * (kConvK - 1);
-        const Tin* xc = x + (static_cast<size_t>(b) * a.D + ch) * T;
-        float win[kConvK];
-#pragma unroll
-        for (int j = 0; j < kConvK - 1; ++j) win[j] = to_f32(st[j]);
-        for (int t = 0; t < T; ++t) {
-            win[kConvK - 1] = to_f32(xc[t]);
-            dst[t * stride] = conv_silu(wv, win);
-#pragma unroll
-            for (int j = 0; j < kConvK - 1; ++j) win[j] = win[j + 1];
-        }
-        if (cout != nullptr && owner) {
-            // new window: the K-1 most recent raw inputs of concat(state, x[0..T-1])
-            Tin* co = cout + (static_cast<size_t>(b) * a.D + ch) * (kConvK - 1);
-#pragma unroll
-            for (int j = 0; j < kConvK - 1; ++j) {
-                const int pos = T + j;  // position in the concatenated window
-                co[j] = (pos < kConvK - 1) ? st[pos] : xc[pos - (kConvK - 1)];
-            }
-        }
-    }
-    __syncthreads();
-
-    // 3. L2 norms, q scale and k.q, one wave per token
+// Steps 3-5 once the conv outputs of every token sit in LDS: L2 norms, the q
+// scale and k.q (one wave per token), then the recurrence token by token on the
+// register tile, writing the state after each token and the outputs.
+template <typename Tin, int DK, int DV, int NT, int CW, bool NT_STORE>
+__device__ __forceinline__ void recur_tail(const RecArgs& a, const Unit& u, const RecLds& L, int T,
+                                           float4 (&s)[RecGeom<DK, DV, NT, CW>::RPT]) {
+    using G = RecGeom<DK, DV, NT, CW>;
+    constexpr int CG = G::CG, RG = G::RG, RPT = G::RPT, NW = G::NW;
+    const int tid = threadIdx.x;
+    const int cg = tid % CG, rg = tid / CG;
+    const int lane = tid % kWave, wave = tid / kWave;
     const Tin* gate = static_cast<const Tin*>(a.gate);
     const Tin* beta = static_cast<const Tin*>(a.beta);
     const float qscale = 1.0f / sqrtf(static_cast<float>(DK));
     for (int t = wave; t < T; t += NW) {
         float qq = 0.f, kk = 0.f, kq = 0.f;
         for (int i = lane; i < DK; i += kWave) {
-            const float qv = sq[t * DK + i], kv = sk[t * DK + i];
+            const float qv = L.sq[t * DK + i], kv = L.sk[t * DK + i];
             qq = __fmaf_rn(qv, qv, qq);
             kk = __fmaf_rn(kv, kv, kk);
             kq = __fmaf_rn(kv, qv, kq);
@@ -140,25 +148,24 @@ __global__ __launch_bounds__(NT) void recurrent_kernel(RecArgs a) {
         const float rk = a.use_l2 ? 1.0f / sqrtf(kk + a.eps) : 1.0f;
         const float qs = rq * qscale;
         for (int i = lane; i < DK; i += kWave) {
-            sq[t * DK + i] *= qs;
-            sk[t * DK + i] *= rk;
+            L.sq[t * DK + i] *= qs;
+            L.sk[t * DK + i] *= rk;
         }
         if (lane == 0) {
-            const size_t gi = (static_cast<size_t>(b) * T + t) * a.Hv + h;
-            s_alpha[t] = expf(to_f32(gate[gi]));
-            s_beta[t] = to_f32(beta[gi]);
-            s_kq[t] = kq * rk * qs;
+            const size_t gi = (static_cast<size_t>(u.b) * T + t) * a.Hv + u.h;
+            L.s_alpha[t] = expf(to_f32(gate[gi]));
+            L.s_beta[t] = to_f32(beta[gi]);
+            L.s_kq[t] = kq * rk * qs;
         }
     }
     __syncthreads();
 
-    // 4. the recurrence, token by token
     for (int t = 0; t < T; ++t) {
         float pk[4] = {0.f, 0.f, 0.f, 0.f}, pq[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int r = 0; r < RPT; ++r) {
             const int i = rg + r * RG;
-            const float kv = sk[t * DK + i], qv = sq[t * DK + i];
+            const float kv = L.sk[t * DK + i], qv = L.sq[t * DK + i];
             pk[0] = __fmaf_rn(s[r].x, kv, pk[0]); pq[0] = __fmaf_rn(s[r].x, qv, pq[0]);
             pk[1] = __fmaf_rn(s[r].y, kv, pk[1]); pq[1] = __fmaf_rn(s[r].y, qv, pq[1]);
             pk[2] = __fmaf_rn(s[r].z, kv, pk[2]); pq[2] = __fmaf_rn(s[r].z, qv, pq[2]);
@@ -174,31 +181,31 @@ __global__ __launch_bounds__(NT) void recurrent_kernel(RecArgs a) {
             }
         }
         if (lane < CG) {
-            float* rp = red + (wave * CG + lane) * 8;
+            float* rp = L.red + (wave * CG + lane) * 8;
 #pragma unroll
             for (int c = 0; c < 4; ++c) { rp[c] = pk[c]; rp[4 + c] = pq[c]; }
         }
         __syncthreads();
-        const float al = s_alpha[t], be = s_beta[t];
+        const float al = L.s_alpha[t], be = L.s_beta[t];
         if (tid < CW) {
             const int j = tid, jg = j / 4, jc = j % 4;
             float PK = 0.f, PQ = 0.f;
 #pragma unroll
             for (int wv = 0; wv < NW; ++wv) {
-                PK += red[(wv * CG + jg) * 8 + jc];
-                PQ += red[(wv * CG + jg) * 8 + 4 + jc];
+                PK += L.red[(wv * CG + jg) * 8 + jc];
+                PQ += L.red[(wv * CG + jg) * 8 + 4 + jc];
             }
             const float p = al * PK;
-            const float d = be * (sv[t * CW + j] - p);
-            s_delta[j] = d;
-            a.o[((static_cast<size_t>(b) * T + t) * a.Hv + h) * DV + j0 + j] = __fmaf_rn(d, s_kq[t], al * PQ);
+            const float d = be * (L.sv[t * CW + j] - p);
+            L.s_delta[j] = d;
+            a.o[((static_cast<size_t>(u.b) * T + t) * a.Hv + u.h) * DV + u.j0 + j] = __fmaf_rn(d, L.s_kq[t], al * PQ);
         }
         __syncthreads();
-        const float4 dl = *reinterpret_cast<const float4*>(s_delta + 4 * cg);
-        float* Sout = a.S_out + ((static_cast<size_t>(b) * T + t) * a.Hv + h) * DK * DV + j0;
+        const float4 dl = *reinterpret_cast<const float4*>(L.s_delta + 4 * cg);
+        float* Sout = a.S_out + ((static_cast<size_t>(u.b) * T + t) * a.Hv + u.h) * DK * DV + u.j0;
 #pragma unroll
         for (int r = 0; r < RPT; ++r) {
-            const float kv = sk[t * DK + rg + r * RG];
+            const float kv = L.sk[t * DK + rg + r * RG];
             s[r].x = __fmaf_rn(kv, dl.x, al * s[r].x);
             s[r].y = __fmaf_rn(kv, dl.y, al * s[r].y);
             s[r].z = __fmaf_rn(kv, dl.z, al * s[r].z);
@@ -214,11 +221,55 @@ __global__ __launch_bounds__(NT) void recurrent_kernel(RecArgs a) {
     }
 }
 
-template <int DK, int CW, int NT>
-size_t recurrent_lds_bytes(int T) {
-    constexpr int CG = CW / 4;
-    constexpr int NW = NT / kWave;
-    return sizeof(float) * (static_cast<size_t>(T) * (2 * DK + CW) + 3 * T + NW * CG * 8 + CW);
+// Any T (verify blocks, and decode at head dim 16): one unit per workgroup.
+template <typename Tin, int DK, int DV, int NT, int CW, bool NT_STORE, bool NT_LOAD>
+__global__ __launch_bounds__(NT) void recurrent_kernel(RecArgs a) {
+    using G = RecGeom<DK, DV, NT, CW>;
+    extern __shared__ float lds[];
+    const int T = a.T;
+    const RecLds L = rec_lds<DK, CW, G::NW>(lds, T);
+    const Unit u = unit_of<G::NSPLIT, CW>(a, blockIdx.x);
+
+    // 1. state tile -> registers, issued first
+    float4 s[G::RPT];
+    load_tile<DK, DV, NT, CW, NT_LOAD>(a, u, s);
+
+    // 2. conv + SiLU of this unit's channels for every token of the block
+    const Tin* x = static_cast<const Tin*>(a.qkv);
+    const Tin* w = static_cast<const Tin*>(a.w);
+    const Tin* cin = static_cast<const Tin*>(a.conv_in);
+    Tin* cout = static_cast<Tin*>(a.conv_out);
+    for (int c = threadIdx.x; c < G::NCH; c += NT) {
+        int ch, stride;
+        float* dst;
+        bool owner;
+        fe_channel<DK, DV, CW>(a, u, L, c, &ch, &dst, &stride, &owner);
+        float wv[kConvK];
+#pragma unroll
+        for (int j = 0; j < kConvK; ++j) wv[j] = to_f32(w[static_cast<size_t>(ch) * kConvK + j]);
+        const Tin* st = cin + (static_cast<size_t>(u.b) * a.D + ch) * (kConvK - 1);
+        const Tin* xc = x + (static_cast<size_t>(u.b) * a.D + ch) * T;
+        float win[kConvK];
+#pragma unroll
+        for (int j = 0; j < kConvK - 1; ++j) win[j] = to_f32(st[j]);
+        for (int t = 0; t < T; ++t) {
+            win[kConvK - 1] = to_f32(xc[t]);
+            dst[t * stride] = conv_silu(wv, win);
+#pragma unroll
+            for (int j = 0; j < kConvK - 1; ++j) win[j] = win[j + 1];
+        }
+        if (cout != nullptr && owner) {
+            // new window: the K-1 most recent raw inputs of concat(state, x[0..T-1])
+            Tin* co = cout + (static_cast<size_t>(u.b) * a.D + ch) * (kConvK - 1);
+#pragma unroll
+            for (int j = 0; j < kConvK - 1; ++j) {
+                const int pos = T + j;  // position in the concatenated window
+                co[j] = (pos < kConvK - 1) ? st[pos] : xc[pos - (kConvK - 1)];
+            }
+        }
+    }
+    __syncthreads();
+    recur_tail<Tin, DK, DV, NT, CW, NT_STORE>(a, u, L, T, s);
 }
 
 // Commit: S_out[b,h] = S_snap[b, a_b, h]; the conv window after token a_b.
@@ -262,12 +313,13 @@ hipError_t launch_rec(const RecArgs& a, hipStream_t stream) {
                            dim3(a.B * a.Hv * (DV / CW)), dim3(NT), args, lds, stream);
 }
 
-// d = 128: 512 threads (8 waves) hold the 128 x 128 tile as 8 float4 per thread,
-// so 4 workgroups fit a CU and the 2048 workgroups of a B = 64, Hv = 32 decode
-// run in two full rounds. The state is streamed: it is written with
-// non-temporal stores (each tile is read once and written once per call, so
-// caching the writes only evicts useful lines); in a cold-cache sweep this
-// took the decode step from 67.7 us to 50.8 us.
+// d = 128: 512 threads (8 waves) hold the 128 x 128 tile as 8 float4 per thread.
+// The state is streamed: it is written with non-temporal stores (each tile is
+// read once and written once per call, so caching the writes only evicts useful
+// lines); in a cold-cache sweep this took the decode step from 67.7 us to
+// 50.8 us. (A persistent variant that prefetched the next tile measured the
+// same: reads and writes are both already streaming near the box's mixed
+// read/write limit.)
 hipError_t launch_recurrent(const RecArgs& a, int in_dtype, int d, hipStream_t stream) {
     if (d == 128) {
         return in_dtype == 1 ? launch_rec<bf16_t, 128, 128, 512, 128, true, false>(a, stream)
