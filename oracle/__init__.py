@@ -8,5 +8,5 @@ with numpy arrays; `build.py` compiles it with gcc.
 """
 from .oracle import (  # noqa: F401
     OracleParams, build_oracle, conv1d_silu, front_end, delta_rule, gdn_forward,
-    verify_commit, set_mutation, mutation, MUTATIONS, default_threads,
+    verify_commit, set_mutation, mutation, MUTATIONS, default_threads, gate_beta, gated_rmsnorm,
 )

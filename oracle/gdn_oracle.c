@@ -76,6 +76,9 @@ enum {
     MUT_QK_SWAPPED = 11,             /* Q and K channel blocks swapped */
     MUT_NO_SILU = 12,                /* conv output without SiLU */
     MUT_DECAY_AFTER_WRITE = 13,      /* decay applied after the write */
+    MUT_GATE_SIGN = 14,              /* gate = +exp(A_log) softplus(..) */
+    MUT_RMS_SUM = 15,                /* RMSNorm with the sum of squares, not the mean */
+    MUT_RMS_SIGMOID_GATE = 16,       /* output gated by sigmoid(z), not silu(z) */
 };
 static int g_mutation = 0;
 void orc_set_mutation(int m) { g_mutation = m; }
@@ -489,6 +492,49 @@ int orc_gdn_forward(const orc_params* p, int B, int L, const double* x, const do
                     out_c[q] = (pos < K - 1) ? st_c[pos] : x_c[pos - (K - 1)];
                 }
             }
+        }
+    }
+    return ORC_OK;
+}
+
+/* ---- gate / beta parameterisation -----------------------------------------------
+ * "MNN Model Support: Qwen3.5", §1.2, the paragraph after Step 5: beta is the
+ * sigmoid of a raw projection b, and the log-decay is
+ *   gate = -exp(A_log) * softplus(a + dt_bias)     (<= 0, so exp(gate) is in (0, 1])
+ * with A_log and dt_bias learned per V head. softplus(x) = log(1 + e^x).
+ * a, b: [n_tok, Hv]; A_log, dt_bias: [Hv]; outputs gate, beta: [n_tok, Hv]. */
+static double softplus(double x) { return x > 0 ? x + log1p(exp(-x)) : log1p(exp(x)); }
+
+int orc_gate_beta(int64_t n_tok, int Hv, const double* a, const double* b, const double* A_log,
+                  const double* dt_bias, double* gate, double* beta) {
+    if (n_tok < 0 || Hv <= 0 || !a || !b || !A_log || !dt_bias || !gate || !beta) return ORC_ERR_ARG;
+    for (int64_t t = 0; t < n_tok; ++t)
+        for (int h = 0; h < Hv; ++h) {
+            const int64_t i = t * Hv + h;
+            gate[i] = (g_mutation == MUT_GATE_SIGN ? 1.0 : -1.0) * exp(A_log[h]) * softplus(a[i] + dt_bias[h]);
+            beta[i] = 1.0 / (1.0 + exp(-b[i]));
+        }
+    return ORC_OK;
+}
+
+/* ---- gated RMSNorm -----------------------------------------------------------------
+ * "MNN Model Support: Qwen3.5", §2 "Gated RMSNorm": over the last dimension,
+ *   h = x * rsqrt(mean(x^2) + eps);  h = weight * h;  h = h * silu(gate)
+ * applied to the layer output per (token, V head) over d_v, the gate being z
+ * from in_proj_z. x, z, out: [n_rows, dv]; weight: [dv]. */
+int orc_gated_rmsnorm(int64_t n_rows, int dv, const double* x, const double* z, const double* weight,
+                      double eps, double* out) {
+    if (n_rows < 0 || dv <= 0 || !x || !z || !weight || !out) return ORC_ERR_ARG;
+    for (int64_t r = 0; r < n_rows; ++r) {
+        const double* xr = x + r * dv;
+        const double* zr = z + r * dv;
+        double ms = 0.0;
+        for (int j = 0; j < dv; ++j) ms += xr[j] * xr[j];
+        if (g_mutation != MUT_RMS_SUM) ms /= dv;
+        const double inv = 1.0 / sqrt(ms + eps);
+        for (int j = 0; j < dv; ++j) {
+            const double gz = (g_mutation == MUT_RMS_SIGMOID_GATE) ? 1.0 / (1.0 + exp(-zr[j])) : silu(zr[j]);
+            out[r * dv + j] = weight[j] * (xr[j] * inv) * gz;
         }
     }
     return ORC_OK;

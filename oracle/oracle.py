@@ -33,6 +33,9 @@ MUTATIONS = {
     "qk_swapped": 11,
     "no_silu": 12,
     "decay_after_write": 13,
+    "gate_sign": 14,
+    "rms_sum": 15,
+    "rms_sigmoid_gate": 16,
 }
 
 
@@ -64,8 +67,11 @@ def _load():
         lib.orc_front_end.argtypes = [P, I, I, P, P, P, P, I, P, P, P]
         lib.orc_gdn_forward.argtypes = [P, I, I, P, P, P, P, P, P, P, P, P, P, I, P, I]
         lib.orc_verify_commit.argtypes = [P, I, I, P, P, P, P, P, P]
+        lib.orc_gate_beta.argtypes = [ctypes.c_int64, I, P, P, P, P, P, P]
+        lib.orc_gated_rmsnorm.argtypes = [ctypes.c_int64, I, P, P, P, ctypes.c_double, P]
         for f in (lib.orc_delta_rule, lib.orc_conv1d_silu, lib.orc_front_end,
-                  lib.orc_gdn_forward, lib.orc_verify_commit):
+                  lib.orc_gdn_forward, lib.orc_verify_commit, lib.orc_gate_beta,
+                  lib.orc_gated_rmsnorm):
             f.restype = I
         _lib = lib
     return _lib
@@ -223,3 +229,25 @@ def verify_commit(p: OracleParams, accept_len, x, conv_in, snap):
     _check(_load().orc_verify_commit(ctypes.byref(pc), B, T, _ptr(acc), _ptr(x), _ptr(conv_in),
                                      _ptr(snap), _ptr(conv_out), _ptr(S_out)), "verify_commit")
     return S_out, conv_out
+
+
+def gate_beta(a, b, A_log, dt_bias):
+    """gate = -exp(A_log) softplus(a + dt_bias), beta = sigmoid(b). a, b [..., Hv]; A_log, dt_bias [Hv]."""
+    a, b, A_log, dt_bias = map(_f64, (a, b, A_log, dt_bias))
+    Hv = A_log.shape[0]
+    n = a.size // Hv
+    gate = np.zeros_like(a)
+    beta = np.zeros_like(b)
+    _check(_load().orc_gate_beta(n, Hv, _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias), _ptr(gate),
+                                 _ptr(beta)), "gate_beta")
+    return gate, beta
+
+
+def gated_rmsnorm(x, z, weight, eps):
+    """weight * x * rsqrt(mean(x^2) + eps) * silu(z) over the last dimension."""
+    x, z, weight = map(_f64, (x, z, weight))
+    dv = x.shape[-1]
+    out = np.zeros_like(x)
+    _check(_load().orc_gated_rmsnorm(x.size // dv, dv, _ptr(x), _ptr(z), _ptr(weight), float(eps),
+                                     _ptr(out)), "gated_rmsnorm")
+    return out

@@ -21,6 +21,9 @@ What pins what (passages of "MNN Model Support: Qwen3.5"):
     whose output identifies which K head each V head read.
   * whole layer: composition of the pinned pieces; carry invariants (split calls, ragged
     packing, snapshots, commit).
+  * §1.2 gate/beta parameterisation: torch softplus/sigmoid in fp64, closed forms
+    (softplus(0) = ln 2, sigmoid(0) = 1/2, sigmoid(b) + sigmoid(-b) = 1), gate <= 0.
+  * §2 gated RMSNorm: torch rms_norm and silu in fp64, scale invariance, zero gate.
 """
 from __future__ import annotations
 
@@ -427,9 +430,51 @@ def pin_verify_commit():
         assert np.array_equal(c_out[bb], r["conv_out"][0])
 
 
+# ---------------------------------------------------------------------------
+# gate/beta parameterisation and gated RMSNorm
+# ---------------------------------------------------------------------------
+def pin_gate_beta():
+    import torch
+    rng = np.random.default_rng(51)
+    Hv = 6
+    a = 3.0 * rng.standard_normal((5, Hv))
+    b = 3.0 * rng.standard_normal((5, Hv))
+    A_log = rng.standard_normal(Hv)
+    dt_bias = rng.standard_normal(Hv)
+    g, be = oracle.gate_beta(a, b, A_log, dt_bias)
+    ta = torch.from_numpy(a)
+    ref_g = (-torch.exp(torch.from_numpy(A_log)) * torch.nn.functional.softplus(ta + torch.from_numpy(dt_bias))).numpy()
+    ref_b = torch.sigmoid(torch.from_numpy(b)).numpy()
+    assert _rel(g, ref_g) < 1e-14 and _rel(be, ref_b) < 1e-14
+    assert np.all(g <= 0) and np.all((be > 0) & (be < 1))
+    # closed forms: a + dt_bias = 0 gives softplus = ln 2; A_log = 0 gives a unit factor
+    g0, b0 = oracle.gate_beta(-np.ones((1, 2)), np.zeros((1, 2)), np.zeros(2), np.ones(2))
+    assert np.allclose(g0, -math.log(2.0), rtol=0, atol=1e-15) and np.allclose(b0, 0.5, rtol=0, atol=1e-16)
+    _, bp = oracle.gate_beta(a, b, A_log, dt_bias)
+    _, bm = oracle.gate_beta(a, -b, A_log, dt_bias)
+    assert np.allclose(bp + bm, 1.0, rtol=0, atol=1e-15)
+
+
+def pin_gated_rmsnorm():
+    import torch
+    rng = np.random.default_rng(52)
+    dv = 16
+    x = rng.standard_normal((7, 3, dv))
+    z = rng.standard_normal((7, 3, dv))
+    w = 1.0 + 0.2 * rng.standard_normal(dv)
+    eps = 1e-6
+    out = oracle.gated_rmsnorm(x, z, w, eps)
+    tx, tz = torch.from_numpy(x), torch.from_numpy(z)
+    ref = (torch.nn.functional.rms_norm(tx, (dv,), torch.from_numpy(w), eps) * torch.nn.functional.silu(tz)).numpy()
+    assert _rel(out, ref) < 1e-14
+    # scale invariance (up to eps) and a zero gate
+    assert _rel(oracle.gated_rmsnorm(4.0 * x, z, w, 0.0), oracle.gated_rmsnorm(x, z, w, 0.0)) < 1e-14
+    assert np.array_equal(oracle.gated_rmsnorm(x, np.zeros_like(z), w, eps), np.zeros_like(x))
+
+
 ALL_PINS = [
     pin_hand_worked, pin_rational_brute_force, pin_kronecker_form, pin_chunked_form,
     pin_closed_forms, pin_lms_and_norm_bound, pin_conv_library, pin_conv_onehot_and_carry,
     pin_front_end_mapping_and_norms, pin_gqa_end_to_end_probe, pin_layer_composition,
-    pin_layer_carry_invariants, pin_verify_commit,
+    pin_layer_carry_invariants, pin_verify_commit, pin_gate_beta, pin_gated_rmsnorm,
 ]
