@@ -16,7 +16,9 @@ bracketed by HIP events on the launch stream for the per-kernel duration used
 by the roofline.
 
 Other workloads (--workload verify | prefill | ragged | commit) time the other
-entry points on their configurations; they print the same kind of JSON line.
+entry points on their configurations; --workload decode_fused times the decode
+step through gdn_decode_step_ex with the gate/beta prologue and the gated
+RMSNorm epilogue. They print the same kind of JSON line.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
 """
@@ -93,15 +95,22 @@ def run_timed(torch, step_fn, steps, warmup):
 # ---------------------------------------------------------------------------
 # decode (default)
 # ---------------------------------------------------------------------------
-def bench_decode(args, torch, gdn, gi):
+def bench_decode(args, torch, gdn, gi, fused=False):
     sh, w_ = gi.QWEN, gi.WORKLOADS[1]
     seed, B, NSTEP = w_.seed, gi.DECODE_B, gi.DECODE_STEPS
     p = gdn.GdnParams(sh.Hk, sh.Hv, sh.dk, sh.dv, sh.K, True, 1e-6, gdn.GDN_BF16)
     dev = lambda a, bf=True: (torch.from_numpy(a).cuda().to(torch.bfloat16) if bf else torch.from_numpy(a).cuda())
     log("generating decode inputs ...")
     xs = [dev(gi.qkv(sh, B, 1, seed, "bf16", step=s)) for s in range(NSTEP)]
-    gs = [dev(gi.gate(sh, B, 1, seed, "bf16", step=s)) for s in range(NSTEP)]
-    bs = [dev(gi.beta(sh, B, 1, seed, "bf16", step=s)) for s in range(NSTEP)]
+    if fused:   # raw a/b through the prologue, gated RMSNorm epilogue with z
+        gs = [dev(gi.a_raw(sh, B, 1, seed, "bf16", step=s)) for s in range(NSTEP)]
+        bs = [dev(gi.b_raw(sh, B, 1, seed, "bf16", step=s)) for s in range(NSTEP)]
+        zs = [dev(gi.z_gate(sh, B, 1, seed, "bf16", step=s)) for s in range(NSTEP)]
+        fus = [gdn.GdnFusion(dev(gi.a_log(sh, seed, "bf16")), dev(gi.dt_bias(sh, seed, "bf16")), z,
+                             dev(gi.norm_weight(sh, seed, "bf16")), 1e-6) for z in zs]
+    else:
+        gs = [dev(gi.gate(sh, B, 1, seed, "bf16", step=s)) for s in range(NSTEP)]
+        bs = [dev(gi.beta(sh, B, 1, seed, "bf16", step=s)) for s in range(NSTEP)]
     w = dev(gi.conv_weight(sh, seed, "bf16"))
     S0 = dev(gi.state0(sh, B, seed, 0.1), bf=False)
     c0 = dev(gi.conv_state0(sh, B, seed, 1.0, "bf16"))
@@ -116,7 +125,10 @@ def bench_decode(args, torch, gdn, gi):
             r = i % replicas
             ci, co = conv[r][par[r]], conv[r][1 - par[r]]
             j = i % NSTEP
-            gdn.gdn_decode_step(p, xs[j], gs[j], bs[j], w, ci, co, S[r], o)
+            if fused:
+                gdn.gdn_decode_step_ex(p, fus[j], xs[j], gs[j], bs[j], w, ci, co, S[r], o)
+            else:
+                gdn.gdn_decode_step(p, xs[j], gs[j], bs[j], w, ci, co, S[r], o)
             par[r] ^= 1
         return step
 
@@ -127,13 +139,16 @@ def bench_decode(args, torch, gdn, gi):
                   + sh.D * sh.K * 2                           # conv weight
                   + B * sh.Hv * 2 * 2                         # gate, beta
                   + B * sh.Hv * sh.dv * 4)                    # o
+    if fused:
+        bytes_step += B * sh.Hv * sh.dv * 2 + (2 * sh.Hv + sh.dv) * 2   # z; A_log, dt_bias, norm weight
     achieved = bytes_step / (kms * 1e-3) / 1e9
     digest = source_digest(["gdn_recurrent.hip", "gdn_common.hpp"])
-    traffic = traffic_from_counters("decode_B64_d128", digest)
+    traffic = traffic_from_counters("decode_fused_B64_d128" if fused else "decode_B64_d128", digest)
     res = {
         "metric": METRIC, "value": B * args.steps / wall, "unit": "tokens/s",
         "ms_per_step": 1e3 * wall / args.steps,
-        "config": {"workload": w_.name, "B": B, "Hk": sh.Hk, "Hv": sh.Hv, "dk": sh.dk, "dv": sh.dv,
+        "config": {"workload": w_.name + ("+gate_beta_prologue+gated_rmsnorm_epilogue" if fused else ""),
+                   "B": B, "Hk": sh.Hk, "Hv": sh.Hv, "dk": sh.dk, "dv": sh.dv,
                    "conv_K": sh.K, "inputs": "bf16", "state": "fp32",
                    "cache": "cold: 4 rotating state replicas"},
         "dtype": "f32",
@@ -283,7 +298,7 @@ def main():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "verify", "commit", "prefill", "ragged"])
+                    choices=["decode", "verify", "commit", "prefill", "ragged", "decode_fused"])
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--warm", action="store_true",
                     help="decode: also time the warm-cache rate (one state replica)")
@@ -295,7 +310,7 @@ def main():
         print(f"bench.py runs on one GPU only: the layer's path is built and measured on a single "
               f"MI355X (asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
-    defaults = {"decode": (256, 32), "verify": (50, 5), "commit": (50, 5), "prefill": (20, 3),
+    defaults = {"decode": (256, 32), "decode_fused": (256, 32), "verify": (50, 5), "commit": (50, 5), "prefill": (20, 3),
                 "ragged": (10, 2)}[args.workload]
     args.steps = defaults[0] if args.steps is None else args.steps
     args.warmup = defaults[1] if args.warmup is None else args.warmup
@@ -315,6 +330,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     fn = {"decode": bench_decode, "verify": bench_verify,
+          "decode_fused": lambda a, t, g, i: bench_decode(a, t, g, i, fused=True),
           "commit": lambda a, t, g, i: bench_verify(a, t, g, i, commit=True),
           "prefill": bench_prefill,
           "ragged": lambda a, t, g, i: bench_prefill(a, t, g, i, ragged=True)}[args.workload]

@@ -16,6 +16,13 @@ Value distributions (the tiny fp32 case and all bf16 cases use the same ones):
   S0           ~ N(0, 0.1^2) or zero          [N, Hv, dk, dv]  (always fp32)
   conv_state0  ~ N(0, 1) or zero              [N, D, K-1]
 
+Inputs of the optional prologue/epilogue fusions:
+  a_raw, b_raw ~ N(0, 1)                      [B, L, Hv]  (raw gate/beta projections)
+  A_log        = log(U(1, 16))                [Hv]
+  dt_bias      = softplus^-1(dt), log10(dt) ~ U(-3, -1)   [Hv]
+  z            ~ N(0, 1)                      [B, L, Hv, dv]
+  norm_weight  ~ 1 + N(0, 0.1^2)              [dv]
+
 Values are drawn in float64 and rounded once, by round-to-nearest-even, to the
 storage type (bf16 or fp32). All arrays are returned as float32 numpy arrays
 whose values are exactly representable in the storage type, so both sides see
@@ -29,6 +36,7 @@ import numpy as np
 
 # tensor ids of the per-tensor random streams
 TID_QKV, TID_W, TID_GATE, TID_BETA, TID_S0, TID_CONV0, TID_ACCEPT, TID_LENS = range(8)
+TID_A_RAW, TID_B_RAW, TID_A_LOG, TID_DT_BIAS, TID_Z, TID_NORM_W = range(8, 14)
 
 
 def round_bf16(x) -> np.ndarray:
@@ -108,6 +116,34 @@ def conv_state0(shape: Shape, N: int, seed: int, std: float, dtype: str) -> np.n
     if std == 0.0:
         return np.zeros((N, shape.D, shape.K - 1), np.float32)
     return round_to(_rng(seed, TID_CONV0).normal(0.0, std, (N, shape.D, shape.K - 1)), dtype)
+
+
+def a_raw(shape: Shape, B: int, L: int, seed: int, dtype: str, step: int | None = None) -> np.ndarray:
+    extra = () if step is None else (step,)
+    return round_to(_rng(seed, TID_A_RAW, *extra).standard_normal((B, L, shape.Hv)), dtype)
+
+
+def b_raw(shape: Shape, B: int, L: int, seed: int, dtype: str, step: int | None = None) -> np.ndarray:
+    extra = () if step is None else (step,)
+    return round_to(_rng(seed, TID_B_RAW, *extra).standard_normal((B, L, shape.Hv)), dtype)
+
+
+def a_log(shape: Shape, seed: int, dtype: str) -> np.ndarray:
+    return round_to(np.log(_rng(seed, TID_A_LOG).uniform(1.0, 16.0, shape.Hv)), dtype)
+
+
+def dt_bias(shape: Shape, seed: int, dtype: str) -> np.ndarray:
+    dt = 10.0 ** _rng(seed, TID_DT_BIAS).uniform(-3.0, -1.0, shape.Hv)
+    return round_to(dt + np.log(-np.expm1(-dt)), dtype)   # the x with log(1 + e^x) = dt
+
+
+def z_gate(shape: Shape, B: int, L: int, seed: int, dtype: str, step: int | None = None) -> np.ndarray:
+    extra = () if step is None else (step,)
+    return round_to(_rng(seed, TID_Z, *extra).standard_normal((B, L, shape.Hv, shape.dv)), dtype)
+
+
+def norm_weight(shape: Shape, seed: int, dtype: str) -> np.ndarray:
+    return round_to(1.0 + _rng(seed, TID_NORM_W).normal(0.0, 0.1, shape.dv), dtype)
 
 
 def accept_len(B: int, T: int, seed: int) -> np.ndarray:

@@ -87,6 +87,29 @@ typedef struct {
     int32_t in_dtype;       /* gdn_dtype of qkv, gate, beta, conv_weight, conv states */
 } gdn_params;
 
+/* Optional fusions. A NULL gdn_fusion pointer, or NULL fields, disable them.
+ *
+ * Prologue ("MNN Model Support: Qwen3.5", §1.2, the gate parameterisation after
+ * Step 5): when A_log is non-NULL, the `gate` and `beta` arguments of a call hold
+ * the raw projections a and b, and the kernels use, in fp32,
+ *     gate = -exp(A_log[h]) * softplus(a + dt_bias[h]),   beta = sigmoid(b).
+ *   A_log, dt_bias  [Hv] in_dtype (dt_bias must be non-NULL with A_log)
+ *
+ * Epilogue (§2 "Gated RMSNorm"): when z is non-NULL, `o` receives, for each
+ * (token, V head) over its dv channels,
+ *     norm_weight[j] * o[j] * rsqrt(mean_j(o^2) + norm_eps) * silu(z[j])
+ * instead of the raw recurrence output.
+ *   z            laid out like o ([B, L, Hv, dv]), in_dtype; must not overlap o
+ *   norm_weight  [dv] in_dtype (must be non-NULL with z)
+ *   norm_eps     >= 0, finite */
+typedef struct {
+    const void* A_log;
+    const void* dt_bias;
+    const void* z;
+    const void* norm_weight;
+    float norm_eps;
+} gdn_fusion;
+
 /* Human-readable name of a status code (static storage). */
 const char* gdn_status_string(gdn_status s);
 
@@ -194,6 +217,26 @@ gdn_status gdn_prefill(const gdn_params* p, int32_t B, int32_t L, const void* qk
                        const void* conv_state_in, void* conv_state_out, float* S, float* o,
                        const int32_t* cu_seqlens, int32_t N, int32_t chunk, void* workspace,
                        size_t workspace_bytes, void* stream);
+
+/*
+ * The same calls with the optional prologue/epilogue fusions of gdn_fusion
+ * (fusion may be NULL: identical to the calls above). Arguments, layouts and
+ * errors are as above; with a prologue `gate`/`beta` carry the raw a/b.
+ */
+gdn_status gdn_decode_step_ex(const gdn_params* p, const gdn_fusion* fusion, int32_t B,
+                              const void* qkv, const void* gate, const void* beta,
+                              const void* conv_weight, const void* conv_state_in,
+                              void* conv_state_out, float* S, float* o, void* stream);
+gdn_status gdn_verify_block_ex(const gdn_params* p, const gdn_fusion* fusion, int32_t B,
+                               int32_t T, const void* qkv, const void* gate, const void* beta,
+                               const void* conv_weight, const void* conv_state_in,
+                               const float* S_in, float* S_snap, float* o, void* stream);
+gdn_status gdn_prefill_ex(const gdn_params* p, const gdn_fusion* fusion, int32_t B, int32_t L,
+                          const void* qkv, const void* gate, const void* beta,
+                          const void* conv_weight, const void* conv_state_in,
+                          void* conv_state_out, float* S, float* o, const int32_t* cu_seqlens,
+                          int32_t N, int32_t chunk, void* workspace, size_t workspace_bytes,
+                          void* stream);
 
 #ifdef __cplusplus
 }

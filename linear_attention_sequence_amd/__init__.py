@@ -25,7 +25,8 @@ STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_DTYPE"
 
 # every symbol include/gdn.h declares
 EXPORTS = ("gdn_status_string", "gdn_version", "gdn_conv1d_silu", "gdn_decode_step",
-           "gdn_verify_block", "gdn_verify_commit", "gdn_prefill_workspace_size", "gdn_prefill")
+           "gdn_verify_block", "gdn_verify_commit", "gdn_prefill_workspace_size", "gdn_prefill",
+           "gdn_decode_step_ex", "gdn_verify_block_ex", "gdn_prefill_ex")
 
 
 class GdnError(RuntimeError):
@@ -66,6 +67,33 @@ class GdnParams:
                         self.conv_kernel, int(self.use_qk_l2norm), self.l2norm_eps, self.in_dtype)
 
 
+class _CFusion(ctypes.Structure):
+    _fields_ = [("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p), ("z", ctypes.c_void_p),
+                ("norm_weight", ctypes.c_void_p), ("norm_eps", ctypes.c_float)]
+
+
+@dataclasses.dataclass
+class GdnFusion:
+    """gdn_fusion: optional gate/beta prologue (A_log, dt_bias [Hv]) and gated-RMSNorm
+    epilogue (z shaped like o, norm_weight [dv]); tensors in the params' input dtype."""
+    A_log: torch.Tensor | None = None
+    dt_bias: torch.Tensor | None = None
+    z: torch.Tensor | None = None
+    norm_weight: torch.Tensor | None = None
+    norm_eps: float = 1e-6
+
+    def c(self, p: "GdnParams") -> _CFusion:
+        for t, n in ((self.A_log, "A_log"), (self.dt_bias, "dt_bias"), (self.z, "z"),
+                     (self.norm_weight, "norm_weight")):
+            _expect(t, p.torch_dtype, n)
+        return _CFusion(_ptr(self.A_log), _ptr(self.dt_bias), _ptr(self.z), _ptr(self.norm_weight),
+                        float(self.norm_eps))
+
+
+def _fusion_ref(p, fusion):
+    return None if fusion is None else ctypes.byref(fusion.c(p))
+
+
 _lib = None
 
 
@@ -91,8 +119,12 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.gdn_prefill_workspace_size.argtypes = [PP, I32, I32, I32, I32]
     lib.gdn_prefill_workspace_size.restype = SZ
     lib.gdn_prefill.argtypes = [PP, I32, I32, V, V, V, V, V, V, V, V, V, I32, I32, V, SZ, V]
+    PF = ctypes.POINTER(_CFusion)
+    lib.gdn_decode_step_ex.argtypes = [PP, PF, I32, V, V, V, V, V, V, V, V, V]
+    lib.gdn_verify_block_ex.argtypes = [PP, PF, I32, I32, V, V, V, V, V, V, V, V, V]
+    lib.gdn_prefill_ex.argtypes = [PP, PF, I32, I32, V, V, V, V, V, V, V, V, V, I32, I32, V, SZ, V]
     for fn in ("gdn_conv1d_silu", "gdn_decode_step", "gdn_verify_block", "gdn_verify_commit",
-               "gdn_prefill"):
+               "gdn_prefill", "gdn_decode_step_ex", "gdn_verify_block_ex", "gdn_prefill_ex"):
         getattr(lib, fn).restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -158,6 +190,20 @@ def gdn_decode_step(p: GdnParams, qkv, gate, beta, conv_weight, conv_state_in, c
           _stream(stream))
 
 
+def gdn_decode_step_ex(p: GdnParams, fusion: GdnFusion | None, qkv, gate, beta, conv_weight,
+                       conv_state_in, conv_state_out, S, o, stream=None):
+    """gdn_decode_step with the gdn_fusion prologue/epilogue (gate/beta hold raw a/b with A_log)."""
+    for t, n in ((qkv, "qkv"), (gate, "gate"), (beta, "beta"), (conv_weight, "conv_weight"),
+                 (conv_state_in, "conv_state_in"), (conv_state_out, "conv_state_out")):
+        _expect(t, p.torch_dtype, n)
+    _expect(S, torch.float32, "S")
+    _expect(o, torch.float32, "o")
+    B = qkv.shape[0]
+    _call("gdn_decode_step_ex", ctypes.byref(p.c()), _fusion_ref(p, fusion), B, _ptr(qkv),
+          _ptr(gate), _ptr(beta), _ptr(conv_weight), _ptr(conv_state_in), _ptr(conv_state_out),
+          _ptr(S), _ptr(o), _stream(stream))
+
+
 def gdn_verify_block(p: GdnParams, qkv, gate, beta, conv_weight, conv_state_in, S_in, S_snap, o,
                      stream=None):
     """T tokens per sequence with a state snapshot after each. qkv [B,D,T]; S_snap [B,T,Hv,dk,dv]."""
@@ -170,6 +216,20 @@ def gdn_verify_block(p: GdnParams, qkv, gate, beta, conv_weight, conv_state_in, 
     _call("gdn_verify_block", ctypes.byref(p.c()), B, T, _ptr(qkv), _ptr(gate), _ptr(beta),
           _ptr(conv_weight), _ptr(conv_state_in), _ptr(S_in), _ptr(S_snap), _ptr(o),
           _stream(stream))
+
+
+def gdn_verify_block_ex(p: GdnParams, fusion: GdnFusion | None, qkv, gate, beta, conv_weight,
+                        conv_state_in, S_in, S_snap, o, stream=None):
+    """gdn_verify_block with the gdn_fusion prologue/epilogue."""
+    for t, n in ((qkv, "qkv"), (gate, "gate"), (beta, "beta"), (conv_weight, "conv_weight"),
+                 (conv_state_in, "conv_state_in")):
+        _expect(t, p.torch_dtype, n)
+    for t, n in ((S_in, "S_in"), (S_snap, "S_snap"), (o, "o")):
+        _expect(t, torch.float32, n)
+    B, _, T = qkv.shape
+    _call("gdn_verify_block_ex", ctypes.byref(p.c()), _fusion_ref(p, fusion), B, T, _ptr(qkv),
+          _ptr(gate), _ptr(beta), _ptr(conv_weight), _ptr(conv_state_in), _ptr(S_in),
+          _ptr(S_snap), _ptr(o), _stream(stream))
 
 
 def gdn_verify_commit(p: GdnParams, accept_len, qkv, conv_state_in, S_snap, conv_state_out, S_out,
@@ -204,6 +264,24 @@ def gdn_prefill(p: GdnParams, qkv, gate, beta, conv_weight, conv_state_in, conv_
     _call("gdn_prefill", ctypes.byref(p.c()), B, L, _ptr(qkv), _ptr(gate), _ptr(beta),
           _ptr(conv_weight), _ptr(conv_state_in), _ptr(conv_state_out), _ptr(S), _ptr(o),
           _ptr(cu_seqlens), N, chunk, _ptr(workspace), ws_bytes, _stream(stream))
+
+
+def gdn_prefill_ex(p: GdnParams, fusion: GdnFusion | None, qkv, gate, beta, conv_weight,
+                   conv_state_in, conv_state_out, S, o, workspace, cu_seqlens=None, chunk: int = 64,
+                   stream=None):
+    """gdn_prefill with the gdn_fusion prologue/epilogue."""
+    for t, n in ((qkv, "qkv"), (gate, "gate"), (beta, "beta"), (conv_weight, "conv_weight"),
+                 (conv_state_in, "conv_state_in"), (conv_state_out, "conv_state_out")):
+        _expect(t, p.torch_dtype, n)
+    _expect(S, torch.float32, "S")
+    _expect(o, torch.float32, "o")
+    _expect(cu_seqlens, torch.int32, "cu_seqlens")
+    B, _, L = qkv.shape
+    N = S.shape[0]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _call("gdn_prefill_ex", ctypes.byref(p.c()), _fusion_ref(p, fusion), B, L, _ptr(qkv),
+          _ptr(gate), _ptr(beta), _ptr(conv_weight), _ptr(conv_state_in), _ptr(conv_state_out),
+          _ptr(S), _ptr(o), _ptr(cu_seqlens), N, chunk, _ptr(workspace), ws_bytes, _stream(stream))
 
 
 def prefill_workspace(p: GdnParams, B: int, L: int, N: int, chunk: int = 64, device="cuda"):

@@ -65,6 +65,23 @@ size_t tile_bytes(const gdn_params* p) {
 
 gdn_status launched(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH; }
 
+// gdn_fusion -> kernel view; checks that each enabled fusion has all its arrays.
+gdn_status fusion_of(const gdn_fusion* f, gdn::Fusion* out) {
+    *out = gdn::Fusion{nullptr, nullptr, nullptr, nullptr, 0.f};
+    if (f == nullptr) return GDN_OK;
+    if (f->A_log != nullptr && f->dt_bias == nullptr) return GDN_ERR_NULL;
+    if (f->z != nullptr) {
+        if (f->norm_weight == nullptr) return GDN_ERR_NULL;
+        if (!std::isfinite(f->norm_eps) || f->norm_eps < 0.f) return GDN_ERR_SHAPE;
+    }
+    out->A_log = f->A_log;
+    out->dt_bias = f->A_log ? f->dt_bias : nullptr;
+    out->z = f->z;
+    out->norm_w = f->z ? f->norm_weight : nullptr;
+    out->norm_eps = f->z ? f->norm_eps : 0.f;
+    return GDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -122,13 +139,15 @@ gdn_status gdn_conv1d_silu(const gdn_params* p, int32_t B, int32_t L, const void
     return GDN_OK;
 }
 
-static gdn_status recurrent_common(const gdn_params* p, int32_t B, int32_t T, const void* qkv,
-                                   const void* gate, const void* beta, const void* conv_weight,
-                                   const void* conv_state_in, void* conv_state_out,
-                                   const float* S_in, float* S_out, float* o, void* stream,
-                                   bool in_place) {
+static gdn_status recurrent_common(const gdn_params* p, const gdn_fusion* fusion, int32_t B,
+                                   int32_t T, const void* qkv, const void* gate, const void* beta,
+                                   const void* conv_weight, const void* conv_state_in,
+                                   void* conv_state_out, const float* S_in, float* S_out, float* o,
+                                   void* stream, bool in_place) {
     gdn_status st = check_params(p);
     if (st != GDN_OK) return st;
+    gdn::Fusion fu;
+    if ((st = fusion_of(fusion, &fu)) != GDN_OK) return st;
     if (B < 0) return GDN_ERR_SHAPE;
     if (T < 1) return GDN_ERR_SHAPE;
     if (T > kMaxT) return GDN_ERR_UNSUPPORTED;
@@ -153,27 +172,47 @@ static gdn_status recurrent_common(const gdn_params* p, int32_t B, int32_t T, co
         {conv_state_out, conv_state_out ? static_cast<size_t>(B) * D * (kK - 1) * es : 0, true},
         {S_out, state * T, true},
         {o, static_cast<size_t>(B) * T * Hv * p->head_v_dim * sizeof(float), true},
+        {fu.A_log, fu.A_log ? Hv * es : 0, false},
+        {fu.dt_bias, fu.dt_bias ? Hv * es : 0, false},
+        {fu.z, fu.z ? static_cast<size_t>(B) * T * Hv * p->head_v_dim * es : 0, false},
+        {fu.norm_w, fu.norm_w ? static_cast<size_t>(p->head_v_dim) * es : 0, false},
     };
     if ((st = check_alias(bufs)) != GDN_OK) return st;
     const gdn::RecArgs a{B, T, p->num_k_heads, p->num_v_heads, static_cast<int>(D),
                          p->use_qk_l2norm, p->l2norm_eps, qkv, gate, beta, conv_weight,
-                         conv_state_in, conv_state_out, S_in, S_out, o};
+                         conv_state_in, conv_state_out, S_in, S_out, o, fu};
     return launched(gdn::launch_recurrent(a, p->in_dtype, p->head_k_dim, static_cast<hipStream_t>(stream)));
 }
 
 gdn_status gdn_decode_step(const gdn_params* p, int32_t B, const void* qkv, const void* gate,
                            const void* beta, const void* conv_weight, const void* conv_state_in,
                            void* conv_state_out, float* S, float* o, void* stream) {
-    return recurrent_common(p, B, 1, qkv, gate, beta, conv_weight, conv_state_in, conv_state_out,
-                            S, S, o, stream, true);
+    return recurrent_common(p, nullptr, B, 1, qkv, gate, beta, conv_weight, conv_state_in,
+                            conv_state_out, S, S, o, stream, true);
+}
+
+gdn_status gdn_decode_step_ex(const gdn_params* p, const gdn_fusion* fusion, int32_t B,
+                              const void* qkv, const void* gate, const void* beta,
+                              const void* conv_weight, const void* conv_state_in,
+                              void* conv_state_out, float* S, float* o, void* stream) {
+    return recurrent_common(p, fusion, B, 1, qkv, gate, beta, conv_weight, conv_state_in,
+                            conv_state_out, S, S, o, stream, true);
 }
 
 gdn_status gdn_verify_block(const gdn_params* p, int32_t B, int32_t T, const void* qkv,
                             const void* gate, const void* beta, const void* conv_weight,
                             const void* conv_state_in, const float* S_in, float* S_snap,
                             float* o, void* stream) {
-    return recurrent_common(p, B, T, qkv, gate, beta, conv_weight, conv_state_in, nullptr, S_in,
-                            S_snap, o, stream, false);
+    return recurrent_common(p, nullptr, B, T, qkv, gate, beta, conv_weight, conv_state_in, nullptr,
+                            S_in, S_snap, o, stream, false);
+}
+
+gdn_status gdn_verify_block_ex(const gdn_params* p, const gdn_fusion* fusion, int32_t B,
+                               int32_t T, const void* qkv, const void* gate, const void* beta,
+                               const void* conv_weight, const void* conv_state_in,
+                               const float* S_in, float* S_snap, float* o, void* stream) {
+    return recurrent_common(p, fusion, B, T, qkv, gate, beta, conv_weight, conv_state_in, nullptr,
+                            S_in, S_snap, o, stream, false);
 }
 
 gdn_status gdn_verify_commit(const gdn_params* p, int32_t B, int32_t T,
@@ -236,9 +275,22 @@ gdn_status gdn_prefill(const gdn_params* p, int32_t B, int32_t L, const void* qk
                        const void* conv_state_in, void* conv_state_out, float* S, float* o,
                        const int32_t* cu_seqlens, int32_t N, int32_t chunk, void* workspace,
                        size_t workspace_bytes, void* stream) {
+    return gdn_prefill_ex(p, nullptr, B, L, qkv, gate, beta, conv_weight, conv_state_in,
+                          conv_state_out, S, o, cu_seqlens, N, chunk, workspace, workspace_bytes,
+                          stream);
+}
+
+gdn_status gdn_prefill_ex(const gdn_params* p, const gdn_fusion* fusion, int32_t B, int32_t L,
+                          const void* qkv, const void* gate, const void* beta,
+                          const void* conv_weight, const void* conv_state_in,
+                          void* conv_state_out, float* S, float* o, const int32_t* cu_seqlens,
+                          int32_t N, int32_t chunk, void* workspace, size_t workspace_bytes,
+                          void* stream) {
     const bool ragged = cu_seqlens != nullptr;
     gdn_status st = prefill_check_sizes(p, B, L, N, chunk, ragged);
     if (st != GDN_OK) return st;
+    gdn::Fusion fu;
+    if ((st = fusion_of(fusion, &fu)) != GDN_OK) return st;
     if (N == 0) return GDN_OK;
     // with no tokens (B*L == 0) qkv, gate, beta and o may be empty (NULL): S is kept
     // and the conv window copied
@@ -265,12 +317,16 @@ gdn_status gdn_prefill(const gdn_params* p, int32_t B, int32_t L, const void* qk
         {S, static_cast<size_t>(N) * Hv * tile_bytes(p), true},
         {o, static_cast<size_t>(B) * L * Hv * p->head_v_dim * sizeof(float), true},
         {workspace, need, true},
+        {fu.A_log, fu.A_log ? Hv * es : 0, false},
+        {fu.dt_bias, fu.dt_bias ? Hv * es : 0, false},
+        {fu.z, fu.z ? static_cast<size_t>(B) * L * Hv * p->head_v_dim * es : 0, false},
+        {fu.norm_w, fu.norm_w ? static_cast<size_t>(p->head_v_dim) * es : 0, false},
     };
     if ((st = check_alias(bufs)) != GDN_OK) return st;
     const gdn::PrefillArgs a{B, L, N, p->num_k_heads, p->num_v_heads, static_cast<int>(D), chunk,
                              p->use_qk_l2norm, p->l2norm_eps, qkv, gate, beta, conv_weight,
                              conv_state_in, conv_state_out, S, o, cu_seqlens, workspace,
-                             workspace_bytes};
+                             workspace_bytes, fu};
     return launched(gdn::launch_prefill(a, p->in_dtype, p->head_k_dim, static_cast<hipStream_t>(stream)));
 }
 

@@ -28,6 +28,21 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// Sum over the 64 lanes of a wavefront, returned wave-uniform (in scalar
+// registers): DPP adds within quads (lanes ^1, ^2) and rows of 16 (rotate by 4,
+// then 8), then the four row totals are read out and added in row order.
+__device__ __forceinline__ float wave_sum_uniform(float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false));  // row_ror:4
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));  // row_ror:8
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
 // Depthwise causal conv of one channel at one position followed by SiLU:
 // silu(sum_j w[j] * win[j]) where win[K-1] is the current token. The sum is
 // taken in tap order with explicit fused multiply-adds.
@@ -36,6 +51,48 @@ __device__ __forceinline__ float conv_silu(const float* w, const float* win) {
 #pragma unroll
     for (int j = 1; j < kConvK; ++j) acc = __fmaf_rn(w[j], win[j], acc);
     return acc / (1.0f + expf(-acc));
+}
+
+// Short-sequence transcendental forms for the fusion prologue/epilogue, built on
+// the hardware exp2/log2/rcp/rsqrt instructions (about 1 ulp each), so that the
+// fused kernels keep the register budget of the plain ones.
+__device__ __forceinline__ float exp_hw(float x) {
+    return __builtin_amdgcn_exp2f(x * 1.44269504088896341f);   // e^x = 2^(x log2 e)
+}
+
+// log(1 + y) for y >= 0 with the compensated form log(u) * y / (u - 1), u = 1 + y
+// (Goldberg, "What every computer scientist should know about floating-point
+// arithmetic", Theorem 4): the rounding of 1 + y cancels out of the ratio.
+__device__ __forceinline__ float log1p_hw(float y) {
+    const float u = 1.0f + y;
+    if (u == 1.0f) return y;
+    return __builtin_amdgcn_logf(u) * 0.693147180559945309f * (y * __builtin_amdgcn_rcpf(u - 1.0f));
+}
+
+// softplus(x) = max(x, 0) + log(1 + e^-|x|)
+__device__ __forceinline__ float softplus_hw(float x) {
+    return fmaxf(x, 0.f) + log1p_hw(exp_hw(-fabsf(x)));
+}
+
+__device__ __forceinline__ float sigmoid_hw(float x) {
+    return __builtin_amdgcn_rcpf(1.0f + exp_hw(-x));
+}
+
+// gate and beta of V head h at flat index idx, with the optional prologue
+// gate = -exp(A_log[h]) softplus(a + dt_bias[h]), beta = sigmoid(b) when A_log is set
+// (then `gate`/`beta` hold the raw a/b).
+template <typename Tin>
+__device__ __forceinline__ void gate_beta_at(const void* gate, const void* beta, const void* A_log,
+                                             const void* dt_bias, size_t idx, int h, float* g, float* b) {
+    float gv = to_f32(static_cast<const Tin*>(gate)[idx]);
+    float bv = to_f32(static_cast<const Tin*>(beta)[idx]);
+    if (A_log != nullptr) {
+        gv = -exp_hw(to_f32(static_cast<const Tin*>(A_log)[h])) *
+             softplus_hw(gv + to_f32(static_cast<const Tin*>(dt_bias)[h]));
+        bv = sigmoid_hw(bv);
+    }
+    *g = gv;
+    *b = bv;
 }
 
 // Sequence n of a launch: row, first token and length. With cu_seqlens the
@@ -49,6 +106,20 @@ __device__ __forceinline__ Seg segment_of(int n, int L, const int32_t* cu) {
     b = b < 0 ? 0 : (b > L ? L : b);
     s.row = 0; s.start = a; s.len = b > a ? b - a : 0;
     return s;
+}
+
+// Sequence that owns token p of row 0 under cu_seqlens (clamped entries), or -1.
+__device__ __forceinline__ int token_owner(int p, int L, int N, const int32_t* cu) {
+    int lo = 0, hi = N - 1, n = -1;
+    while (lo <= hi) {  // last n whose clamped start is <= p
+        const int mid = (lo + hi) >> 1;
+        int st = cu[mid];
+        st = st < 0 ? 0 : (st > L ? L : st);
+        if (st <= p) { n = mid; lo = mid + 1; } else { hi = mid - 1; }
+    }
+    if (n < 0) return -1;
+    const Seg sg = segment_of(n, L, cu);
+    return p < sg.start + sg.len ? n : -1;
 }
 
 }  // namespace gdn

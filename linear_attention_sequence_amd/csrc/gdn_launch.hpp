@@ -8,6 +8,16 @@
 
 namespace gdn {
 
+// Optional prologue (A_log != nullptr: gate/beta hold the raw a/b) and epilogue
+// (z != nullptr: gated RMSNorm of o). See gdn_fusion in gdn.h.
+struct Fusion {
+    const void* A_log;      // [Hv]
+    const void* dt_bias;    // [Hv]
+    const void* z;          // like o
+    const void* norm_w;     // [dv]
+    float norm_eps;
+};
+
 // decode (T = 1, S_out == S_in allowed) and verify (S_out = snapshots)
 struct RecArgs {
     int B, T, Hk, Hv, D;
@@ -22,6 +32,7 @@ struct RecArgs {
     const float* S_in;    // [B, Hv, dk, dv]
     float* S_out;         // [B, T, Hv, dk, dv]
     float* o;             // [B, T, Hv, dv]
+    Fusion fu;
 };
 
 struct CommitArgs {
@@ -59,6 +70,7 @@ struct PrefillArgs {
     const int32_t* cu;       // [N+1] or nullptr
     void* ws;                // workspace
     size_t ws_bytes;
+    Fusion fu;
 };
 
 hipError_t launch_recurrent(const RecArgs& a, int in_dtype, int d, hipStream_t stream);
@@ -69,5 +81,7 @@ size_t prefill_workspace_bytes(int B, int L, int N, int Hk, int Hv, int d, int c
 hipError_t launch_prefill(const PrefillArgs& a, int in_dtype, int d, hipStream_t stream);
 size_t prefill_mfma_workspace_bytes(int B, int L, int N, int Hk, int Hv);
 hipError_t launch_prefill_mfma(const PrefillArgs& a, int in_dtype, hipStream_t stream);
+// gated RMSNorm of o in place over the tokens of every sequence (prefill epilogue)
+hipError_t launch_prefill_epilogue(const PrefillArgs& a, int in_dtype, int d, hipStream_t stream);
 
 }  // namespace gdn

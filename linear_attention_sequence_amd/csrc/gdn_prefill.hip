@@ -210,8 +210,10 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, Prefi
     const Tin* beta = static_cast<const Tin*>(a.beta);
     const int tid = threadIdx.x;
     if (tid < C) {
-        s_g[tid] = tid < nt ? to_f32(gate[(tok0 + tid) * a.Hv + h]) : 0.f;
-        s_b[tid] = tid < nt ? to_f32(beta[(tok0 + tid) * a.Hv + h]) : 0.f;
+        float gv = 0.f, bv = 0.f;
+        if (tid < nt) gate_beta_at<Tin>(gate, beta, a.fu.A_log, a.fu.dt_bias, (tok0 + tid) * a.Hv + h, h, &gv, &bv);
+        s_g[tid] = gv;
+        s_b[tid] = bv;
     }
     __syncthreads();
     if (tid == 0) {
@@ -414,8 +416,57 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, int in_dtype, hipStream
     return launch_conv_state(ca, in_dtype, stream);
 }
 
-hipError_t launch_prefill(const PrefillArgs& a, int in_dtype, int d, hipStream_t stream) {
-    if (a.chunk != 64) return hipErrorInvalidValue;
+// Gated RMSNorm of the prefill output in place (the epilogue of gdn_fusion):
+// one wave per (token, V head) row over its DV channels; tokens outside every
+// sequence are left untouched.
+template <typename Tin, int DV>
+__global__ __launch_bounds__(256) void gated_rmsnorm_kernel(PrefillArgs a) {
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const long long row = static_cast<long long>(blockIdx.x) * 4 + wave;   // tok * Hv + h
+    if (row >= static_cast<long long>(a.B) * a.L * a.Hv) return;           // whole wave
+    const long long tok = row / a.Hv;
+    const int p = static_cast<int>(tok % a.L);
+    if (a.cu != nullptr && token_owner(p, a.L, a.N, a.cu) < 0) return;     // whole wave
+    float* o = a.o + row * DV;
+    const Tin* z = static_cast<const Tin*>(a.fu.z) + row * DV;
+    const Tin* w = static_cast<const Tin*>(a.fu.norm_w);
+    constexpr int PER = (DV + kWave - 1) / kWave;
+    float v[PER];
+    float ss = 0.f;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        const int j = lane + q * kWave;
+        v[q] = j < DV ? o[j] : 0.f;
+        ss = __fmaf_rn(v[q], v[q], ss);
+    }
+    ss = wave_sum(ss);
+    const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / DV) + a.fu.norm_eps);
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        const int j = lane + q * kWave;
+        if (j < DV) {
+            const float zv = to_f32(z[j]);
+            o[j] = to_f32(w[j]) * (v[q] * inv) * (zv * sigmoid_hw(zv));
+        }
+    }
+}
+
+template <typename Tin, int DV>
+static hipError_t launch_epi_t(const PrefillArgs& a, hipStream_t stream) {
+    const long long rows = static_cast<long long>(a.B) * a.L * a.Hv;
+    if (rows == 0) return hipSuccess;
+    if ((rows + 3) / 4 > 0x7fffffffLL) return hipErrorInvalidValue;
+    void* args[] = {const_cast<PrefillArgs*>(&a)};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&gated_rmsnorm_kernel<Tin, DV>),
+                           dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), args, 0, stream);
+}
+
+hipError_t launch_prefill_epilogue(const PrefillArgs& a, int in_dtype, int d, hipStream_t stream) {
+    if (d == 128) return in_dtype == 1 ? launch_epi_t<bf16_t, 128>(a, stream) : launch_epi_t<float, 128>(a, stream);
+    return in_dtype == 1 ? launch_epi_t<bf16_t, 16>(a, stream) : launch_epi_t<float, 16>(a, stream);
+}
+
+static hipError_t launch_prefill_core(const PrefillArgs& a, int in_dtype, int d, hipStream_t stream) {
     // bf16 inputs run the dense products on fp16 MFMA (within the bf16 error
     // budget); fp32 inputs keep every operation in fp32 on the vector ALUs.
     if (d == 128) {
@@ -424,6 +475,13 @@ hipError_t launch_prefill(const PrefillArgs& a, int in_dtype, int d, hipStream_t
     }
     return in_dtype == 1 ? launch_prefill_t<bf16_t, 16>(a, in_dtype, stream)
                          : launch_prefill_t<float, 16>(a, in_dtype, stream);
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, int in_dtype, int d, hipStream_t stream) {
+    if (a.chunk != 64) return hipErrorInvalidValue;
+    hipError_t e = launch_prefill_core(a, in_dtype, d, stream);
+    if (e == hipSuccess && a.fu.z != nullptr) e = launch_prefill_epilogue(a, in_dtype, d, stream);
+    return e;
 }
 
 }  // namespace gdn

@@ -312,8 +312,10 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a, Ws ws) {
         }
     }
     if (tid < C) {
-        s_g[tid] = tid < nt ? to_f32(gate[(tok0 + tid) * a.Hv + h]) : 0.f;
-        s_b[tid] = tid < nt ? to_f32(beta[(tok0 + tid) * a.Hv + h]) : 0.f;
+        float gv = 0.f, bv = 0.f;
+        if (tid < nt) gate_beta_at<Tin>(gate, beta, a.fu.A_log, a.fu.dt_bias, (tok0 + tid) * a.Hv + h, h, &gv, &bv);
+        s_g[tid] = gv;
+        s_b[tid] = bv;
     }
     // q rows of this wave's 16-token tile, straight into registers (A operands)
     f16x8 aq[4];

@@ -44,7 +44,7 @@ struct RecGeom {
 };
 
 struct RecLds {
-    float *sq, *sk, *sv, *s_alpha, *s_beta, *s_kq, *red, *s_delta;
+    float *sq, *sk, *sv, *s_alpha, *s_beta, *s_kq, *red, *s_delta, *s_rms, *s_o, *s_gz;
 };
 
 template <int DK, int CW, int NW>
@@ -58,14 +58,18 @@ __device__ __forceinline__ RecLds rec_lds(float* lds, int T) {
     L.s_kq = L.s_beta + T;               // [T] k_hat . q_hat
     L.red = L.s_kq + T;                  // [NW][CG][8] partial dot products
     L.s_delta = L.red + NW * (CW / 4) * 8;  // [CW]
+    L.s_rms = L.s_delta + CW;               // [4] per-wave sums of o^2 (gated RMSNorm)
+    L.s_o = L.s_rms + 4;                    // [CW] raw output of the token (gated RMSNorm)
+    L.s_gz = L.s_o + CW;                    // [T][CW] norm_weight * silu(z) (gated RMSNorm)
     return L;
 }
 
-template <int DK, int CW, int NT>
+template <int DK, int CW, int NT, bool EPI>
 size_t recurrent_lds_bytes(int T) {
     constexpr int CG = CW / 4;
     constexpr int NW = NT / kWave;
-    return sizeof(float) * (static_cast<size_t>(T) * (2 * DK + CW) + 3 * T + NW * CG * 8 + CW);
+    return sizeof(float) * (static_cast<size_t>(T) * (2 * DK + CW) + 3 * T + NW * CG * 8 + CW + 4 +
+                            (EPI ? static_cast<size_t>(T + 1) * CW : 0));
 }
 
 // Which (sequence, V head, column slice) a unit index names.
@@ -122,14 +126,15 @@ __device__ __forceinline__ void load_tile(const RecArgs& a, const Unit& u, float
 // Steps 3-5 once the conv outputs of every token sit in LDS: L2 norms, the q
 // scale and k.q (one wave per token), then the recurrence token by token on the
 // register tile, writing the state after each token and the outputs.
-template <typename Tin, int DK, int DV, int NT, int CW, bool NT_STORE>
+template <typename Tin, int DK, int DV, int NT, int CW, bool NT_STORE, bool PRO, bool EPI>
 __device__ __forceinline__ void recur_tail(const RecArgs& a, const Unit& u, const RecLds& L, int T,
                                            float4 (&s)[RecGeom<DK, DV, NT, CW>::RPT]) {
     using G = RecGeom<DK, DV, NT, CW>;
     constexpr int CG = G::CG, RG = G::RG, RPT = G::RPT, NW = G::NW;
     const int tid = threadIdx.x;
     const int cg = tid % CG, rg = tid / CG;
-    const int lane = tid % kWave, wave = tid / kWave;
+    const int lane = tid % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform
     const Tin* gate = static_cast<const Tin*>(a.gate);
     const Tin* beta = static_cast<const Tin*>(a.beta);
     const float qscale = 1.0f / sqrtf(static_cast<float>(DK));
@@ -153,8 +158,15 @@ __device__ __forceinline__ void recur_tail(const RecArgs& a, const Unit& u, cons
         }
         if (lane == 0) {
             const size_t gi = (static_cast<size_t>(u.b) * T + t) * a.Hv + u.h;
-            L.s_alpha[t] = expf(to_f32(gate[gi]));
-            L.s_beta[t] = to_f32(beta[gi]);
+            float gv, bv;
+            if constexpr (PRO) {
+                gate_beta_at<Tin>(gate, beta, a.fu.A_log, a.fu.dt_bias, gi, u.h, &gv, &bv);
+            } else {
+                gv = to_f32(gate[gi]);
+                bv = to_f32(beta[gi]);
+            }
+            L.s_alpha[t] = expf(gv);
+            L.s_beta[t] = bv;
             L.s_kq[t] = kq * rk * qs;
         }
     }
@@ -187,6 +199,8 @@ __device__ __forceinline__ void recur_tail(const RecArgs& a, const Unit& u, cons
         }
         __syncthreads();
         const float al = L.s_alpha[t], be = L.s_beta[t];
+        const size_t orow = ((static_cast<size_t>(u.b) * T + t) * a.Hv + u.h) * DV + u.j0;
+        float ov = 0.f;
         if (tid < CW) {
             const int j = tid, jg = j / 4, jc = j % 4;
             float PK = 0.f, PQ = 0.f;
@@ -198,7 +212,17 @@ __device__ __forceinline__ void recur_tail(const RecArgs& a, const Unit& u, cons
             const float p = al * PK;
             const float d = be * (L.sv[t * CW + j] - p);
             L.s_delta[j] = d;
-            a.o[((static_cast<size_t>(u.b) * T + t) * a.Hv + u.h) * DV + u.j0 + j] = __fmaf_rn(d, L.s_kq[t], al * PQ);
+            ov = __fmaf_rn(d, L.s_kq[t], al * PQ);
+            if constexpr (EPI) L.s_o[j] = ov;
+            else a.o[orow + j] = ov;
+        }
+        constexpr int OW = (CW + kWave - 1) / kWave;   // waves holding output columns
+        static_assert(OW <= 4, "s_rms holds four partial sums");
+        if constexpr (EPI) {                            // gated RMSNorm: per-wave sums of o^2
+            if (wave < OW) {
+                const float ss = wave_sum_uniform(ov * ov);
+                if (lane == 0) L.s_rms[wave] = ss;
+            }
         }
         __syncthreads();
         const float4 dl = *reinterpret_cast<const float4*>(L.s_delta + 4 * cg);
@@ -218,11 +242,20 @@ __device__ __forceinline__ void recur_tail(const RecArgs& a, const Unit& u, cons
                 *reinterpret_cast<float4*>(dst) = s[r];
             }
         }
+        // gated RMSNorm of this token's output, after the state update so that
+        // its temporaries do not overlap the update's
+        if (EPI && tid < CW) {
+            float ss = 0.f;
+#pragma unroll
+            for (int wv = 0; wv < OW; ++wv) ss += L.s_rms[wv];
+            const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / DV) + a.fu.norm_eps);
+            a.o[orow + tid] = (L.s_o[tid] * inv) * L.s_gz[t * CW + tid];
+        }
     }
 }
 
 // Any T (verify blocks, and decode at head dim 16): one unit per workgroup.
-template <typename Tin, int DK, int DV, int NT, int CW, bool NT_STORE, bool NT_LOAD>
+template <typename Tin, int DK, int DV, int NT, int CW, bool NT_STORE, bool NT_LOAD, bool PRO, bool EPI>
 __global__ __launch_bounds__(NT) void recurrent_kernel(RecArgs a) {
     using G = RecGeom<DK, DV, NT, CW>;
     extern __shared__ float lds[];
@@ -268,8 +301,18 @@ __global__ __launch_bounds__(NT) void recurrent_kernel(RecArgs a) {
             }
         }
     }
+    if constexpr (EPI) {
+        // gated RMSNorm factors of every token: norm_weight[j] * silu(z[j])
+        const Tin* z = static_cast<const Tin*>(a.fu.z);
+        const Tin* nw = static_cast<const Tin*>(a.fu.norm_w);
+        for (int i = threadIdx.x; i < T * CW; i += NT) {
+            const int t = i / CW, j = i % CW;
+            const float zv = to_f32(z[((static_cast<size_t>(u.b) * T + t) * a.Hv + u.h) * DV + u.j0 + j]);
+            L.s_gz[i] = to_f32(nw[u.j0 + j]) * (zv * sigmoid_hw(zv));
+        }
+    }
     __syncthreads();
-    recur_tail<Tin, DK, DV, NT, CW, NT_STORE>(a, u, L, T, s);
+    recur_tail<Tin, DK, DV, NT, CW, NT_STORE, PRO, EPI>(a, u, L, T, s);
 }
 
 // Commit: S_out[b,h] = S_snap[b, a_b, h]; the conv window after token a_b.
@@ -305,12 +348,27 @@ __global__ __launch_bounds__(256) void commit_kernel(CommitArgs a) {
     }
 }
 
+template <typename Tin, int DK, int DV, int NT, int CW, bool NT_STORE, bool NT_LOAD, bool PRO, bool EPI>
+hipError_t launch_rec_t(const RecArgs& a, hipStream_t stream) {
+    // the fused gated RMSNorm needs the whole dv row of a head in one workgroup
+    static_assert(CW == DV, "column slices would split the RMSNorm row");
+    const size_t lds = recurrent_lds_bytes<DK, CW, NT, EPI>(a.T);
+    void* args[] = {const_cast<RecArgs*>(&a)};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&recurrent_kernel<Tin, DK, DV, NT, CW, NT_STORE, NT_LOAD, PRO, EPI>),
+                           dim3(a.B * a.Hv * (DV / CW)), dim3(NT), args, lds, stream);
+}
+
+// The fusions are compile-time variants, so the plain kernel carries none of
+// their registers (its occupancy decides how many state bytes are in flight).
 template <typename Tin, int DK, int DV, int NT, int CW, bool NT_STORE, bool NT_LOAD>
 hipError_t launch_rec(const RecArgs& a, hipStream_t stream) {
-    const size_t lds = recurrent_lds_bytes<DK, CW, NT>(a.T);
-    void* args[] = {const_cast<RecArgs*>(&a)};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&recurrent_kernel<Tin, DK, DV, NT, CW, NT_STORE, NT_LOAD>),
-                           dim3(a.B * a.Hv * (DV / CW)), dim3(NT), args, lds, stream);
+    const bool pro = a.fu.A_log != nullptr, epi = a.fu.z != nullptr;
+    if (pro) {
+        return epi ? launch_rec_t<Tin, DK, DV, NT, CW, NT_STORE, NT_LOAD, true, true>(a, stream)
+                   : launch_rec_t<Tin, DK, DV, NT, CW, NT_STORE, NT_LOAD, true, false>(a, stream);
+    }
+    return epi ? launch_rec_t<Tin, DK, DV, NT, CW, NT_STORE, NT_LOAD, false, true>(a, stream)
+               : launch_rec_t<Tin, DK, DV, NT, CW, NT_STORE, NT_LOAD, false, false>(a, stream);
 }
 
 // d = 128: 512 threads (8 waves) hold the 128 x 128 tile as 8 float4 per thread.

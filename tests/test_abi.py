@@ -147,3 +147,39 @@ def test_prefill_validation(lib):
     need_r = lib.gdn_prefill_workspace_size(p, 1, 4096, 8, 64)
     assert need_r >= need
     assert prefill(N=0, cu=A(11)) == OK
+
+
+def F(A_log=None, dt_bias=None, z=None, w=None, eps=1e-6):
+    return ctypes.byref(gdn._CFusion(A_log, dt_bias, z, w, eps))
+
+
+def test_fusion_validation(lib):
+    p = P()
+
+    def dec(fu, B=4, o=A(8)):
+        return lib.gdn_decode_step_ex(p, fu, B, A(1), A(2), A(3), A(4), A(5), A(6), A(7), o, None)
+
+    def ver(fu, B=4, T=4):
+        return lib.gdn_verify_block_ex(p, fu, B, T, A(1), A(2), A(3), A(4), A(5), A(7), A(9),
+                                       A(8), None)
+
+    need = lib.gdn_prefill_workspace_size(p, 1, 4096, 1, 64)
+
+    def pre(fu, B=1, L=4096, N=1):
+        return lib.gdn_prefill_ex(p, fu, B, L, A(1), A(2), A(3), A(4), A(5), A(6), A(7), A(8),
+                                  None, N, 64, A(12), need, None)
+
+    for call in (dec, ver, pre):
+        assert call(F(A_log=A(13))) == NULL, call            # A_log without dt_bias
+        assert call(F(z=A(15))) == NULL, call                # z without norm_weight
+        assert call(F(z=A(15), w=A(16), eps=-1.0)) == SHAPE, call
+        assert call(F(z=A(15), w=A(16), eps=float("inf"))) == SHAPE, call
+        assert call(F(z=A(8), w=A(16))) == ALIAS, call       # z == o
+        assert call(F(A_log=A(13), dt_bias=A(8))) == ALIAS, call   # dt_bias == o
+    # an empty call is valid with any complete fusion, and NULL fusion is the plain call
+    assert dec(F(A_log=A(13), dt_bias=A(14), z=A(15), w=A(16)), B=0) == OK
+    assert ver(F(A_log=A(13), dt_bias=A(14)), B=0) == OK
+    assert pre(F(z=A(15), w=A(16)), B=0, N=0) == OK
+    assert dec(None, B=0) == OK
+    # fields of a disabled fusion are ignored (dt_bias without A_log, eps without z)
+    assert dec(F(dt_bias=A(8), eps=float("nan")), B=0) == OK
