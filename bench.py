@@ -18,7 +18,8 @@ by the roofline.
 Other workloads (--workload verify | prefill | ragged | commit) time the other
 entry points on their configurations; --workload decode_fused times the decode
 step through gdn_decode_step_ex with the gate/beta prologue and the gated
-RMSNorm epilogue. They print the same kind of JSON line.
+RMSNorm epilogue (prefill_fused and ragged_fused likewise for gdn_prefill_ex).
+They print the same kind of JSON line.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
 """
@@ -247,7 +248,7 @@ def bench_verify(args, torch, gdn, gi, commit=False):
 PREFILL_FLOP_PER_TOKEN_HEAD = 163840   # bf16-MFMA-shaped work of the chunked form, C = 64, d = 128
 
 
-def bench_prefill(args, torch, gdn, gi, ragged=False):
+def bench_prefill(args, torch, gdn, gi, ragged=False, fused=False):
     sh = gi.QWEN
     w_ = gi.WORKLOADS[3 if ragged else 2]
     seed = w_.seed
@@ -261,8 +262,14 @@ def bench_prefill(args, torch, gdn, gi, ragged=False):
     dev = lambda a: torch.from_numpy(a).cuda().to(torch.bfloat16)
     reps = 1 if ragged else 4   # 64 MiB of qkv per call: 4 replicas exceed the 256 MB cache
     xs = [dev(gi.qkv(sh, 1, L, seed + 100 * r, "bf16")) for r in range(reps)]
-    g = dev(gi.gate(sh, 1, L, seed, "bf16"))
-    b = dev(gi.beta(sh, 1, L, seed, "bf16"))
+    if fused:   # raw a/b through the prologue, gated RMSNorm epilogue with z
+        g = dev(gi.a_raw(sh, 1, L, seed, "bf16"))
+        b = dev(gi.b_raw(sh, 1, L, seed, "bf16"))
+        fus = gdn.GdnFusion(dev(gi.a_log(sh, seed, "bf16")), dev(gi.dt_bias(sh, seed, "bf16")),
+                            dev(gi.z_gate(sh, 1, L, seed, "bf16")), dev(gi.norm_weight(sh, seed, "bf16")), 1e-6)
+    else:
+        g = dev(gi.gate(sh, 1, L, seed, "bf16"))
+        b = dev(gi.beta(sh, 1, L, seed, "bf16"))
     w = dev(gi.conv_weight(sh, seed, "bf16"))
     c0 = torch.zeros((N, sh.D, sh.K - 1), device="cuda", dtype=torch.bfloat16)
     c_out = torch.empty_like(c0)
@@ -274,7 +281,10 @@ def bench_prefill(args, torch, gdn, gi, ragged=False):
     def step(i):
         # the state is carried in place, so each call continues from the last one's
         # final state: the work per call is the same whatever S holds
-        gdn.gdn_prefill(p, xs[i % reps], g, b, w, c0, c_out, S, o, ws, cu_seqlens=cu)
+        if fused:
+            gdn.gdn_prefill_ex(p, fus, xs[i % reps], g, b, w, c0, c_out, S, o, ws, cu_seqlens=cu)
+        else:
+            gdn.gdn_prefill(p, xs[i % reps], g, b, w, c0, c_out, S, o, ws, cu_seqlens=cu)
 
     wall, kms = run_timed(torch, step, args.steps, args.warmup)
     flops = PREFILL_FLOP_PER_TOKEN_HEAD * L * sh.Hv
@@ -282,7 +292,8 @@ def bench_prefill(args, torch, gdn, gi, ragged=False):
     return {
         "metric": METRIC, "value": L * args.steps / wall, "unit": "tokens/s",
         "ms_per_step": 1e3 * wall / args.steps,
-        "config": {"workload": w_.name, "L_total": L, "N": N, "Hk": sh.Hk, "Hv": sh.Hv, "dk": sh.dk,
+        "config": {"workload": w_.name + ("+gate_beta_prologue+gated_rmsnorm_epilogue" if fused else ""),
+                   "L_total": L, "N": N, "Hk": sh.Hk, "Hv": sh.Hv, "dk": sh.dk,
                    "dv": sh.dv, "chunk": 64, "cache": f"{reps} input replicas"},
         "dtype": "f32",
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -298,7 +309,8 @@ def main():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "verify", "commit", "prefill", "ragged", "decode_fused"])
+                    choices=["decode", "verify", "commit", "prefill", "ragged", "decode_fused",
+                             "prefill_fused", "ragged_fused"])
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--warm", action="store_true",
                     help="decode: also time the warm-cache rate (one state replica)")
@@ -311,7 +323,7 @@ def main():
               f"MI355X (asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
     defaults = {"decode": (256, 32), "decode_fused": (256, 32), "verify": (50, 5), "commit": (50, 5), "prefill": (20, 3),
-                "ragged": (10, 2)}[args.workload]
+                "ragged": (10, 2), "prefill_fused": (20, 3), "ragged_fused": (10, 2)}[args.workload]
     args.steps = defaults[0] if args.steps is None else args.steps
     args.warmup = defaults[1] if args.warmup is None else args.warmup
     if args.workload != "decode":
@@ -333,7 +345,9 @@ def main():
           "decode_fused": lambda a, t, g, i: bench_decode(a, t, g, i, fused=True),
           "commit": lambda a, t, g, i: bench_verify(a, t, g, i, commit=True),
           "prefill": bench_prefill,
-          "ragged": lambda a, t, g, i: bench_prefill(a, t, g, i, ragged=True)}[args.workload]
+          "ragged": lambda a, t, g, i: bench_prefill(a, t, g, i, ragged=True),
+          "prefill_fused": lambda a, t, g, i: bench_prefill(a, t, g, i, fused=True),
+          "ragged_fused": lambda a, t, g, i: bench_prefill(a, t, g, i, ragged=True, fused=True)}[args.workload]
     res = fn(args, torch, gdn, gi)
     out = {"metric": res.pop("metric"), "value": res.pop("value"), "unit": res.pop("unit"),
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,

@@ -546,43 +546,64 @@ __device__ __forceinline__ f16x8 lds_a(const _Float16* base, int row, int ks, in
 
 extern __shared__ __align__(1024) unsigned char g_stage[];   // 2 stages
 
-// Issue the wave-wide 1 KB global->LDS loads of one stage. `wave` must be
-// wave-uniform (readfirstlane'd): each load lies wholly inside one region, so
-// the region choice is a scalar branch and only the row/granule arithmetic is
-// per lane.
-template <int CPW, int NW>
+// Issue the wave-wide 1 KB global->LDS loads of the regions of one stage that
+// PARTS selects (bits: W, Q, KT, P, U, coefficients). Every region starts on a
+// 1 KB boundary; wave w issues the region's instructions w, w + NW, ... as
+// straight-line code. With NW a multiple of 4 the swizzle of a lane's granule is
+// the same in every instruction of a region, so each load is a lane base plus a
+// constant stride. `wave` must be wave-uniform (readfirstlane'd).
+constexpr int ST_W = 1, ST_Q = 2, ST_KT = 4, ST_P = 8, ST_U = 16, ST_CF = 32, ST_ALL = 63;
+template <int CPW, int NW, int PARTS>
 __device__ __forceinline__ void issue_stage(const PrefillArgs& a, const Ws& ws, int id, size_t tok0, int nt,
                                             int h, int hk, int ucol0, int buf, int wave, int lane) {
     using SG = Stage<CPW>;
+    static_assert(NW % 4 == 0 && SG::UG % NW == 0, "stage split assumes 4 or 8 waves");
+    static_assert(SG::Q % 64 == 0 && SG::KT % 64 == 0 && SG::P % 64 == 0 && SG::U % 64 == 0 && SG::CF % 64 == 0,
+                  "regions must start on instruction boundaries");
     const size_t wbase = (static_cast<size_t>(id) * a.Hv + h) * C * D;
     const size_t ktbase = (static_cast<size_t>(id) * a.Hk + hk) * D * C;
     const size_t pbase = (static_cast<size_t>(id) * a.Hv + h) * C * C;
     const size_t cfbase = (static_cast<size_t>(id) * a.Hv + h) * COEF;
     unsigned char* stage = g_stage + buf * SG::BYTES;
-    for (int q = wave; q < SG::INSTR; q += NW) {
-        const int item = 64 * q + lane;
-        const void* src;
-        if (64 * q < SG::Q) {                     // W rows, swizzled granules
-            const int r = item >> 4, j = (item & 15) ^ (r & 15);
-            src = ws.W + wbase + r * D + 8 * j;
-        } else if (64 * q < SG::KT) {             // q rows of the K head (rows past the end: a finite row)
-            const int it = item - SG::Q, r = it >> 4, j = (it & 15) ^ (r & 15);
-            const int rr = r < nt ? r : nt - 1;
-            src = ws.qh + ((tok0 + rr) * a.Hk + hk) * D + 8 * j;
-        } else if (64 * q < SG::P) {              // keys transposed
-            const int it = item - SG::KT, i = it >> 3, j = (it & 7) ^ (i & 7);
-            src = ws.KT + ktbase + i * C + 8 * j;
-        } else if (64 * q < SG::U) {              // P
-            const int it = item - SG::P, t = it >> 3, j = (it & 7) ^ (t & 7);
-            src = ws.P + pbase + t * C + 8 * j;
-        } else if (64 * q < SG::CF) {             // this workgroup's columns of U
-            const int it = item - SG::U, t = it / SG::UG, j = it % SG::UG;
-            src = ws.U + wbase + t * D + ucol0 + 8 * j;
-        } else {                                  // coefficients; lanes past the end land in padding
-            const int it = item - SG::CF;
-            src = ws.coef + cfbase + 4 * (it < COEF / 4 ? it : 0);
-        }
-        __builtin_amdgcn_global_load_lds(src, stage + q * 1024, 16, 0, 0);
+    auto ld = [&](const void* src, int q) { __builtin_amdgcn_global_load_lds(src, stage + q * 1024, 16, 0, 0); };
+    // W and Q: 16 granules per row, an instruction covers rows 4q'..4q'+3
+    const int r16l = 4 * wave + (lane >> 4);                 // row of instruction i = 0
+    const int j16 = (lane & 15) ^ (r16l & 15);               // (4 * NW * i) is a multiple of 16
+    if constexpr ((PARTS & ST_W) != 0) {
+        const _Float16* src = ws.W + wbase + r16l * D + 8 * j16;
+#pragma unroll
+        for (int i = 0; i < 16 / NW; ++i) ld(src + i * 4 * NW * D, SG::W / 64 + wave + NW * i);
+    }
+#pragma unroll
+    for (int i = 0; i < ((PARTS & ST_Q) ? 16 / NW : 0); ++i) {   // rows past the end: a finite row
+        const int r = r16l + 4 * NW * i;
+        const int rr = r < nt ? r : nt - 1;
+        ld(ws.qh + ((tok0 + rr) * a.Hk + hk) * D + 8 * j16, SG::Q / 64 + wave + NW * i);
+    }
+    // KT and P: 8 granules per row, an instruction covers rows 8q'..8q'+7
+    const int r8l = 8 * wave + (lane >> 3);
+    const int j8 = (lane & 7) ^ (lane >> 3);                  // row & 7 == lane >> 3
+    if constexpr ((PARTS & ST_KT) != 0) {
+        const _Float16* src = ws.KT + ktbase + r8l * C + 8 * j8;
+#pragma unroll
+        for (int i = 0; i < 16 / NW; ++i) ld(src + i * 8 * NW * C, SG::KT / 64 + wave + NW * i);
+    }
+    if constexpr ((PARTS & ST_P) != 0) {
+        const _Float16* src = ws.P + pbase + r8l * C + 8 * j8;
+#pragma unroll
+        for (int i = 0; i < 8 / NW; ++i) ld(src + i * 8 * NW * C, SG::P / 64 + wave + NW * i);
+    }
+    // this workgroup's columns of U: UG granules per row, 64 / UG rows per instruction
+    if constexpr ((PARTS & ST_U) != 0) {
+        constexpr int RPI = 64 / SG::UG;
+        const int t = RPI * wave + lane / SG::UG, j = lane % SG::UG;
+        const _Float16* src = ws.U + wbase + t * D + ucol0 + 8 * j;
+#pragma unroll
+        for (int i = 0; i < SG::UG / NW; ++i) ld(src + i * RPI * NW * D, SG::U / 64 + wave + NW * i);
+    }
+    // coefficients (40 granules; lanes past the end land in padding)
+    if constexpr ((PARTS & ST_CF) != 0) {
+        if (wave == NW - 1) ld(ws.coef + cfbase + 4 * (lane < COEF / 4 ? lane : 0), SG::CF / 64);
     }
 }
 
@@ -622,35 +643,22 @@ __global__ __launch_bounds__(NW * 64) void carry_kernel(PrefillArgs a, Ws ws) {
             }
 
     const size_t row_tok = static_cast<size_t>(seg.row) * a.L + seg.start;
-    // outputs of the previous chunk, stored one iteration late so that the wait
-    // for the next stage never waits on freshly issued stores
-    float opend[4][NTW][4];
-    size_t otok = 0;
-    int ont = 0;
-    issue_stage<CPW, NW>(a, ws, base, row_tok, min(C, seg.len), h, hk, ucol0, 0, wave, lane);
-    for (int c = 0; c <= nch; ++c) {
+    const size_t ts = static_cast<size_t>(a.Hv) * D;   // token stride of o
+    issue_stage<CPW, NW, ST_ALL>(a, ws, base, row_tok, min(C, seg.len), h, hk, ucol0, 0, wave, lane);
+    // The next chunk's stage is issued in three parts spread over this chunk's
+    // phases (each part before the phase that would otherwise wait on the memory
+    // pipeline), so that the vector-memory issue queue never backs up the MFMA work.
+    for (int c = 0; c < nch; ++c) {
         __builtin_amdgcn_s_waitcnt(0);   // this wave's share of the stage has landed
         __syncthreads();                 // ... and every wave's; the other stage is free
-        if (c > 0) {
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int t = 16 * mt + 4 * g + e;
-                    if (t < ont) {
-                        float* orow = a.o + ((otok + t) * a.Hv + h) * D + col0 + r16;
-#pragma unroll
-                        for (int nt = 0; nt < NTW; ++nt) orow[16 * nt] = opend[mt][nt][e];
-                    }
-                }
-        }
-        if (c == nch) break;
         const int id = base + c;
         const int ntc = min(C, seg.len - c * C);
         const size_t tok0 = row_tok + static_cast<size_t>(c) * C;
-        if (c + 1 < nch)
-            issue_stage<CPW, NW>(a, ws, id + 1, tok0 + C, min(C, seg.len - (c + 1) * C), h, hk, ucol0, (c + 1) & 1,
-                                 wave, lane);
+        const bool more = c + 1 < nch;
+        const int ntn = min(C, seg.len - (c + 1) * C);
+        if (more)
+            issue_stage<CPW, NW, ST_W | ST_U | ST_CF>(a, ws, id + 1, tok0 + C, ntn, h, hk, ucol0, (c + 1) & 1,
+                                                      wave, lane);
         const unsigned char* st = g_stage + (c & 1) * SG::BYTES;
         const _Float16* Wl = reinterpret_cast<const _Float16*>(st + SG::W * 16);
         const _Float16* Ql = reinterpret_cast<const _Float16*>(st + SG::Q * 16);
@@ -716,7 +724,12 @@ __global__ __launch_bounds__(NW * 64) void carry_kernel(PrefillArgs a, Ws ws) {
                     dp[nt][ks][e] = static_cast<_Float16>(v * cfr[t]);
                 }
 
-        // O = diag(exp(Gam)) Q S + P Delta (stored at the next iteration)
+        if (more)
+            issue_stage<CPW, NW, ST_Q | ST_P>(a, ws, id + 1, tok0 + C, ntn, h, hk, ucol0, (c + 1) & 1, wave, lane);
+
+        // O = diag(exp(Gam)) Q S + P Delta, stored as soon as a 16-token tile is done
+        float* ob = a.o + (tok0 * a.Hv + h) * D + col0 + r16 + 4 * g * ts;
+        const bool full = ntc == C;                            // uniform: every row stored
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
             f32x4v a1[NTW], a2[NTW];
@@ -737,12 +750,15 @@ __global__ __launch_bounds__(NW * 64) void carry_kernel(PrefillArgs a, Ws ws) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float eg = cf[16 * mt + 4 * g + e] * iS;
+                if (full || 16 * mt + 4 * g + e < ntc) {
+                    float* orow = ob + (16 * mt + e) * ts;
 #pragma unroll
-                for (int nt = 0; nt < NTW; ++nt) opend[mt][nt][e] = __fmaf_rn(eg, a1[nt][e], iD * a2[nt][e]);
+                    for (int nt = 0; nt < NTW; ++nt) orow[16 * nt] = __fmaf_rn(eg, a1[nt][e], iD * a2[nt][e]);
+                }
             }
         }
-        otok = tok0;
-        ont = ntc;
+        if (more)
+            issue_stage<CPW, NW, ST_KT>(a, ws, id + 1, tok0 + C, ntn, h, hk, ucol0, (c + 1) & 1, wave, lane);
 
         // S = exp(Gam_last) S + K^T diag(exp(Gam_last - Gam)) Delta; max|S| for the next chunk
         smax = 0.f;
