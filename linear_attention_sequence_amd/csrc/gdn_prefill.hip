@@ -416,49 +416,66 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, int in_dtype, hipStream
     return launch_conv_state(ca, in_dtype, stream);
 }
 
-// Gated RMSNorm of the prefill output in place (the epilogue of gdn_fusion):
-// one wave per (token, V head) row over its DV channels; tokens outside every
-// sequence are left untouched.
+// Gated RMSNorm of the prefill output in place (the epilogue of gdn_fusion).
+// One workgroup per token (all Hv rows of it; tokens outside every sequence are
+// left untouched, decided once per workgroup); a row of DV channels is reduced
+// by a group of G = min(DV, 64) lanes, and a wave's rows are loaded before any
+// is reduced so that their loads are in flight together.
 template <typename Tin, int DV>
 __global__ __launch_bounds__(256) void gated_rmsnorm_kernel(PrefillArgs a) {
+    constexpr int G = DV < kWave ? DV : kWave;          // lanes per row
+    constexpr int RPW = kWave / G;                      // rows per wave pass
+    constexpr int PER = DV / G;                         // channels per lane
+    constexpr int UNR = 4;                              // passes in flight
+    const long long tok = blockIdx.x;                   // row * L + position
+    if (a.cu != nullptr && token_owner(static_cast<int>(tok % a.L), a.L, a.N, a.cu) < 0) return;
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-    const long long row = static_cast<long long>(blockIdx.x) * 4 + wave;   // tok * Hv + h
-    if (row >= static_cast<long long>(a.B) * a.L * a.Hv) return;           // whole wave
-    const long long tok = row / a.Hv;
-    const int p = static_cast<int>(tok % a.L);
-    if (a.cu != nullptr && token_owner(p, a.L, a.N, a.cu) < 0) return;     // whole wave
-    float* o = a.o + row * DV;
-    const Tin* z = static_cast<const Tin*>(a.fu.z) + row * DV;
+    const int sub = lane / G, gl = lane % G;
+    float* o = a.o + tok * a.Hv * DV;
+    const Tin* z = static_cast<const Tin*>(a.fu.z) + tok * a.Hv * DV;
     const Tin* w = static_cast<const Tin*>(a.fu.norm_w);
-    constexpr int PER = (DV + kWave - 1) / kWave;
-    float v[PER];
-    float ss = 0.f;
+    float wn[PER];
 #pragma unroll
-    for (int q = 0; q < PER; ++q) {
-        const int j = lane + q * kWave;
-        v[q] = j < DV ? o[j] : 0.f;
-        ss = __fmaf_rn(v[q], v[q], ss);
-    }
-    ss = wave_sum(ss);
-    const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / DV) + a.fu.norm_eps);
+    for (int q = 0; q < PER; ++q) wn[q] = to_f32(w[gl + q * G]);
+    // pass k of this wave covers heads (k * 4 + wave) * RPW + sub
+    for (int k0 = 0; (k0 * 4 + wave) * RPW < a.Hv; k0 += UNR) {
+        float v[UNR][PER], zv[UNR][PER];
 #pragma unroll
-    for (int q = 0; q < PER; ++q) {
-        const int j = lane + q * kWave;
-        if (j < DV) {
-            const float zv = to_f32(z[j]);
-            o[j] = to_f32(w[j]) * (v[q] * inv) * (zv * sigmoid_hw(zv));
+        for (int u = 0; u < UNR; ++u) {
+            const int h = ((k0 + u) * 4 + wave) * RPW + sub;
+            const int hc = h < a.Hv ? h : a.Hv - 1;     // clamped: loads stay unconditional
+#pragma unroll
+            for (int q = 0; q < PER; ++q) {
+                v[u][q] = o[static_cast<size_t>(hc) * DV + gl + q * G];
+                zv[u][q] = to_f32(z[static_cast<size_t>(hc) * DV + gl + q * G]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+            const int h = ((k0 + u) * 4 + wave) * RPW + sub;
+            float ss = 0.f;
+#pragma unroll
+            for (int q = 0; q < PER; ++q) ss = __fmaf_rn(v[u][q], v[u][q], ss);
+#pragma unroll
+            for (int m = G / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, kWave);
+            const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / DV) + a.fu.norm_eps);
+            if (h < a.Hv) {
+#pragma unroll
+                for (int q = 0; q < PER; ++q)
+                    o[static_cast<size_t>(h) * DV + gl + q * G] = wn[q] * (v[u][q] * inv) * (zv[u][q] * sigmoid_hw(zv[u][q]));
+            }
         }
     }
 }
 
 template <typename Tin, int DV>
 static hipError_t launch_epi_t(const PrefillArgs& a, hipStream_t stream) {
-    const long long rows = static_cast<long long>(a.B) * a.L * a.Hv;
-    if (rows == 0) return hipSuccess;
-    if ((rows + 3) / 4 > 0x7fffffffLL) return hipErrorInvalidValue;
+    const long long toks = static_cast<long long>(a.B) * a.L;
+    if (toks == 0) return hipSuccess;
+    if (toks > 0x7fffffffLL) return hipErrorInvalidValue;
     void* args[] = {const_cast<PrefillArgs*>(&a)};
     return hipLaunchKernel(reinterpret_cast<const void*>(&gated_rmsnorm_kernel<Tin, DV>),
-                           dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), args, 0, stream);
+                           dim3(static_cast<unsigned>(toks)), dim3(256), args, 0, stream);
 }
 
 hipError_t launch_prefill_epilogue(const PrefillArgs& a, int in_dtype, int d, hipStream_t stream) {
