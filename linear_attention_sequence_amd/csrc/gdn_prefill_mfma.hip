@@ -40,8 +40,8 @@ namespace pf2 {
 
 constexpr int C = 64;      // chunk length
 constexpr int D = 128;     // head dim (dk == dv)
-constexpr int TT = 64;     // front-end tile (tokens)
-constexpr int RAW = TT + 5;  // raw tile row stride (floats): 67 used, odd-ish stride against bank conflicts
+constexpr int TT = 32;     // front-end tile (tokens): 19 KB of LDS, eight workgroups per CU
+constexpr int RAW = TT + 5;  // raw tile row stride (floats): TT + 3 used, odd stride against bank conflicts
 // per (chunk, V head) coefficients: [0, C) exp(Gam_t); [C, 2C) exp(Gam_last - Gam_t);
 // 2C: exp(Gam_last); 2C + 1: 2^uexp, the scale of the stored U; padded to 40 granules
 constexpr int COEF = 160;
@@ -128,8 +128,9 @@ __device__ __forceinline__ float fast_silu(float x) {
 // ---- steps 1-4 ------------------------------------------------------------------
 template <typename Tin>
 __global__ __launch_bounds__(256) void front_kernel(PrefillArgs a, Ws ws) {
-    __shared__ float buf[D * RAW];           // raw[c][m] (window of 67 tokens), then ys[t][c] (stride 129)
+    __shared__ float buf[D * RAW];           // raw[c][m] (window of TT + 3 tokens), then ys[t][c] (stride 129)
     __shared__ int s_n[TT], s_start[TT];
+    static_assert(TT * (D + 1) <= D * RAW, "the transposed outputs reuse the raw tile");
     const int units = 2 * a.Hk + a.Hv;
     const int tiles = (a.L + TT - 1) / TT;
     long long blk = blockIdx.x;
@@ -141,37 +142,74 @@ __global__ __launch_bounds__(256) void front_kernel(PrefillArgs a, Ws ws) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const Tin* x = static_cast<const Tin*>(a.qkv) + (static_cast<size_t>(row) * a.D + ch0) * a.L;
 
+    // a wave loads TT consecutive tokens of 64 / TT channels per instruction
+    // (coalesced); the 3 tokens before the tile (3 x 128 values) come from two
+    // loads per thread. Every load is unconditional, from a clamped position, and
+    // masked afterwards, so that all of them are in flight at once (a load under a
+    // branch is waited for inside the branch).
+    constexpr int CPI = kWave / TT;                  // channels per load instruction
+    constexpr int ROWS = D / 4 / CPI;                // instructions per wave
+    const int lt = lane % TT, lc = lane / TT;
+    float v[ROWS], hv[2];
+    {
+        const int p = p0 + lt;
+        const bool pv = p < a.L;
+        const int pc = pv ? p : a.L - 1;
+#pragma unroll
+        for (int i = 0; i < ROWS; ++i) {
+            const float lv = to_f32(x[static_cast<size_t>((wave * ROWS + i) * CPI + lc) * a.L + pc]);
+            v[i] = pv ? lv : 0.f;
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int item = tid + 256 * k;                 // < 3 * D for k == 0 and tid < 128 when k == 1
+            const int hc = item < 3 * D ? item / 3 : 0, hj = item % 3;
+            const int ph = p0 - 3 + hj;                     // < L since p0 < L
+            const float lh = to_f32(x[static_cast<size_t>(hc) * a.L + (ph >= 0 ? ph : 0)]);
+            hv[k] = ph >= 0 ? lh : 0.f;
+        }
+    }
+    // sequence of every token of the tile; with cu_seqlens the (clamped) table is
+    // searched in LDS when it fits in the tile buffer, which is free until the
+    // loads above are written into it
+    const bool cu_lds = a.cu != nullptr && a.N + 1 <= D * RAW;
+    if (cu_lds) {
+        int* scu = reinterpret_cast<int*>(buf);
+        for (int i = tid; i <= a.N; i += 256) {
+            const int v0 = a.cu[i];
+            scu[i] = v0 < 0 ? 0 : (v0 > a.L ? a.L : v0);
+        }
+        __syncthreads();
+    }
     if (tid < TT) {
         const int p = p0 + tid;
         int start = 0, n = -1;
-        if (p < a.L) n = owner_of(p, row, a, &start);
+        if (p < a.L) {
+            if (cu_lds) {
+                const int* scu = reinterpret_cast<const int*>(buf);
+                int lo = 0, hi = a.N - 1;
+                while (lo <= hi) {                          // last n whose start is <= p
+                    const int mid = (lo + hi) >> 1;
+                    if (scu[mid] <= p) { n = mid; lo = mid + 1; } else { hi = mid - 1; }
+                }
+                if (n >= 0) {
+                    start = scu[n];
+                    if (p >= scu[n + 1]) n = -1;            // past the end (or an empty pair)
+                }
+            } else {
+                n = owner_of(p, row, a, &start);
+            }
+        }
         s_n[tid] = n;
         s_start[tid] = start;
     }
-    // a wave loads 64 consecutive tokens of one channel per instruction (coalesced);
-    // all of a wave's rows are issued before the first one is used
-    {
-        constexpr int ROWS = D / 4;
-        // unconditional loads from clamped positions, masked afterwards, so that
-        // every row is in flight at once (a load under a branch is waited for
-        // inside the branch)
-        float v[ROWS], hv[ROWS];
-        const int p = p0 + lane, ph = p0 - 3 + lane;
-        const bool pv = p < a.L, hvld = lane < 3 && ph >= 0 && ph < a.L;
-        const int pc = pv ? p : a.L - 1, phc = hvld ? ph : pc;
+    if (cu_lds) __syncthreads();                            // the table is read before buf is reused
 #pragma unroll
-        for (int i = 0; i < ROWS; ++i) {
-            const Tin* xc = x + static_cast<size_t>(wave * ROWS + i) * a.L;
-            const float lv = to_f32(xc[pc]), lh = to_f32(xc[phc]);
-            v[i] = pv ? lv : 0.f;
-            hv[i] = hvld ? lh : 0.f;
-        }
+    for (int i = 0; i < ROWS; ++i) buf[((wave * ROWS + i) * CPI + lc) * RAW + 3 + lt] = v[i];
 #pragma unroll
-        for (int i = 0; i < ROWS; ++i) {
-            const int c = wave * ROWS + i;
-            buf[c * RAW + 3 + lane] = v[i];
-            if (lane < 3) buf[c * RAW + lane] = hv[i];
-        }
+    for (int k = 0; k < 2; ++k) {
+        const int item = tid + 256 * k;
+        if (item < 3 * D) buf[(item / 3) * RAW + item % 3] = hv[k];
     }
     __syncthreads();
     const int c = tid & (D - 1), th = tid >> 7;   // channel, token half
@@ -223,16 +261,17 @@ __global__ __launch_bounds__(256) void front_kernel(PrefillArgs a, Ws ws) {
     for (int j = 0; j < TT / 2; ++j) buf[(th * (TT / 2) + j) * (D + 1) + c] = y[j];
     __syncthreads();
     const bool is_q = u < a.Hk, is_k = !is_q && u < 2 * a.Hk;
-    // per-token sum of squares: thread (token tid % 64, channel quarter tid / 64)
-    // reads its quarter column-wise (lanes run along tokens: conflict-free)
-    __shared__ float s_part[4][TT];
+    // per-token sum of squares: thread (token tid % TT, channel part tid / TT)
+    // reads its part column-wise (lanes run along tokens: conflict-free)
+    constexpr int NPART = 256 / TT, PW = D / NPART;
+    __shared__ float s_part[NPART][TT];
     __shared__ float s_scale[TT];
     if (is_q || is_k) {
-        const int t = tid & (TT - 1), qq = tid >> 6;
+        const int t = tid % TT, qq = tid / TT;
         float ss = 0.f;
 #pragma unroll 8
-        for (int cc = 0; cc < D / 4; ++cc) {
-            const float v = buf[t * (D + 1) + qq * (D / 4) + cc];
+        for (int cc = 0; cc < PW; ++cc) {
+            const float v = buf[t * (D + 1) + qq * PW + cc];
             ss = __fmaf_rn(v, v, ss);
         }
         s_part[qq][t] = ss;
@@ -241,26 +280,31 @@ __global__ __launch_bounds__(256) void front_kernel(PrefillArgs a, Ws ws) {
     if (tid < TT) {
         float r = 1.f;
         if (is_q || is_k) {
-            const float ss = (s_part[0][tid] + s_part[1][tid]) + (s_part[2][tid] + s_part[3][tid]);
+            float ss = 0.f;
+#pragma unroll
+            for (int q = 0; q < NPART; ++q) ss += s_part[q][tid];
             if (a.use_l2) r = 1.0f / sqrtf(ss + a.eps);
             if (is_q) r *= 1.0f / sqrtf(static_cast<float>(D));
         }
         s_scale[tid] = r;
     }
     __syncthreads();
-    // one wave per token: lane writes channels 2*lane, 2*lane+1 (256 contiguous bytes)
-    for (int i = 0; i < TT / 4; ++i) {
-        const int t = wave * (TT / 4) + i;
-        if (s_n[t] < 0) continue;            // uniform across the wave
-        const float r = s_scale[t];
-        const size_t tok = static_cast<size_t>(row) * a.L + p0 + t;
-        _Float16* dst = is_q ? ws.qh + (tok * a.Hk + u) * D
-                      : is_k ? ws.kh + (tok * a.Hk + (u - a.Hk)) * D
-                             : ws.vh + (tok * a.Hv + (u - 2 * a.Hk)) * D;
-        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-        const h2 v = {static_cast<_Float16>(buf[t * (D + 1) + 2 * lane] * r),
-                      static_cast<_Float16>(buf[t * (D + 1) + 2 * lane + 1] * r)};
-        *reinterpret_cast<h2*>(dst + 2 * lane) = v;
+    // 16 lanes per token, 8 channels (16 bytes) per lane: a wave stores 4 tokens
+    // per instruction, 16 tokens in all
+    {
+        const int tq = lane >> 4, j = lane & 15;
+        _Float16* base = is_q ? ws.qh + u * D : is_k ? ws.kh + (u - a.Hk) * D : ws.vh + (u - 2 * a.Hk) * D;
+        const int hs = is_q || is_k ? a.Hk : a.Hv;   // heads per token in the destination
+#pragma unroll
+        for (int i = 0; i < TT / 16; ++i) {
+            const int t = wave * (TT / 4) + 4 * i + tq;
+            const float r = s_scale[t];
+            f16x8 v;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = static_cast<_Float16>(buf[t * (D + 1) + 8 * j + e] * r);
+            const size_t tok = static_cast<size_t>(row) * a.L + p0 + t;
+            if (s_n[t] >= 0) *reinterpret_cast<f16x8*>(base + tok * hs * D + 8 * j) = v;
+        }
     }
 }
 
