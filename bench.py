@@ -18,8 +18,10 @@ by the roofline.
 Other workloads (--workload verify | prefill | ragged | commit) time the other
 entry points on their configurations; --workload decode_fused times the decode
 step through gdn_decode_step_ex with the gate/beta prologue and the gated
-RMSNorm epilogue (prefill_fused and ragged_fused likewise for gdn_prefill_ex).
-They print the same kind of JSON line.
+RMSNorm epilogue (prefill_fused and ragged_fused likewise for gdn_prefill_ex);
+spec_round_copy and spec_round_slots time one speculative round (verify plus
+commit) with the accepted state copied, or read in place from the snapshot
+slots; --verify-t sets the block width. They print the same kind of JSON line.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
 """
@@ -196,9 +198,13 @@ def cpu_baseline_decode(gi, sh, seed, B, budget_s=12.0):
 # ---------------------------------------------------------------------------
 # verify (B = 128, T = 4) and commit
 # ---------------------------------------------------------------------------
-def bench_verify(args, torch, gdn, gi, commit=False):
+def bench_verify(args, torch, gdn, gi, commit=False, rnd=None):
+    """verify (one gdn_verify_block), commit (one gdn_verify_commit), or a whole
+    speculative round: rnd == "copy" is verify + commit of the accepted state,
+    rnd == "slots" is gdn_verify_block_slots from the previous block's snapshots
+    (updated in place) + a window-only commit."""
     sh, w_ = gi.QWEN, gi.WORKLOADS[4]
-    seed, B, T = w_.seed, gi.VERIFY_B, gi.VERIFY_T
+    seed, B, T = w_.seed, gi.VERIFY_B, args.verify_t
     p = gdn.GdnParams(sh.Hk, sh.Hv, sh.dk, sh.dv, sh.K, True, 1e-6, gdn.GDN_BF16)
     dev = lambda a, bf=True: (torch.from_numpy(a).cuda().to(torch.bfloat16) if bf else torch.from_numpy(a).cuda())
     x = dev(gi.qkv(sh, B, T, seed, "bf16"))
@@ -215,20 +221,33 @@ def bench_verify(args, torch, gdn, gi, commit=False):
     gdn.gdn_verify_block(p, x, g, b, w, c0, S_in, snap, o)
 
     def step(i):
-        if commit:
+        if rnd == "copy":       # the committed state ping-pongs between S_in and S_out
+            src, dst = (S_in, S_out) if i % 2 == 0 else (S_out, S_in)
+            gdn.gdn_verify_block(p, x, g, b, w, c0, src, snap, o)
+            gdn.gdn_verify_commit(p, acc, x, c0, snap, c_out, dst)
+        elif rnd == "slots":
+            gdn.gdn_verify_block_slots(p, None, x, g, b, w, c0, snap, acc, snap, o)
+            gdn.gdn_verify_commit(p, acc, x, c0, None, c_out, None)
+        elif commit:
             gdn.gdn_verify_commit(p, acc, x, c0, snap, c_out, S_out)
         else:
             gdn.gdn_verify_block(p, x, g, b, w, c0, S_in, snap, o)
 
     wall, kms = run_timed(torch, step, args.steps, args.warmup)
     tile = sh.dk * sh.dv * 4
-    if commit:
-        nbytes = B * sh.Hv * tile * 2 + B * 4 + B * sh.D * (sh.K - 1) * 2 * 2 + B * sh.D * T * 2
-        name, kern = "verify_commit_B128_T4_d128", "commit_kernel"
+    conv_b = B * sh.D * (sh.K - 1) * 2 * 2 + B * sh.D * T * 2 + B * 4   # window roll of a commit
+    vbytes = (B * sh.Hv * tile * (1 + T) + B * sh.D * T * 2 + B * sh.D * (sh.K - 1) * 2
+              + sh.D * sh.K * 2 + B * T * sh.Hv * 2 * 2 + B * T * sh.Hv * sh.dv * 4)
+    if rnd is not None:
+        nbytes = vbytes + conv_b + (B * sh.Hv * tile * 2 if rnd == "copy" else B * 4)
+        name = f"spec_round_{rnd}_B{B}_T{T}_Hk16_Hv32_d128"
+        kern = "speculative round: verify + commit (two launches, timed together)"
+    elif commit:
+        nbytes = B * sh.Hv * tile * 2 + conv_b
+        name, kern = f"verify_commit_B{B}_T{T}_d128", "commit_kernel"
     else:
-        nbytes = (B * sh.Hv * tile * (1 + T) + B * sh.D * T * 2 + B * sh.D * (sh.K - 1) * 2
-                  + sh.D * sh.K * 2 + B * T * sh.Hv * 2 * 2 + B * T * sh.Hv * sh.dv * 4)
-        name, kern = w_.name, "recurrent_kernel (verify, T=4)"
+        nbytes = vbytes
+        name, kern = (w_.name if T == gi.VERIFY_T else f"verify_B{B}_T{T}_Hk16_Hv32_d128"), f"recurrent_kernel (verify, T={T})"
     achieved = nbytes / (kms * 1e-3) / 1e9
     return {
         "metric": METRIC, "value": (B if commit else B * T) * args.steps / wall, "unit": "tokens/s",
@@ -310,7 +329,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "verify", "commit", "prefill", "ragged", "decode_fused",
-                             "prefill_fused", "ragged_fused"])
+                             "prefill_fused", "ragged_fused", "spec_round_copy", "spec_round_slots"])
+    ap.add_argument("--verify-t", type=int, default=4,
+                    help="verify/commit/spec_round_*: block width T (tokens per sequence per block)")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--warm", action="store_true",
                     help="decode: also time the warm-cache rate (one state replica)")
@@ -323,7 +344,8 @@ def main():
               f"MI355X (asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
     defaults = {"decode": (256, 32), "decode_fused": (256, 32), "verify": (50, 5), "commit": (50, 5), "prefill": (20, 3),
-                "ragged": (10, 2), "prefill_fused": (20, 3), "ragged_fused": (10, 2)}[args.workload]
+                "ragged": (10, 2), "prefill_fused": (20, 3), "ragged_fused": (10, 2),
+                "spec_round_copy": (50, 5), "spec_round_slots": (50, 5)}[args.workload]
     args.steps = defaults[0] if args.steps is None else args.steps
     args.warmup = defaults[1] if args.warmup is None else args.warmup
     if args.workload != "decode":
@@ -347,6 +369,8 @@ def main():
           "prefill": bench_prefill,
           "ragged": lambda a, t, g, i: bench_prefill(a, t, g, i, ragged=True),
           "prefill_fused": lambda a, t, g, i: bench_prefill(a, t, g, i, fused=True),
+          "spec_round_copy": lambda a, t, g, i: bench_verify(a, t, g, i, rnd="copy"),
+          "spec_round_slots": lambda a, t, g, i: bench_verify(a, t, g, i, rnd="slots"),
           "ragged_fused": lambda a, t, g, i: bench_prefill(a, t, g, i, ragged=True, fused=True)}[args.workload]
     res = fn(args, torch, gdn, gi)
     out = {"metric": res.pop("metric"), "value": res.pop("value"), "unit": res.pop("unit"),

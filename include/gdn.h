@@ -181,11 +181,38 @@ gdn_status gdn_verify_block(const gdn_params* p, int32_t B, int32_t T, const voi
  *   S_snap         [B, T, Hv, dk, dv] fp32
  *   conv_state_out [B, D, K-1] in_dtype (must not overlap conv_state_in)
  *   S_out          [B, Hv, dk, dv] fp32 (must not overlap S_snap)
+ * S_snap and S_out may both be NULL: then only the conv window is rolled (the
+ * state stays in the snapshots, for gdn_verify_block_slots).
  */
 gdn_status gdn_verify_commit(const gdn_params* p, int32_t B, int32_t T,
                              const int32_t* accept_len, const void* qkv,
                              const void* conv_state_in, const float* S_snap,
                              void* conv_state_out, float* S_out, void* stream);
+
+/*
+ * gdn_verify_block_slots — the next verify block started straight from the
+ * snapshots of the previous one, so that accepting a prefix copies no state
+ * ("mlxcel benchmarks" page, lablup/mlxcel docs/benchmarks.md, the MTP
+ * speculative-decoding section: a drafted block is verified in one forward
+ * pass and its block width is swept from 2 to 8). Identical to
+ * gdn_verify_block_ex, bit for bit, with S_in[b] = S_prev[b, slot[b]].
+ *   S_prev         [B, T_prev, Hv, dk, dv] fp32  snapshots of the previous block
+ *   T_prev         1..16
+ *   slot           [B] int32 (device), clamped into [0, T_prev-1]; for the
+ *                  speculative loop it is the accept_len of the previous block
+ *   S_snap         [B, T, Hv, dk, dv] fp32; may be S_prev itself when
+ *                  T == T_prev (every (sequence, head) tile is read whole by one
+ *                  workgroup before that workgroup writes it); any other overlap
+ *                  with S_prev is GDN_ERR_ALIAS
+ *   conv_state_in  the window after the accepted prefix, e.g. from
+ *                  gdn_verify_commit with S_snap = S_out = NULL
+ * Other arguments as for gdn_verify_block_ex. slot NULL: GDN_ERR_NULL.
+ */
+gdn_status gdn_verify_block_slots(const gdn_params* p, const gdn_fusion* fusion, int32_t B,
+                                  int32_t T, const void* qkv, const void* gate, const void* beta,
+                                  const void* conv_weight, const void* conv_state_in,
+                                  const float* S_prev, int32_t T_prev, const int32_t* slot,
+                                  float* S_snap, float* o, void* stream);
 
 /*
  * gdn_prefill_workspace_size — bytes of device workspace gdn_prefill needs for

@@ -26,7 +26,7 @@ STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_DTYPE"
 # every symbol include/gdn.h declares
 EXPORTS = ("gdn_status_string", "gdn_version", "gdn_conv1d_silu", "gdn_decode_step",
            "gdn_verify_block", "gdn_verify_commit", "gdn_prefill_workspace_size", "gdn_prefill",
-           "gdn_decode_step_ex", "gdn_verify_block_ex", "gdn_prefill_ex")
+           "gdn_decode_step_ex", "gdn_verify_block_ex", "gdn_prefill_ex", "gdn_verify_block_slots")
 
 
 class GdnError(RuntimeError):
@@ -123,8 +123,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.gdn_decode_step_ex.argtypes = [PP, PF, I32, V, V, V, V, V, V, V, V, V]
     lib.gdn_verify_block_ex.argtypes = [PP, PF, I32, I32, V, V, V, V, V, V, V, V, V]
     lib.gdn_prefill_ex.argtypes = [PP, PF, I32, I32, V, V, V, V, V, V, V, V, V, I32, I32, V, SZ, V]
+    lib.gdn_verify_block_slots.argtypes = [PP, PF, I32, I32, V, V, V, V, V, V, I32, V, V, V, V]
     for fn in ("gdn_conv1d_silu", "gdn_decode_step", "gdn_verify_block", "gdn_verify_commit",
-               "gdn_prefill", "gdn_decode_step_ex", "gdn_verify_block_ex", "gdn_prefill_ex"):
+               "gdn_prefill", "gdn_decode_step_ex", "gdn_verify_block_ex", "gdn_prefill_ex",
+               "gdn_verify_block_slots"):
         getattr(lib, fn).restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -232,9 +234,25 @@ def gdn_verify_block_ex(p: GdnParams, fusion: GdnFusion | None, qkv, gate, beta,
           _ptr(S_snap), _ptr(o), _stream(stream))
 
 
+def gdn_verify_block_slots(p: GdnParams, fusion: GdnFusion | None, qkv, gate, beta, conv_weight,
+                           conv_state_in, S_prev, slot, S_snap, o, stream=None):
+    """Verify block starting from snapshot slot[b] of S_prev [B,T_prev,Hv,dk,dv] (may be S_snap)."""
+    for t, n in ((qkv, "qkv"), (gate, "gate"), (beta, "beta"), (conv_weight, "conv_weight"),
+                 (conv_state_in, "conv_state_in")):
+        _expect(t, p.torch_dtype, n)
+    for t, n in ((S_prev, "S_prev"), (S_snap, "S_snap"), (o, "o")):
+        _expect(t, torch.float32, n)
+    _expect(slot, torch.int32, "slot")
+    B, _, T = qkv.shape
+    _call("gdn_verify_block_slots", ctypes.byref(p.c()), _fusion_ref(p, fusion), B, T, _ptr(qkv),
+          _ptr(gate), _ptr(beta), _ptr(conv_weight), _ptr(conv_state_in), _ptr(S_prev),
+          S_prev.shape[1], _ptr(slot), _ptr(S_snap), _ptr(o), _stream(stream))
+
+
 def gdn_verify_commit(p: GdnParams, accept_len, qkv, conv_state_in, S_snap, conv_state_out, S_out,
                       stream=None):
-    """Keep snapshot accept_len[b] per row and roll the conv window to match."""
+    """Keep snapshot accept_len[b] per row and roll the conv window to match
+    (S_snap and S_out both None: the conv window only)."""
     _expect(accept_len, torch.int32, "accept_len")
     for t, n in ((qkv, "qkv"), (conv_state_in, "conv_state_in"), (conv_state_out, "conv_state_out")):
         _expect(t, p.torch_dtype, n)

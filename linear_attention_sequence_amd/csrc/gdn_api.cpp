@@ -139,13 +139,20 @@ gdn_status gdn_conv1d_silu(const gdn_params* p, int32_t B, int32_t L, const void
     return GDN_OK;
 }
 
+// decode (in_place: S_out == S_in), verify (S_out = snapshots) and verify from
+// the snapshots of a previous block (slot != NULL: S_in is [B, slot_T, Hv, dk, dv]
+// and sequence b starts from its snapshot slot[b]; S_in == S_out is allowed when
+// slot_T == T, since every (sequence, head) tile is read whole before it is written)
 static gdn_status recurrent_common(const gdn_params* p, const gdn_fusion* fusion, int32_t B,
                                    int32_t T, const void* qkv, const void* gate, const void* beta,
                                    const void* conv_weight, const void* conv_state_in,
                                    void* conv_state_out, const float* S_in, float* S_out, float* o,
-                                   void* stream, bool in_place) {
+                                   void* stream, bool in_place, bool slots = false,
+                                   const int32_t* slot = nullptr, int32_t slot_T = 0) {
     gdn_status st = check_params(p);
     if (st != GDN_OK) return st;
+    if (slots && slot_T < 1) return GDN_ERR_SHAPE;
+    if (slots && slot_T > kMaxT) return GDN_ERR_UNSUPPORTED;
     gdn::Fusion fu;
     if ((st = fusion_of(fusion, &fu)) != GDN_OK) return st;
     if (B < 0) return GDN_ERR_SHAPE;
@@ -155,20 +162,24 @@ static gdn_status recurrent_common(const gdn_params* p, const gdn_fusion* fusion
     if (B == 0) return GDN_OK;
     if (!qkv || !gate || !beta || !conv_weight || !conv_state_in || !S_in || !S_out || !o)
         return GDN_ERR_NULL;
+    if (slots && slot == nullptr) return GDN_ERR_NULL;
     if (in_place && !conv_state_out) return GDN_ERR_NULL;
     if (!aligned(S_in, 16) || !aligned(S_out, 16) || !aligned(o, 16)) return GDN_ERR_ALIGN;
     const long long D = dimD(p);
     const size_t es = esize(p);
     const size_t Hv = static_cast<size_t>(p->num_v_heads);
     const size_t state = static_cast<size_t>(B) * Hv * tile_bytes(p);
+    const bool same = slot != nullptr && S_in == S_out && slot_T == T;   // snapshots updated in place
+    const size_t in_bytes = (in_place || same) ? 0 : state * (slot != nullptr ? slot_T : 1);
     const Buf bufs[] = {
         {qkv, static_cast<size_t>(B) * D * T * es, false},
         {gate, static_cast<size_t>(B) * T * Hv * es, false},
         {beta, static_cast<size_t>(B) * T * Hv * es, false},
         {conv_weight, static_cast<size_t>(D) * kK * es, false},
         {conv_state_in, static_cast<size_t>(B) * D * (kK - 1) * es, false},
-        // decode updates S in place: it is listed once, as an output
-        {S_in, in_place ? 0 : state, false},
+        {slot, slot != nullptr ? static_cast<size_t>(B) * 4 : 0, false},
+        // an input updated in place is listed once, as an output
+        {S_in, in_bytes, false},
         {conv_state_out, conv_state_out ? static_cast<size_t>(B) * D * (kK - 1) * es : 0, true},
         {S_out, state * T, true},
         {o, static_cast<size_t>(B) * T * Hv * p->head_v_dim * sizeof(float), true},
@@ -180,7 +191,7 @@ static gdn_status recurrent_common(const gdn_params* p, const gdn_fusion* fusion
     if ((st = check_alias(bufs)) != GDN_OK) return st;
     const gdn::RecArgs a{B, T, p->num_k_heads, p->num_v_heads, static_cast<int>(D),
                          p->use_qk_l2norm, p->l2norm_eps, qkv, gate, beta, conv_weight,
-                         conv_state_in, conv_state_out, S_in, S_out, o, fu};
+                         conv_state_in, conv_state_out, S_in, S_out, o, fu, slot, slot_T};
     return launched(gdn::launch_recurrent(a, p->in_dtype, p->head_k_dim, static_cast<hipStream_t>(stream)));
 }
 
@@ -215,6 +226,15 @@ gdn_status gdn_verify_block_ex(const gdn_params* p, const gdn_fusion* fusion, in
                             S_in, S_snap, o, stream, false);
 }
 
+gdn_status gdn_verify_block_slots(const gdn_params* p, const gdn_fusion* fusion, int32_t B,
+                                  int32_t T, const void* qkv, const void* gate, const void* beta,
+                                  const void* conv_weight, const void* conv_state_in,
+                                  const float* S_prev, int32_t T_prev, const int32_t* slot,
+                                  float* S_snap, float* o, void* stream) {
+    return recurrent_common(p, fusion, B, T, qkv, gate, beta, conv_weight, conv_state_in, nullptr,
+                            S_prev, S_snap, o, stream, false, true, slot, T_prev);
+}
+
 gdn_status gdn_verify_commit(const gdn_params* p, int32_t B, int32_t T,
                              const int32_t* accept_len, const void* qkv,
                              const void* conv_state_in, const float* S_snap,
@@ -225,8 +245,8 @@ gdn_status gdn_verify_commit(const gdn_params* p, int32_t B, int32_t T,
     if (T > kMaxT) return GDN_ERR_UNSUPPORTED;
     if (static_cast<long long>(B) * p->num_v_heads > kMaxGrid) return GDN_ERR_SHAPE;
     if (B == 0) return GDN_OK;
-    if (!accept_len || !qkv || !conv_state_in || !S_snap || !conv_state_out || !S_out)
-        return GDN_ERR_NULL;
+    if (!accept_len || !qkv || !conv_state_in || !conv_state_out) return GDN_ERR_NULL;
+    if ((S_snap == nullptr) != (S_out == nullptr)) return GDN_ERR_NULL;   // both NULL: window only
     if (!aligned(S_snap, 16) || !aligned(S_out, 16)) return GDN_ERR_ALIGN;
     const long long D = dimD(p);
     const size_t es = esize(p);
@@ -235,9 +255,9 @@ gdn_status gdn_verify_commit(const gdn_params* p, int32_t B, int32_t T,
         {accept_len, static_cast<size_t>(B) * 4, false},
         {qkv, static_cast<size_t>(B) * D * T * es, false},
         {conv_state_in, static_cast<size_t>(B) * D * (kK - 1) * es, false},
-        {S_snap, state * T, false},
+        {S_snap, S_snap ? state * T : 0, false},
         {conv_state_out, static_cast<size_t>(B) * D * (kK - 1) * es, true},
-        {S_out, state, true},
+        {S_out, S_out ? state : 0, true},
     };
     if ((st = check_alias(bufs)) != GDN_OK) return st;
     const gdn::CommitArgs a{B, T, p->num_v_heads, static_cast<int>(D), accept_len, qkv,

@@ -29,10 +29,12 @@ struct RecArgs {
     const void* w;        // [D, 1, K]
     const void* conv_in;  // [B, D, K-1]
     void* conv_out;       // [B, D, K-1] or nullptr
-    const float* S_in;    // [B, Hv, dk, dv]
+    const float* S_in;    // [B, Hv, dk, dv], or [B, slot_T, Hv, dk, dv] with slot
     float* S_out;         // [B, T, Hv, dk, dv]
     float* o;             // [B, T, Hv, dv]
     Fusion fu;
+    const int32_t* slot;  // [B] snapshot index per sequence (clamped to [0, slot_T)), or nullptr
+    int slot_T;           // snapshots per sequence in S_in when slot is set
 };
 
 struct CommitArgs {
@@ -42,7 +44,7 @@ struct CommitArgs {
     const void* conv_in;    // [B, D, K-1]
     const float* S_snap;    // [B, T, Hv, dk, dv]
     void* conv_out;         // [B, D, K-1]
-    float* S_out;           // [B, Hv, dk, dv]
+    float* S_out;           // [B, Hv, dk, dv], or nullptr (then S_snap is unused: conv window only)
 };
 
 struct ConvArgs {

@@ -110,7 +110,13 @@ template <int DK, int DV, int NT, int CW, bool NT_LOAD>
 __device__ __forceinline__ void load_tile(const RecArgs& a, const Unit& u, float4 (&s)[RecGeom<DK, DV, NT, CW>::RPT]) {
     using G = RecGeom<DK, DV, NT, CW>;
     const int cg = threadIdx.x % G::CG, rg = threadIdx.x / G::CG;
-    const float* Sin = a.S_in + static_cast<size_t>(u.bh) * DK * DV + u.j0;
+    size_t src = u.bh;                   // (sequence, head) tile of S_in
+    if (a.slot != nullptr) {             // snapshot slot[b] of a previous verify block
+        int k = a.slot[u.b];
+        k = k < 0 ? 0 : (k > a.slot_T - 1 ? a.slot_T - 1 : k);
+        src = (static_cast<size_t>(u.b) * a.slot_T + k) * a.Hv + u.h;
+    }
+    const float* Sin = a.S_in + src * DK * DV + u.j0;
 #pragma unroll
     for (int r = 0; r < G::RPT; ++r) {
         const float* src = Sin + static_cast<size_t>(rg + r * G::RG) * DV + 4 * cg;
@@ -325,10 +331,12 @@ __global__ __launch_bounds__(256) void commit_kernel(CommitArgs a) {
     const int h = bh - b * a.Hv;
     int acc = a.accept[b];
     acc = acc < 0 ? 0 : (acc > a.T - 1 ? a.T - 1 : acc);
-    const float4* src = reinterpret_cast<const float4*>(
-        a.S_snap + ((static_cast<size_t>(b) * a.T + acc) * a.Hv + h) * DK * DV);
-    float4* dst = reinterpret_cast<float4*>(a.S_out + static_cast<size_t>(bh) * DK * DV);
-    for (int e = threadIdx.x; e < DK * DV / 4; e += 256) dst[e] = src[e];
+    if (a.S_out != nullptr) {
+        const float4* src = reinterpret_cast<const float4*>(
+            a.S_snap + ((static_cast<size_t>(b) * a.T + acc) * a.Hv + h) * DK * DV);
+        float4* dst = reinterpret_cast<float4*>(a.S_out + static_cast<size_t>(bh) * DK * DV);
+        for (int e = threadIdx.x; e < DK * DV / 4; e += 256) dst[e] = src[e];
+    }
 
     const Tin* x = static_cast<const Tin*>(a.qkv);
     const Tin* cin = static_cast<const Tin*>(a.conv_in);

@@ -183,3 +183,28 @@ def test_fusion_validation(lib):
     assert dec(None, B=0) == OK
     # fields of a disabled fusion are ignored (dt_bias without A_log, eps without z)
     assert dec(F(dt_bias=A(8), eps=float("nan")), B=0) == OK
+
+
+def test_verify_slots_and_window_only_commit_validation(lib):
+    p = P()
+
+    def vs(B=4, T=4, S_prev=A(7), T_prev=4, slot=A(10), S_snap=A(9), o=A(8)):
+        return lib.gdn_verify_block_slots(p, None, B, T, A(1), A(2), A(3), A(4), A(5), S_prev, T_prev,
+                                          slot, S_snap, o, None)
+
+    assert vs(slot=None) == NULL
+    assert vs(S_prev=None) == NULL
+    assert vs(T_prev=0) == SHAPE
+    assert vs(T_prev=17) == UNSUP
+    assert vs(S_snap=A(7), T_prev=3) == ALIAS          # same buffer, different block widths
+    assert vs(S_snap=ctypes.c_void_p(0x7f0000000000 + 7 * 0x100000000 + 4096), T_prev=4) == ALIAS
+    assert vs(slot=A(9)) == ALIAS                        # slot inside the snapshots being written
+    assert vs(B=0) == OK
+    assert vs(B=0, S_snap=A(7)) == OK                    # in place (T == T_prev)
+
+    def commit(S_snap=A(9), S_out=A(7), cout=A(6)):
+        return lib.gdn_verify_commit(p, 4, 4, A(10), A(1), A(5), S_snap, cout, S_out, None)
+
+    assert commit(S_snap=None) == NULL                   # one of the two only
+    assert commit(S_out=None) == NULL
+    assert commit(S_snap=None, S_out=None, cout=A(5)) == ALIAS
