@@ -46,7 +46,7 @@
  *     validated on the host; the kernels clamp them (stated per call) so that
  *     no value makes them read or write out of bounds.
  *   - The library is stateless and reentrant. Calls on one stream run in order.
- *   - Supported set: head_k_dim == head_v_dim in {16, 128}; conv_kernel == 4;
+ *   - Supported set: head_k_dim == head_v_dim in {16, 64, 128}; conv_kernel == 4;
  *     Hv % Hk == 0; verify T in [1, 16]; prefill chunk == 64. Anything else
  *     returns GDN_ERR_UNSUPPORTED.
  */

@@ -47,7 +47,8 @@ gdn_status check_params(const gdn_params* p) {
     if (p->num_v_heads % p->num_k_heads != 0) return GDN_ERR_SHAPE;
     if (p->use_qk_l2norm != 0 && p->use_qk_l2norm != 1) return GDN_ERR_SHAPE;
     if (!std::isfinite(p->l2norm_eps) || p->l2norm_eps < 0.f) return GDN_ERR_SHAPE;
-    if (p->head_k_dim != p->head_v_dim || (p->head_k_dim != 16 && p->head_k_dim != 128))
+    if (p->head_k_dim != p->head_v_dim ||
+        (p->head_k_dim != 16 && p->head_k_dim != 64 && p->head_k_dim != 128))
         return GDN_ERR_UNSUPPORTED;
     if (p->conv_kernel != kK) return GDN_ERR_UNSUPPORTED;
     const long long D = 2LL * p->num_k_heads * p->head_k_dim + 1LL * p->num_v_heads * p->head_v_dim;

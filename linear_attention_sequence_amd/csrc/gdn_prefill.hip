@@ -480,6 +480,7 @@ static hipError_t launch_epi_t(const PrefillArgs& a, hipStream_t stream) {
 
 hipError_t launch_prefill_epilogue(const PrefillArgs& a, int in_dtype, int d, hipStream_t stream) {
     if (d == 128) return in_dtype == 1 ? launch_epi_t<bf16_t, 128>(a, stream) : launch_epi_t<float, 128>(a, stream);
+    if (d == 64) return in_dtype == 1 ? launch_epi_t<bf16_t, 64>(a, stream) : launch_epi_t<float, 64>(a, stream);
     return in_dtype == 1 ? launch_epi_t<bf16_t, 16>(a, stream) : launch_epi_t<float, 16>(a, stream);
 }
 
@@ -489,6 +490,10 @@ static hipError_t launch_prefill_core(const PrefillArgs& a, int in_dtype, int d,
     if (d == 128) {
         return in_dtype == 1 ? launch_prefill_mfma(a, in_dtype, stream)
                              : launch_prefill_t<float, 128>(a, in_dtype, stream);
+    }
+    if (d == 64) {   // the dense products stay on the vector ALUs at this head size
+        return in_dtype == 1 ? launch_prefill_t<bf16_t, 64>(a, in_dtype, stream)
+                             : launch_prefill_t<float, 64>(a, in_dtype, stream);
     }
     return in_dtype == 1 ? launch_prefill_t<bf16_t, 16>(a, in_dtype, stream)
                          : launch_prefill_t<float, 16>(a, in_dtype, stream);

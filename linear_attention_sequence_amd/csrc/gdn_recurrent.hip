@@ -391,6 +391,10 @@ hipError_t launch_recurrent(const RecArgs& a, int in_dtype, int d, hipStream_t s
         return in_dtype == 1 ? launch_rec<bf16_t, 128, 128, 512, 128, true, false>(a, stream)
                              : launch_rec<float, 128, 128, 512, 128, true, false>(a, stream);
     }
+    if (d == 64) {   // 256 threads, 4 float4 of the 64 x 64 tile each
+        return in_dtype == 1 ? launch_rec<bf16_t, 64, 64, 256, 64, true, false>(a, stream)
+                             : launch_rec<float, 64, 64, 256, 64, true, false>(a, stream);
+    }
     return in_dtype == 1 ? launch_rec<bf16_t, 16, 16, 64, 16, true, false>(a, stream)
                          : launch_rec<float, 16, 16, 64, 16, true, false>(a, stream);
 }
@@ -406,6 +410,10 @@ hipError_t launch_commit(const CommitArgs& a, int in_dtype, int d, hipStream_t s
     if (d == 128) {
         return in_dtype == 1 ? launch_com<bf16_t, 128, 128>(a, stream)
                              : launch_com<float, 128, 128>(a, stream);
+    }
+    if (d == 64) {
+        return in_dtype == 1 ? launch_com<bf16_t, 64, 64>(a, stream)
+                             : launch_com<float, 64, 64>(a, stream);
     }
     return in_dtype == 1 ? launch_com<bf16_t, 16, 16>(a, stream)
                          : launch_com<float, 16, 16>(a, stream);

@@ -71,7 +71,8 @@ def test_param_validation(lib):
     assert decode(lib, P(use_qk_l2norm=2)) == SHAPE
     assert decode(lib, P(l2norm_eps=-1.0)) == SHAPE
     assert decode(lib, P(l2norm_eps=float("nan"))) == SHAPE
-    assert decode(lib, P(head_k_dim=64, head_v_dim=64)) == UNSUP
+    assert decode(lib, P(head_k_dim=32, head_v_dim=32)) == UNSUP
+    assert decode(lib, P(head_k_dim=256, head_v_dim=256)) == UNSUP
     assert decode(lib, P(head_k_dim=128, head_v_dim=16)) == UNSUP
     assert decode(lib, P(conv_kernel=3)) == UNSUP
 
