@@ -588,7 +588,7 @@ __device__ __forceinline__ f16x8 lds_a(const _Float16* base, int row, int ks, in
     return f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-extern __shared__ __align__(1024) unsigned char g_stage[];   // 2 stages
+extern __shared__ __align__(1024) unsigned char g_stage[];   // 2 stages (+ output tiles)
 
 // Issue the wave-wide 1 KB global->LDS loads of the regions of one stage that
 // PARTS selects (bits: W, Q, KT, P, U, coefficients). Every region starts on a
@@ -654,6 +654,12 @@ __device__ __forceinline__ void issue_stage(const PrefillArgs& a, const Ws& ws, 
 template <int NTW, int NW>
 __global__ __launch_bounds__(NW * 64) void carry_kernel(PrefillArgs a, Ws ws) {
     constexpr int CPW = NW * NTW * 16;
+    // One wave per SIMD (NW <= 4) leaves registers to hold a whole phase's operands:
+    // their LDS reads are then issued ahead of the phase's MFMAs under one wait (a
+    // scheduling barrier keeps them there). With two waves per SIMD the waves hide
+    // each other's latency and the loops are left to the compiler, which would
+    // otherwise spill.
+    constexpr bool BATCH = NW <= 4;
     using SG = Stage<CPW>;
     const int nh = a.N * a.Hv;
     const int cs = blockIdx.x / nh;                      // the CS workgroups of a head share blockIdx % 8 (XCD)
@@ -730,27 +736,64 @@ __global__ __launch_bounds__(NW * 64) void carry_kernel(PrefillArgs a, Ws ws) {
         // Delta = U - W S (rows past the end of the sequence are zero)
         float dl[4][NTW][4];
         float dmax = 0.f;
+        if constexpr (BATCH) {
+            f16x8 aw[4][4];
+            _Float16 uh[4][NTW][4];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            f32x4v acc[NTW];
+            for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) acc[nt] = f32x4v{0, 0, 0, 0};
+                for (int ks = 0; ks < 4; ++ks) aw[mt][ks] = lds_a<16>(Wl, 16 * mt + r16, ks, g);
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const f16x8 aw = lds_a<16>(Wl, 16 * mt + r16, ks, g);
+            for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                for (int nt = 0; nt < NTW; ++nt) acc[nt] = mfma16x16x32(aw, sb[nt][ks], acc[nt]);
+                for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        uh[mt][nt][e] = Ul[(16 * mt + 4 * g + e) * 8 * SG::UG + lcol0 + 16 * nt + r16];
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                f32x4v acc[NTW];
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt) acc[nt] = f32x4v{0, 0, 0, 0};
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                    for (int nt = 0; nt < NTW; ++nt) acc[nt] = mfma16x16x32(aw[mt][ks], sb[nt][ks], acc[nt]);
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int t = 16 * mt + 4 * g + e;
+                        const float u = static_cast<float>(uh[mt][nt][e]);
+                        const float d = (t < ntc) ? __fmaf_rn(u, uscale, -iS * acc[nt][e]) : 0.f;
+                        dl[mt][nt][e] = d;
+                        dmax = fmaxf(dmax, fabsf(d));
+                    }
             }
-#pragma unroll
-            for (int nt = 0; nt < NTW; ++nt)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int t = 16 * mt + 4 * g + e;
-                    const float u = static_cast<float>(Ul[t * 8 * SG::UG + lcol0 + 16 * nt + r16]);
-                    const float d = (t < ntc) ? __fmaf_rn(u, uscale, -iS * acc[nt][e]) : 0.f;
-                    dl[mt][nt][e] = d;
-                    dmax = fmaxf(dmax, fabsf(d));
+        } else {
+    #pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                f32x4v acc[NTW];
+    #pragma unroll
+                for (int nt = 0; nt < NTW; ++nt) acc[nt] = f32x4v{0, 0, 0, 0};
+    #pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    const f16x8 aw = lds_a<16>(Wl, 16 * mt + r16, ks, g);
+    #pragma unroll
+                    for (int nt = 0; nt < NTW; ++nt) acc[nt] = mfma16x16x32(aw, sb[nt][ks], acc[nt]);
                 }
+    #pragma unroll
+                for (int nt = 0; nt < NTW; ++nt)
+    #pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int t = 16 * mt + 4 * g + e;
+                        const float u = static_cast<float>(Ul[t * 8 * SG::UG + lcol0 + 16 * nt + r16]);
+                        const float d = (t < ntc) ? __fmaf_rn(u, uscale, -iS * acc[nt][e]) : 0.f;
+                        dl[mt][nt][e] = d;
+                        dmax = fmaxf(dmax, fabsf(d));
+                    }
+            }
         }
         const int eD = pow2_exponent(wave_max_nonneg(dmax));
         const float sD = ldexpf(1.f, -eD), iD = ldexpf(1.f, eD);
@@ -771,9 +814,27 @@ __global__ __launch_bounds__(NW * 64) void carry_kernel(PrefillArgs a, Ws ws) {
         if (more)
             issue_stage<CPW, NW, ST_Q | ST_P>(a, ws, id + 1, tok0 + C, ntn, h, hk, ucol0, (c + 1) & 1, wave, lane);
 
-        // O = diag(exp(Gam)) Q S + P Delta, stored as soon as a 16-token tile is done
+        // O = diag(exp(Gam)) Q S + P Delta, stored as soon as it is formed. With four
+        // waves of one tile each (LDS to spare past the two stages) a wave's 64 x 16
+        // tile is transposed through its own 4 KB of LDS and stored token-major, 16
+        // bytes per lane: 4 store instructions instead of 16 scattered dword stores
+        // (14.1k instead of 15.4k cycles per chunk). With eight waves there is no room
+        // and reusing the stage's dead W region needs a barrier, which cost more.
+        constexpr bool OT = NTW == 1 && NW <= 4;
         float* ob = a.o + (tok0 * a.Hv + h) * D + col0 + r16 + 4 * g * ts;
+        float* obuf = reinterpret_cast<float*>(g_stage + 2 * SG::BYTES + wave * 4096);
         const bool full = ntc == C;                            // uniform: every row stored
+        f16x8 aq[4][4], ap[4][2];   // read ahead of the MFMAs when BATCH, else inside the loop
+        if constexpr (BATCH) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) aq[mt][ks] = lds_a<16>(Ql, 16 * mt + r16, ks, g);
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) ap[mt][ks] = lds_a<8>(Pl, 16 * mt + r16, ks, g);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
             f32x4v a1[NTW], a2[NTW];
@@ -781,24 +842,35 @@ __global__ __launch_bounds__(NW * 64) void carry_kernel(PrefillArgs a, Ws ws) {
             for (int nt = 0; nt < NTW; ++nt) { a1[nt] = f32x4v{0, 0, 0, 0}; a2[nt] = a1[nt]; }
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                const f16x8 aq = lds_a<16>(Ql, 16 * mt + r16, ks, g);
+                if constexpr (!BATCH) aq[mt][ks] = lds_a<16>(Ql, 16 * mt + r16, ks, g);
 #pragma unroll
-                for (int nt = 0; nt < NTW; ++nt) a1[nt] = mfma16x16x32(aq, sb[nt][ks], a1[nt]);
+                for (int nt = 0; nt < NTW; ++nt) a1[nt] = mfma16x16x32(aq[mt][ks], sb[nt][ks], a1[nt]);
             }
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const f16x8 ap = lds_a<8>(Pl, 16 * mt + r16, ks, g);
+                if constexpr (!BATCH) ap[mt][ks] = lds_a<8>(Pl, 16 * mt + r16, ks, g);
 #pragma unroll
-                for (int nt = 0; nt < NTW; ++nt) a2[nt] = mfma16x16x32(ap, db[nt][ks], a2[nt]);
+                for (int nt = 0; nt < NTW; ++nt) a2[nt] = mfma16x16x32(ap[mt][ks], db[nt][ks], a2[nt]);
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float eg = cf[16 * mt + 4 * g + e] * iS;
-                if (full || 16 * mt + 4 * g + e < ntc) {
+                if constexpr (OT) {
+                    obuf[(16 * mt + 4 * g + e) * 16 + r16] = __fmaf_rn(eg, a1[0][e], iD * a2[0][e]);
+                } else if (full || 16 * mt + 4 * g + e < ntc) {
                     float* orow = ob + (16 * mt + e) * ts;
 #pragma unroll
                     for (int nt = 0; nt < NTW; ++nt) orow[16 * nt] = __fmaf_rn(eg, a1[nt][e], iD * a2[nt][e]);
                 }
+            }
+        }
+        if constexpr (OT) {
+            float* orow0 = a.o + (tok0 * a.Hv + h) * D + col0 + 4 * (lane & 3);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 16 * i + (lane >> 2);
+                const float4 v = *reinterpret_cast<const float4*>(obuf + t * 16 + 4 * (lane & 3));
+                if (full || t < ntc) *reinterpret_cast<float4*>(orow0 + t * ts) = v;
             }
         }
         if (more)
@@ -806,6 +878,14 @@ __global__ __launch_bounds__(NW * 64) void carry_kernel(PrefillArgs a, Ws ws) {
 
         // S = exp(Gam_last) S + K^T diag(exp(Gam_last - Gam)) Delta; max|S| for the next chunk
         smax = 0.f;
+        f16x8 ak[8][2];
+        if constexpr (BATCH) {
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) ak[mt][ks] = lds_a<8>(KTl, 16 * mt + r16, ks, g);
+            __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
             f32x4v acc[NTW];
@@ -813,9 +893,9 @@ __global__ __launch_bounds__(NW * 64) void carry_kernel(PrefillArgs a, Ws ws) {
             for (int nt = 0; nt < NTW; ++nt) acc[nt] = f32x4v{0, 0, 0, 0};
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const f16x8 ak = lds_a<8>(KTl, 16 * mt + r16, ks, g);
+                if constexpr (!BATCH) ak[mt][ks] = lds_a<8>(KTl, 16 * mt + r16, ks, g);
 #pragma unroll
-                for (int nt = 0; nt < NTW; ++nt) acc[nt] = mfma16x16x32(ak, dp[nt][ks], acc[nt]);
+                for (int nt = 0; nt < NTW; ++nt) acc[nt] = mfma16x16x32(ak[mt][ks], dp[nt][ks], acc[nt]);
             }
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt)
@@ -867,7 +947,8 @@ static int device_cu_count() {
 template <int NTW, int NW>
 static hipError_t launch_carry(void** args, long long heads, hipStream_t stream) {
     constexpr int CPW = NW * NTW * 16;
-    constexpr size_t lds = 2 * pf2::Stage<CPW>::BYTES;
+    constexpr size_t lds = 2 * pf2::Stage<CPW>::BYTES + (NTW == 1 && NW <= 4 ? NW * 4096 : 0);   // + output tiles
+    static_assert(lds <= 160 * 1024, "LDS of one CU");
     const void* k = reinterpret_cast<const void*>(&pf2::carry_kernel<NTW, NW>);
     // dynamic LDS above 64 KB must be allowed per kernel before its first launch
     static const hipError_t allowed = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
