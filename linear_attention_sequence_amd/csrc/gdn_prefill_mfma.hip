@@ -651,6 +651,26 @@ __device__ __forceinline__ void issue_stage(const PrefillArgs& a, const Ws& ws, 
     }
 }
 
+constexpr int kSortMax = 256;   // packed sequences ranked by length in every carry workgroup
+
+// Sequence of rank r when the N packed sequences are ordered by decreasing length
+// (ties by index). Every thread ranks up to N / blockDim of them against all N.
+__device__ int sequence_of_rank(const PrefillArgs& a, int r) {
+    __shared__ int s_len[kSortMax];
+    __shared__ int s_pick;
+    for (int m = threadIdx.x; m < a.N; m += blockDim.x) s_len[m] = segment_of(m, a.L, a.cu).len;
+    if (threadIdx.x == 0) s_pick = r;   // a rank with no match (r >= N) keeps r (never happens)
+    __syncthreads();
+    for (int m = threadIdx.x; m < a.N; m += blockDim.x) {
+        const int lm = s_len[m];
+        int rank = 0;
+        for (int q = 0; q < a.N; ++q) rank += (s_len[q] > lm || (s_len[q] == lm && q < m)) ? 1 : 0;
+        if (rank == r) s_pick = m;
+    }
+    __syncthreads();
+    return s_pick;
+}
+
 template <int NTW, int NW>
 __global__ __launch_bounds__(NW * 64) void carry_kernel(PrefillArgs a, Ws ws) {
     constexpr int CPW = NW * NTW * 16;
@@ -661,12 +681,32 @@ __global__ __launch_bounds__(NW * 64) void carry_kernel(PrefillArgs a, Ws ws) {
     // otherwise spill.
     constexpr bool BATCH = NW <= 4;
     using SG = Stage<CPW>;
+    constexpr int NS = 128 / CPW;                        // workgroups per head
     const int nh = a.N * a.Hv;
-    const int cs = blockIdx.x / nh;                      // the CS workgroups of a head share blockIdx % 8 (XCD)
-    const int h = (blockIdx.x % nh) % a.Hv;
-    const int n = (blockIdx.x % nh) / a.Hv;
-    const int f = a.Hv / a.Hk, hk = h / f;
     const int tid = threadIdx.x, lane = tid & 63;
+    // blockIdx -> (column slice cs, slot). The NS slices of a slot are dispatched
+    // together and 8 blockIdx apart, i.e. on one XCD, sharing its L2 for the
+    // operands they all read; the tail that does not fill a group of 8 slots is
+    // laid out slice-major.
+    int cs = 0, slot = blockIdx.x;
+    if constexpr (NS > 1) {
+        const int grp = nh / 8, full = 8 * NS * grp;
+        if (static_cast<int>(blockIdx.x) < full) {
+            const int w = blockIdx.x % (8 * NS);
+            cs = w / 8;
+            slot = (blockIdx.x / (8 * NS)) * 8 + w % 8;
+        } else {
+            const int rem = blockIdx.x - full, tail = nh - 8 * grp;
+            cs = rem / tail;
+            slot = 8 * grp + rem % tail;
+        }
+    }
+    const int h = slot % a.Hv;
+    int n = slot / a.Hv;
+    // Packed prompts: slots go to sequences longest first, so that the in-order
+    // dispatch of workgroups to free CUs schedules the longest chains first.
+    if (a.cu != nullptr && a.N <= kSortMax) n = sequence_of_rank(a, n);
+    const int f = a.Hv / a.Hk, hk = h / f;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, r16 = lane & 15;
     const int ucol0 = cs * CPW;                          // first column of this workgroup
@@ -976,9 +1016,13 @@ static hipError_t launch_mfma_t(const PrefillArgs& a, int in_dtype, hipStream_t 
     }
     const long long heads = static_cast<long long>(a.N) * a.Hv;
     if (heads > 0) {
-        // split each head over two workgroups when that still fits one round of the CUs
-        e = (2 * heads <= device_cu_count()) ? launch_carry<1, 4>(args, heads, stream)
-                                             : launch_carry<CARRY_NTW, CARRY_NW>(args, heads, stream);
+        // Split each head over two workgroups when that still fits one round of the
+        // CUs, and for packed prompts when it fits two: their chains differ in length
+        // and, dispatched longest first, the halves finish sooner than whole heads
+        // (8 sequences of 512..8192 tokens: 567 -> 544 us, bound by the longest chain)
+        const int cus = device_cu_count();
+        const bool split = 2 * heads <= cus || (a.cu != nullptr && a.N <= pf2::kSortMax && heads <= cus);
+        e = split ? launch_carry<1, 4>(args, heads, stream) : launch_carry<CARRY_NTW, CARRY_NW>(args, heads, stream);
         if (e != hipSuccess) return e;
     }
     ConvArgs ca{a.B, a.L, a.D, a.N, a.qkv, a.w, a.conv_in, a.conv_out, nullptr, a.cu};
