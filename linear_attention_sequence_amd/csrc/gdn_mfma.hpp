@@ -45,12 +45,15 @@ __device__ __forceinline__ float wave_max_nonneg(float x) {
 
 // Power-of-two scale that brings max|x| into [2^14, 2^15): inside fp16's range
 // with room to spare. Returns the exponent e; values are stored as x * 2^-e and
-// results multiplied back by 2^e (both exact).
+// results multiplied back by 2^e (both exact). The exponent is kept >= -100 so
+// that 2^-e stays finite when max|x| is far below fp32's normal range (a state
+// map that has decayed for many chunks): values under 2^-124 then flush to zero
+// in fp16, which is at most 2^-39 of the largest one.
 __device__ __forceinline__ int pow2_exponent(float maxabs) {
     if (!(maxabs > 0.f) || !isfinite(maxabs)) return 0;
     int ex;
     frexpf(maxabs, &ex);  // maxabs = m * 2^ex, m in [0.5, 1)
-    return ex - 15;
+    return ex - 15 < -100 ? -100 : ex - 15;
 }
 
 }  // namespace gdn

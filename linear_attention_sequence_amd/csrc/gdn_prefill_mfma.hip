@@ -55,7 +55,15 @@ struct Ws {
     _Float16* P;    // [NC, Hv, C, C]
     _Float16* KT;   // [NC, Hk, D, C]  keys of the chunk, transposed
     float* coef;    // [NC, Hv, COEF]: exp(Gam_t), exp(Gam_last - Gam_t), exp(Gam_last), 2^uexp
+    // two-segment carry (see carry_kernel): per sequence the chunks split at cm = nch / 2
+    _Float16* SmidT;  // [N, Hv, D, D] state after the first segment, transposed ([column][row]),
+                      // scaled per 16-column tile by 2^-Sexp
+    int* Sexp;        // [N, Hv, D / 16] those scale exponents
+    float* R;       // [N, Hv, D, D] second segment's end state from a zero entry state
+    float* M;       // [N, Hv, D, D] second segment's state map (its end state from the identity)
+    float* Y;       // [nch - cm, N, Hv, C, D] outputs of the identity columns
     int nc_max;
+    int seg;        // 1: the two-segment carry is in use
     size_t bytes;
 };
 
@@ -64,6 +72,14 @@ static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255);
 static int max_chunks(int B, int L, int N, bool ragged) {
     const int per = (L + C - 1) / C;
     return ragged ? per + N : B * per;
+}
+
+// Unpacked prompts whose heads leave the CUs idle run the carry in two segments:
+// 6 workgroups per head (3 kinds x 2 column halves) must fit one round of the
+// CUs (6 x 42 = 252 <= 256) and each sequence needs at least two chunks.
+constexpr int kSegHeads = 42;
+static bool use_segments(int B, int L, int N, int Hv, bool ragged) {
+    return !ragged && static_cast<long long>(N) * Hv <= kSegHeads && (L + C - 1) / C >= 2 && B == N;
 }
 
 static Ws layout(void* base, int B, int L, int N, int Hk, int Hv, bool ragged) {
@@ -84,6 +100,19 @@ static Ws layout(void* base, int B, int L, int N, int Hk, int Hv, bool ragged) {
     w.P = static_cast<_Float16*>(take(nc * Hv * C * C * 2));
     w.KT = static_cast<_Float16*>(take(nc * Hk * D * C * 2));
     w.coef = static_cast<float*>(take(nc * Hv * COEF * 4));
+    w.seg = use_segments(B, L, N, Hv, ragged) ? 1 : 0;
+    w.SmidT = nullptr;
+    w.Sexp = nullptr;
+    w.R = w.M = w.Y = nullptr;
+    if (w.seg) {
+        const int nch = (L + C - 1) / C, n2 = nch - nch / 2;
+        const size_t tiles = static_cast<size_t>(N) * Hv * D * D;
+        w.SmidT = static_cast<_Float16*>(take(tiles * 2));
+        w.Sexp = static_cast<int*>(take(static_cast<size_t>(N) * Hv * (D / 16) * 4));
+        w.R = static_cast<float*>(take(tiles * 4));
+        w.M = static_cast<float*>(take(tiles * 4));
+        w.Y = static_cast<float*>(take(static_cast<size_t>(n2) * N * Hv * C * D * 4));
+    }
     w.nc_max = static_cast<int>(nc);
     w.bytes = off;
     return w;
@@ -684,23 +713,33 @@ __global__ __launch_bounds__(NW * 64) void carry_kernel(PrefillArgs a, Ws ws) {
     constexpr int NS = 128 / CPW;                        // workgroups per head
     const int nh = a.N * a.Hv;
     const int tid = threadIdx.x, lane = tid & 63;
-    // blockIdx -> (column slice cs, slot). The NS slices of a slot are dispatched
-    // together and 8 blockIdx apart, i.e. on one XCD, sharing its L2 for the
-    // operands they all read; the tail that does not fill a group of 8 slots is
-    // laid out slice-major.
-    int cs = 0, slot = blockIdx.x;
-    if constexpr (NS > 1) {
-        const int grp = nh / 8, full = 8 * NS * grp;
+    // Two-segment mode (ws.seg): the chunks of each sequence split at cm = nch / 2 and
+    // three kinds of workgroup run at once: FIRST carries the first segment from the
+    // entry state; LOCAL carries the second from a zero state; XMAP carries the
+    // identity through the second with U = 0, so that its columns are the segment's
+    // state map M (S_end = M S_mid + R, the chunk maps being affine in the entry
+    // state) and its outputs Y give the entry state's share of every output
+    // (o = o_local + Y S_mid). seg_fix_kernel adds those shares afterwards.
+    const int NK = ws.seg ? 3 : 1;                       // kinds per head
+    // blockIdx -> (slice, slot): the NK * NS slices of a slot are dispatched together
+    // and 8 blockIdx apart, i.e. on one XCD, sharing its L2 for the operands they
+    // read; the tail that does not fill a group of 8 slots is laid out slice-major.
+    int slice = 0, slot = blockIdx.x;
+    if (NK * NS > 1) {
+        const int nsl = NK * NS, grp = nh / 8, full = 8 * nsl * grp;
         if (static_cast<int>(blockIdx.x) < full) {
-            const int w = blockIdx.x % (8 * NS);
-            cs = w / 8;
-            slot = (blockIdx.x / (8 * NS)) * 8 + w % 8;
+            const int w = blockIdx.x % (8 * nsl);
+            slice = w / 8;
+            slot = (blockIdx.x / (8 * nsl)) * 8 + w % 8;
         } else {
             const int rem = blockIdx.x - full, tail = nh - 8 * grp;
-            cs = rem / tail;
+            slice = rem / tail;
             slot = 8 * grp + rem % tail;
         }
     }
+    const int cs = slice % NS;
+    const int kind = slice / NS;                         // 0 FIRST (or the whole chain), 1 LOCAL, 2 XMAP
+    const bool xm = kind == 2;
     const int h = slot % a.Hv;
     int n = slot / a.Hv;
     // Packed prompts: slots go to sequences longest first, so that the in-order
@@ -718,8 +757,12 @@ __global__ __launch_bounds__(NW * 64) void carry_kernel(PrefillArgs a, Ws ws) {
     int nch = chunks_of(seg);
     if (base + nch > ws.nc_max) nch = ws.nc_max - base;   // only malformed cu_seqlens get here
     if (nch <= 0) return;
+    const int cm = nch / 2;                              // segment boundary (two-segment mode)
+    const int cb = (ws.seg && kind > 0) ? cm : 0;        // chunks [cb, ce) of this workgroup
+    const int ce = (ws.seg && kind == 0) ? cm : nch;
 
-    float* Sg = a.S + (static_cast<size_t>(n) * a.Hv + h) * D * D;
+    const size_t tile = (static_cast<size_t>(n) * a.Hv + h) * D * D;
+    float* Sg = a.S + tile;
     float S[8][NTW][4];
     float smax = 0.f;
 #pragma unroll
@@ -728,28 +771,39 @@ __global__ __launch_bounds__(NW * 64) void carry_kernel(PrefillArgs a, Ws ws) {
         for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                S[mt][nt][e] = Sg[(16 * mt + 4 * g + e) * D + col0 + 16 * nt + r16];
+                const int i = 16 * mt + 4 * g + e, j = col0 + 16 * nt + r16;
+                S[mt][nt][e] = kind == 0 ? Sg[i * D + j] : (xm && i == j ? 1.f : 0.f);
                 smax = fmaxf(smax, fabsf(S[mt][nt][e]));
             }
 
     const size_t row_tok = static_cast<size_t>(seg.row) * a.L + seg.start;
-    const size_t ts = static_cast<size_t>(a.Hv) * D;   // token stride of o
-    issue_stage<CPW, NW, ST_ALL>(a, ws, base, row_tok, min(C, seg.len), h, hk, ucol0, 0, wave, lane);
+    // outputs: o (token stride Hv * D), or for XMAP the per-chunk blocks of Y
+    const size_t ts = xm ? static_cast<size_t>(D) : static_cast<size_t>(a.Hv) * D;
+    if (xm)
+        issue_stage<CPW, NW, ST_ALL & ~ST_U>(a, ws, base + cb, row_tok + static_cast<size_t>(cb) * C,
+                                            min(C, seg.len - cb * C), h, hk, ucol0, 0, wave, lane);
+    else
+        issue_stage<CPW, NW, ST_ALL>(a, ws, base + cb, row_tok + static_cast<size_t>(cb) * C,
+                                     min(C, seg.len - cb * C), h, hk, ucol0, 0, wave, lane);
     // The next chunk's stage is issued in three parts spread over this chunk's
     // phases (each part before the phase that would otherwise wait on the memory
     // pipeline), so that the vector-memory issue queue never backs up the MFMA work.
-    for (int c = 0; c < nch; ++c) {
+    for (int c = cb; c < ce; ++c) {
         __builtin_amdgcn_s_waitcnt(0);   // this wave's share of the stage has landed
         __syncthreads();                 // ... and every wave's; the other stage is free
         const int id = base + c;
         const int ntc = min(C, seg.len - c * C);
         const size_t tok0 = row_tok + static_cast<size_t>(c) * C;
-        const bool more = c + 1 < nch;
+        const bool more = c + 1 < ce;
         const int ntn = min(C, seg.len - (c + 1) * C);
-        if (more)
-            issue_stage<CPW, NW, ST_W | ST_U | ST_CF>(a, ws, id + 1, tok0 + C, ntn, h, hk, ucol0, (c + 1) & 1,
-                                                      wave, lane);
-        const unsigned char* st = g_stage + (c & 1) * SG::BYTES;
+        const int sb_ = (c - cb + 1) & 1;                // stage buffer of the next chunk
+        if (more) {
+            if (xm)
+                issue_stage<CPW, NW, ST_W | ST_CF>(a, ws, id + 1, tok0 + C, ntn, h, hk, ucol0, sb_, wave, lane);
+            else
+                issue_stage<CPW, NW, ST_W | ST_U | ST_CF>(a, ws, id + 1, tok0 + C, ntn, h, hk, ucol0, sb_, wave, lane);
+        }
+        const unsigned char* st = g_stage + ((c - cb) & 1) * SG::BYTES;
         const _Float16* Wl = reinterpret_cast<const _Float16*>(st + SG::W * 16);
         const _Float16* Ql = reinterpret_cast<const _Float16*>(st + SG::Q * 16);
         const _Float16* KTl = reinterpret_cast<const _Float16*>(st + SG::KT * 16);
@@ -789,7 +843,8 @@ __global__ __launch_bounds__(NW * 64) void carry_kernel(PrefillArgs a, Ws ws) {
                 for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        uh[mt][nt][e] = Ul[(16 * mt + 4 * g + e) * 8 * SG::UG + lcol0 + 16 * nt + r16];
+                        uh[mt][nt][e] = xm ? static_cast<_Float16>(0.f)
+                                           : Ul[(16 * mt + 4 * g + e) * 8 * SG::UG + lcol0 + 16 * nt + r16];
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
@@ -828,7 +883,7 @@ __global__ __launch_bounds__(NW * 64) void carry_kernel(PrefillArgs a, Ws ws) {
     #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int t = 16 * mt + 4 * g + e;
-                        const float u = static_cast<float>(Ul[t * 8 * SG::UG + lcol0 + 16 * nt + r16]);
+                        const float u = xm ? 0.f : static_cast<float>(Ul[t * 8 * SG::UG + lcol0 + 16 * nt + r16]);
                         const float d = (t < ntc) ? __fmaf_rn(u, uscale, -iS * acc[nt][e]) : 0.f;
                         dl[mt][nt][e] = d;
                         dmax = fmaxf(dmax, fabsf(d));
@@ -852,7 +907,7 @@ __global__ __launch_bounds__(NW * 64) void carry_kernel(PrefillArgs a, Ws ws) {
                 }
 
         if (more)
-            issue_stage<CPW, NW, ST_Q | ST_P>(a, ws, id + 1, tok0 + C, ntn, h, hk, ucol0, (c + 1) & 1, wave, lane);
+            issue_stage<CPW, NW, ST_Q | ST_P>(a, ws, id + 1, tok0 + C, ntn, h, hk, ucol0, sb_, wave, lane);
 
         // O = diag(exp(Gam)) Q S + P Delta, stored as soon as it is formed. With four
         // waves of one tile each (LDS to spare past the two stages) a wave's 64 x 16
@@ -861,7 +916,10 @@ __global__ __launch_bounds__(NW * 64) void carry_kernel(PrefillArgs a, Ws ws) {
         // (14.1k instead of 15.4k cycles per chunk). With eight waves there is no room
         // and reusing the stage's dead W region needs a barrier, which cost more.
         constexpr bool OT = NTW == 1 && NW <= 4;
-        float* ob = a.o + (tok0 * a.Hv + h) * D + col0 + r16 + 4 * g * ts;
+        // this chunk's first output row: o, or for XMAP its block of Y
+        float* obase = xm ? ws.Y + ((static_cast<size_t>(c - cm) * a.N + n) * a.Hv + h) * C * D
+                          : a.o + (tok0 * a.Hv + h) * D;
+        float* ob = obase + col0 + r16 + 4 * g * ts;
         float* obuf = reinterpret_cast<float*>(g_stage + 2 * SG::BYTES + wave * 4096);
         const bool full = ntc == C;                            // uniform: every row stored
         f16x8 aq[4][4], ap[4][2];   // read ahead of the MFMAs when BATCH, else inside the loop
@@ -905,7 +963,7 @@ __global__ __launch_bounds__(NW * 64) void carry_kernel(PrefillArgs a, Ws ws) {
             }
         }
         if constexpr (OT) {
-            float* orow0 = a.o + (tok0 * a.Hv + h) * D + col0 + 4 * (lane & 3);
+            float* orow0 = obase + col0 + 4 * (lane & 3);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = 16 * i + (lane >> 2);
@@ -914,7 +972,7 @@ __global__ __launch_bounds__(NW * 64) void carry_kernel(PrefillArgs a, Ws ws) {
             }
         }
         if (more)
-            issue_stage<CPW, NW, ST_KT>(a, ws, id + 1, tok0 + C, ntn, h, hk, ucol0, (c + 1) & 1, wave, lane);
+            issue_stage<CPW, NW, ST_KT>(a, ws, id + 1, tok0 + C, ntn, h, hk, ucol0, sb_, wave, lane);
 
         // S = exp(Gam_last) S + K^T diag(exp(Gam_last - Gam)) Delta; max|S| for the next chunk
         smax = 0.f;
@@ -946,12 +1004,140 @@ __global__ __launch_bounds__(NW * 64) void carry_kernel(PrefillArgs a, Ws ws) {
                 }
         }
     }
+    // end state: S, or in two-segment mode S_mid (transposed, [column][row]), R or M
+    if (ws.seg && kind == 0) {   // fp16, scaled per wave (its 16-column tiles), the exponent beside it
+        const int ef = pow2_exponent(wave_max_nonneg(smax));
+        const float sf = ldexpf(1.f, -ef);
+        _Float16* dst = ws.SmidT + tile;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
+        for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < NTW; ++nt)
+            for (int nt = 0; nt < NTW; ++nt) {
+                const f16x4 v = {static_cast<_Float16>(S[mt][nt][0] * sf), static_cast<_Float16>(S[mt][nt][1] * sf),
+                                 static_cast<_Float16>(S[mt][nt][2] * sf), static_cast<_Float16>(S[mt][nt][3] * sf)};
+                *reinterpret_cast<f16x4*>(dst + (col0 + 16 * nt + r16) * D + 16 * mt + 4 * g) = v;
+            }
+        if (lane < NTW) ws.Sexp[(static_cast<size_t>(n) * a.Hv + h) * (D / 16) + col0 / 16 + lane] = ef;
+    } else {
+        float* dst = !ws.seg ? Sg : (xm ? ws.M + tile : ws.R + tile);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) Sg[(16 * mt + 4 * g + e) * D + col0 + 16 * nt + r16] = S[mt][nt][e];
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dst[(16 * mt + 4 * g + e) * D + col0 + 16 * nt + r16] = S[mt][nt][e];
+    }
+}
+
+// Second-segment corrections of the two-segment carry on fp16 MFMA, with the
+// same power-of-two operand scaling as the carry: per head, ceil(n2 / 4)
+// workgroups add Y_c S_mid to the outputs of the second segment's n2 chunks (one
+// chunk of 64 rows per wave), two more write the final state M S_mid + R (16 rows
+// per wave). A rows (of Y or M, fp32) are scaled per 16-row tile, S_mid per
+// 16-column tile (stored that way by the first segment's workgroups); both scales
+// factor out of the tile's product, which is then added to acc (the local outputs,
+// or R) in fp32.
+template <int MT>
+__device__ __forceinline__ void fix_tiles(const float* A, int nrows, const _Float16* SmT, const int* sexp, int lane,
+                                          f32x4v (&acc)[MT][8]) {
+    const int g = lane >> 4, r16 = lane & 15;
+    f16x8 bop[8][4];
+    int eb[8];
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+        eb[nt] = sexp[nt];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            bop[nt][ks] = *reinterpret_cast<const f16x8*>(SmT + (16 * nt + r16) * D + 32 * ks + 8 * g);
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        float4 av[8];
+        float amax = 0.f;
+        const bool rv = 16 * mt + r16 < nrows;   // rows past the end of a partial chunk were never written
+        const int rr = rv ? 16 * mt + r16 : 0;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {   // k = 32 (q / 2) + 8 g + 4 (q % 2) + 0..3
+            const float4 v = *reinterpret_cast<const float4*>(A + rr * D + 32 * (q >> 1) + 8 * g + 4 * (q & 1));
+            av[q] = rv ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(av[q].x), fabsf(av[q].y)), fmaxf(fabsf(av[q].z), fabsf(av[q].w))));
+        }
+        const int ea = pow2_exponent(wave_max_nonneg(amax));
+        const float sa = ldexpf(1.f, -ea);
+        f16x8 aop[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const float4 lo = av[2 * ks], hi = av[2 * ks + 1];
+            aop[ks] = f16x8{static_cast<_Float16>(lo.x * sa), static_cast<_Float16>(lo.y * sa),
+                            static_cast<_Float16>(lo.z * sa), static_cast<_Float16>(lo.w * sa),
+                            static_cast<_Float16>(hi.x * sa), static_cast<_Float16>(hi.y * sa),
+                            static_cast<_Float16>(hi.z * sa), static_cast<_Float16>(hi.w * sa)};
+        }
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+            f32x4v prod = f32x4v{0, 0, 0, 0};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) prod = mfma16x16x32(aop[ks], bop[nt][ks], prod);
+            const float sc = ldexpf(1.f, ea + eb[nt]);   // may underflow to 0: the product is then negligible
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[mt][nt][e] = __fmaf_rn(prod[e], sc, acc[mt][nt][e]);
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void seg_fix_kernel(PrefillArgs a, Ws ws) {
+    const int nch = (a.L + C - 1) / C, cm = nch / 2, n2 = nch - cm;
+    const int nob = (n2 + 3) / 4, per = nob + 2;
+    const int r = blockIdx.x % per, nhid = blockIdx.x / per;
+    const int n = nhid / a.Hv, h = nhid % a.Hv;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, r16 = lane & 15;
+    const size_t tile = (static_cast<size_t>(n) * a.Hv + h) * D * D;
+    const _Float16* SmT = ws.SmidT + tile;
+    const int* sexp = ws.Sexp + (static_cast<size_t>(n) * a.Hv + h) * (D / 16);
+    if (r < nob) {                                   // outputs of chunk cm + 4r + wave
+        const int k2 = 4 * r + wave;
+        if (k2 >= n2) return;                        // whole wave
+        const int c = cm + k2;
+        const int ntc = min(C, a.L - c * C);
+        float* ob = a.o + ((static_cast<size_t>(n) * a.L + static_cast<size_t>(c) * C) * a.Hv + h) * D;
+        const size_t ts = static_cast<size_t>(a.Hv) * D;
+        // the local outputs start the accumulators; all loaded up front (rows past
+        // the end of a partial chunk read row 0 and are not stored back)
+        f32x4v acc[4][8];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 16 * mt + 4 * g + e, tc = t < ntc ? t : 0;
+#pragma unroll
+                for (int nt = 0; nt < 8; ++nt) acc[mt][nt][e] = ob[tc * ts + 16 * nt + r16];
+            }
+        fix_tiles<4>(ws.Y + ((static_cast<size_t>(k2) * a.N + n) * a.Hv + h) * C * D, ntc, SmT, sexp, lane, acc);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 16 * mt + 4 * g + e;
+                if (t < ntc) {
+#pragma unroll
+                    for (int nt = 0; nt < 8; ++nt) ob[t * ts + 16 * nt + r16] = acc[mt][nt][e];
+                }
+            }
+    } else {                                         // final state rows 64 (r - nob) + 16 wave ..
+        const int i0 = 64 * (r - nob) + 16 * wave;
+        const float* Rb = ws.R + tile;
+        float* Sb = a.S + tile;
+        f32x4v acc[1][8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt) acc[0][nt][e] = Rb[(i0 + 4 * g + e) * D + 16 * nt + r16];
+        fix_tiles<1>(ws.M + tile + static_cast<size_t>(i0) * D, 16, SmT, sexp, lane, acc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt) Sb[(i0 + 4 * g + e) * D + 16 * nt + r16] = acc[0][nt][e];
+    }
 }
 
 }  // namespace pf2
@@ -1022,7 +1208,16 @@ static hipError_t launch_mfma_t(const PrefillArgs& a, int in_dtype, hipStream_t 
         // (8 sequences of 512..8192 tokens: 567 -> 544 us, bound by the longest chain)
         const int cus = device_cu_count();
         const bool split = 2 * heads <= cus || (a.cu != nullptr && a.N <= pf2::kSortMax && heads <= cus);
-        e = split ? launch_carry<1, 4>(args, heads, stream) : launch_carry<CARRY_NTW, CARRY_NW>(args, heads, stream);
+        if (ws.seg) {   // two-segment carry: 3 kinds x 2 halves per head, then the corrections
+            e = launch_carry<1, 4>(args, 3 * heads, stream);
+            if (e != hipSuccess) return e;
+            const int nch = (a.L + pf2::C - 1) / pf2::C;
+            const int nob = (nch - nch / 2 + 3) / 4;
+            e = hipLaunchKernel(reinterpret_cast<const void*>(&pf2::seg_fix_kernel),
+                                dim3(static_cast<unsigned>(heads * (nob + 2))), dim3(256), args, 0, stream);
+        } else {
+            e = split ? launch_carry<1, 4>(args, heads, stream) : launch_carry<CARRY_NTW, CARRY_NW>(args, heads, stream);
+        }
         if (e != hipSuccess) return e;
     }
     ConvArgs ca{a.B, a.L, a.D, a.N, a.qkv, a.w, a.conv_in, a.conv_out, nullptr, a.cu};

@@ -287,9 +287,31 @@ def test_prefill_deterministic_and_ragged_equals_separate():
         one = {"qkv": inp["qkv"][:, :, s:e], "gate": inp["gate"][:, s:e], "beta": inp["beta"][:, s:e],
                "w": inp["w"], "conv0": inp["conv0"][n:n + 1], "S0": inp["S0"][n:n + 1]}
         r = run_prefill(shape, dtype, one)
-        assert torch.equal(r["o"][0], a["o"][0, s:e])
-        assert torch.equal(r["S"][0], a["S"][n])
         assert torch.equal(r["conv_out"][0], a["conv_out"][n])
+        if e - s <= 64:   # one chunk: the same carry as the packed call, bit for bit
+            assert torch.equal(r["o"][0], a["o"][0, s:e])
+            assert torch.equal(r["S"][0], a["S"][n])
+        else:             # a lone prompt of several chunks takes the two-segment carry
+            assert rel_err(r["o"][0], a["o"][0, s:e].double().cpu().numpy()) <= TOL[dtype]
+            assert rel_err(r["S"][0], a["S"][n].double().cpu().numpy()) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("L", [65, 128, 129, 200, 448, 700])
+def test_prefill_two_segment_carry(L):
+    """A lone prompt (few heads, several chunks) runs the carry in two segments with
+    affine corrections; the packed path (one sequence through cu_seqlens) never does.
+    Both agree with the oracle, and with each other within tolerance."""
+    shape, dtype = SMALL128, "bf16"
+    _say(f"two-segment carry L={L}")
+    inp = layer_inputs(shape, 1, L, 45, dtype, s0_std=0.1, conv_std=1.0)
+    seg = run_prefill(shape, dtype, inp)
+    packed = run_prefill(shape, dtype, inp, cu=gi.cu_seqlens([L]))
+    ref = oracle.gdn_forward(oparams(shape), inp["qkv"], inp["gate"], inp["beta"], inp["w"],
+                             inp["conv0"], inp["S0"])
+    for got in (seg, packed):
+        assert rel_err(got["o"], ref["o"]) <= TOL[dtype]
+        assert rel_err(got["S"], ref["S"]) <= TOL[dtype]
+        assert np.array_equal(got["conv_out"].float().cpu().numpy(), ref["conv_out"])
 
 
 def test_prefill_split_carry():
