@@ -342,17 +342,41 @@ constexpr int KS = D + 8;    // row stride (halfs) of the chunk's keys in LDS
 constexpr int TS = C + 8;    // row stride (halfs) of the transposed operands (16-byte aligned rows)
 constexpr int AS = C + 1;    // row stride (floats) of A and T
 
+// acc += X Y for 16 x 16 fp32 blocks in LDS (row strides AS) on v_mfma_f32_16x16x4_f32
+// (A: lane l holds A[l % 16][l / 16]; B: B[l / 16][l % 16]; D: rows 4 (l / 16) + e,
+// column l % 16); step q contracts k = 4q .. 4q + 3.
+__device__ __forceinline__ f32x4v mma16_f32_lds(const float* X, const float* Y, int lane, f32x4v acc) {
+    const int g = lane >> 4, r16 = lane & 15;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(X[r16 * AS + 4 * q + g], Y[(4 * q + g) * AS + r16], acc, 0, 0, 0);
+    return acc;
+}
+
+// acc += X M with X a 16 x 16 fp32 block in LDS and M in accumulator layout in
+// registers: step q pairs k slot l / 16 with row 4 (l / 16) + q, the row this lane
+// holds as element q, so M feeds the B operand without moving.
+__device__ __forceinline__ f32x4v mma16_f32_reg(const float* X, const f32x4v& m, int lane, f32x4v acc) {
+    const int g = lane >> 4, r16 = lane & 15;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(X[r16 * AS + 4 * g + q], m[q], acc, 0, 0, 0);
+    return acc;
+}
+
 template <typename Tin>
 __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a, Ws ws) {
-    // region: {Kc [C][KS] halfs, Am [C][AS] floats} during the Gram/solve phases,
-    //         {KbT [D][TS], VbT [D][TS] halfs} during the W/U phase
+    // region: {Kc [C][KS] halfs, Am [C][AS] floats} during the Gram phase,
+    //         {Tm [C][AS] floats over Kc, Am} during the solve,
+    //         {KbT [D][TS], VbT [D][TS] halfs} during the W/U phase.
+    // 37.7 KB of LDS in all (and 119 registers): four workgroups per CU.
     constexpr int REGION = 2 * D * TS * 2;  // 36864 B >= 64*136*2 + 64*65*4 = 34048 B
+    static_assert(C * AS * 4 <= C * KS * 2, "T must fit where the keys were");
     __shared__ __align__(16) unsigned char region[REGION];
-    __shared__ float Tm[C * AS];
-    __shared__ float Mt[3][16][17];
     __shared__ float s_g[C], s_b[C], s_gam[C], s_red[4];
     _Float16* Kc = reinterpret_cast<_Float16*>(region);
     float* Am = reinterpret_cast<float*>(region + C * KS * 2);
+    float* Tm = reinterpret_cast<float*>(region);   // written only after the Gram phase's last read of Kc
     _Float16* KbT = reinterpret_cast<_Float16*>(region);
     _Float16* VbT = reinterpret_cast<_Float16*>(region + D * TS * 2);
 
@@ -453,8 +477,10 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a, Ws ws) {
     __syncthreads();
 
     // 3. T = (I + A)^-1, fp32. Diagonal 16x16 blocks by forward substitution
-    //    (lane = (block, column)); off-diagonal blocks by
-    //    T_ij = -T_ii * sum_{k=j}^{i-1} A_ik T_kj, block row by block row.
+    //    (lane = (block, column)); off-diagonal blocks by merging inverses of
+    //    lower-triangular halves, [[P, 0], [Q, R]]^-1 = [[P^-1, 0], [-R^-1 Q P^-1, R^-1]]:
+    //    first the two 32 x 32 diagonal halves, then the 32 x 32 lower-left quarter,
+    //    every 16 x 16 block product on fp32 MFMA.
     if (wave == 0) {
         const int blk = lane >> 4, j = lane & 15;
         float xcol[16];
@@ -475,26 +501,44 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a, Ws ws) {
     }
     __syncthreads();
     {
-        const int r = tid >> 4, cc = tid & 15;
-        for (int bi = 1; bi < 4; ++bi) {
-            for (int bj = 0; bj < bi; ++bj) {
-                float m = 0.f;
-                for (int bk = bj; bk < bi; ++bk)
+        auto blk = [&](int i, int j) { return 16 * i * AS + 16 * j; };   // offset of block (i, j)
+        // merge 16 -> 32: T_{2w+1, 2w} = -T_{2w+1,2w+1} A_{2w+1,2w} T_{2w,2w}, w = 0, 1
+        if (wave < 2) {
+            const int i = 2 * wave + 1, j = 2 * wave;
+            f32x4v m = f32x4v{0, 0, 0, 0};
+            m = mma16_f32_lds(Am + blk(i, j), Tm + blk(j, j), lane, m);
+            f32x4v t = f32x4v{0, 0, 0, 0};
+            t = mma16_f32_reg(Tm + blk(i, i), m, lane, t);
 #pragma unroll
-                    for (int q = 0; q < 16; ++q)
-                        m = __fmaf_rn(Am[(16 * bi + r) * AS + 16 * bk + q], Tm[(16 * bk + q) * AS + 16 * bj + cc], m);
-                Mt[bj][r][cc] = m;
-            }
-            __syncthreads();
-            for (int bj = 0; bj < bi; ++bj) {
-                float v = 0.f;
-#pragma unroll
-                for (int q = 0; q < 16; ++q) v = __fmaf_rn(Tm[(16 * bi + r) * AS + 16 * bi + q], Mt[bj][q][cc], v);
-                Tm[(16 * bi + r) * AS + 16 * bj + cc] = -v;
-            }
-            __syncthreads();
+            for (int e = 0; e < 4; ++e) Tm[blk(i, j) + (4 * g + e) * AS + r16] = -t[e];
         }
+        __syncthreads();
+        // merge 32 -> 64: with N_mj = A_m0 T_0j + A_m1 T_1j (m = 2, 3),
+        // T_ij = -(T_i2 N_2j + T_i3 N_3j) for i = 2 + w / 2, j = w % 2 (T_01 = T_23 = 0)
+        {
+            const int i = 2 + (wave >> 1), j = wave & 1;
+            f32x4v n2 = f32x4v{0, 0, 0, 0}, n3 = f32x4v{0, 0, 0, 0};
+            n2 = mma16_f32_lds(Am + blk(2, 0), Tm + blk(0, j), lane, n2);
+            n2 = mma16_f32_lds(Am + blk(2, 1), Tm + blk(1, j), lane, n2);
+            n3 = mma16_f32_lds(Am + blk(3, 0), Tm + blk(0, j), lane, n3);
+            n3 = mma16_f32_lds(Am + blk(3, 1), Tm + blk(1, j), lane, n3);
+            f32x4v t = f32x4v{0, 0, 0, 0};
+            t = mma16_f32_reg(Tm + blk(i, 2), n2, lane, t);
+            t = mma16_f32_reg(Tm + blk(i, 3), n3, lane, t);
+            // the blocks written here (rows 2-3, columns 0-1) are read by no wave of this step
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Tm[blk(i, j) + (4 * g + e) * AS + r16] = -t[e];
+        }
+        __syncthreads();
     }
+
+    // T rows of this wave as the A operands of step 5, read before KbT overwrites T
+    f16x8 at[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) at[ks][e] = static_cast<_Float16>(Tm[(16 * wave + r16) * AS + 32 * ks + 8 * g + e]);
+    __syncthreads();
 
     // 4. operands of W and U, transposed (k = token): KbT[i][s] = beta_s exp(Gam_s) k_s[i],
     //    VbT[j][s] = beta_s v_s[j] 2^-eV
@@ -534,11 +578,6 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a, Ws ws) {
     __syncthreads();
 
     // 5. W = T KbT^T and U = T VbT^T on MFMA: wave w owns token rows 16w..16w+15
-    f16x8 at[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) at[ks][e] = static_cast<_Float16>(Tm[(16 * wave + r16) * AS + 32 * ks + 8 * g + e]);
     _Float16* Wout = ws.W + (static_cast<size_t>(id) * a.Hv + h) * C * D;
     f32x4v uacc[8];
 #pragma unroll
