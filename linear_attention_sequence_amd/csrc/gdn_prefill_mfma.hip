@@ -818,6 +818,12 @@ __global__ __launch_bounds__(NW * 64) void carry_kernel(PrefillArgs a, Ws ws) {
     const size_t row_tok = static_cast<size_t>(seg.row) * a.L + seg.start;
     // outputs: o (token stride Hv * D), or for XMAP the per-chunk blocks of Y
     const size_t ts = xm ? static_cast<size_t>(D) : static_cast<size_t>(a.Hv) * D;
+    if (xm) {   // U = 0: the U regions of both stages are zeroed once and never loaded
+        for (int i = tid; i < 64 * SG::UG; i += NW * 64) {
+            reinterpret_cast<uint4*>(g_stage + SG::U * 16)[i] = make_uint4(0, 0, 0, 0);
+            reinterpret_cast<uint4*>(g_stage + SG::BYTES + SG::U * 16)[i] = make_uint4(0, 0, 0, 0);
+        }
+    }
     if (xm)
         issue_stage<CPW, NW, ST_ALL & ~ST_U>(a, ws, base + cb, row_tok + static_cast<size_t>(cb) * C,
                                             min(C, seg.len - cb * C), h, hk, ucol0, 0, wave, lane);
@@ -882,8 +888,7 @@ __global__ __launch_bounds__(NW * 64) void carry_kernel(PrefillArgs a, Ws ws) {
                 for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        uh[mt][nt][e] = xm ? static_cast<_Float16>(0.f)
-                                           : Ul[(16 * mt + 4 * g + e) * 8 * SG::UG + lcol0 + 16 * nt + r16];
+                        uh[mt][nt][e] = Ul[(16 * mt + 4 * g + e) * 8 * SG::UG + lcol0 + 16 * nt + r16];
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
@@ -922,7 +927,7 @@ __global__ __launch_bounds__(NW * 64) void carry_kernel(PrefillArgs a, Ws ws) {
     #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int t = 16 * mt + 4 * g + e;
-                        const float u = xm ? 0.f : static_cast<float>(Ul[t * 8 * SG::UG + lcol0 + 16 * nt + r16]);
+                        const float u = static_cast<float>(Ul[t * 8 * SG::UG + lcol0 + 16 * nt + r16]);
                         const float d = (t < ntc) ? __fmaf_rn(u, uscale, -iS * acc[nt][e]) : 0.f;
                         dl[mt][nt][e] = d;
                         dmax = fmaxf(dmax, fabsf(d));
