@@ -364,6 +364,15 @@ __device__ __forceinline__ f32x4v mma16_f32_reg(const float* X, const f32x4v& m,
     return acc;
 }
 
+// Row placement of the chunk's LDS operands read as the A side of a transposed product:
+// row r (bits 4-5 block b5, bits 2-3 a, bit 2 h, bits 0-1 c: r = 32 b5 + 8 a + 4 h + c)
+// sits at 32 b5 + 16 h + 4 a + c, so 16-row tile n = 2 b5 + h of the permuted rows holds,
+// at its row 4 a + c, the row whose MFMA output element c of lane group a is. Each lane
+// group of the transposed product then holds 8 consecutive columns of one output row.
+__device__ __forceinline__ int perm_row(int r) {
+    return (r & ~31) | (((r >> 2) & 1) << 4) | (((r >> 3) & 3) << 2) | (r & 3);
+}
+
 template <typename Tin>
 __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a, Ws ws) {
     // region: {Kc [C][KS] halfs, Am [C][AS] floats} during the Gram phase,
@@ -405,7 +414,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a, Ws ws) {
 #pragma unroll
         for (int q = 0; q < C * (D / 8) / 256; ++q) {
             const int it = tid + 256 * q, r = it >> 4, j = it & 15;
-            *reinterpret_cast<uint4*>(Kc + r * KS + 8 * j) = r < nt ? v[q] : make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4*>(Kc + perm_row(r) * KS + 8 * j) = r < nt ? v[q] : make_uint4(0, 0, 0, 0);
         }
     }
     if (tid < C) {
@@ -441,37 +450,47 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a, Ws ws) {
             const int i = it >> 3, sg = it & 7;
             f16x8 v;
 #pragma unroll
-            for (int q = 0; q < 8; ++q) v[q] = Kc[(8 * sg + q) * KS + i];
+            for (int q = 0; q < 8; ++q) v[q] = Kc[perm_row(8 * sg + q) * KS + i];
             *reinterpret_cast<f16x8*>(kt + i * C + 8 * sg) = v;
         }
     }
     __syncthreads();
 
-    // 2. Gram matrices on MFMA: wave w owns rows 16w..16w+15
+    // 2. Gram matrices on MFMA, transposed (key rows as the A operand, in permuted order):
+    //    wave w owns token rows t = 16w..16w+15 (lane column r16); element e of tile
+    //    n = 2 b5 + hh is key s = 32 b5 + 8 g + 4 hh + e, so a lane holds P[t][32 b5 + 8 g ..]
     {
         f32x4v kk[4], qk[4];
 #pragma unroll
         for (int ntile = 0; ntile < 4; ++ntile) { kk[ntile] = f32x4v{0, 0, 0, 0}; qk[ntile] = kk[ntile]; }
+        const int prow = perm_row(16 * wave + r16);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            const f16x8 ak = *reinterpret_cast<const f16x8*>(Kc + (16 * wave + r16) * KS + 32 * ks + 8 * g);
+            const f16x8 ak = *reinterpret_cast<const f16x8*>(Kc + prow * KS + 32 * ks + 8 * g);
 #pragma unroll
             for (int ntile = 0; ntile < 4; ++ntile) {
                 const f16x8 bk = *reinterpret_cast<const f16x8*>(Kc + (16 * ntile + r16) * KS + 32 * ks + 8 * g);
-                kk[ntile] = mfma16x16x32(ak, bk, kk[ntile]);
-                qk[ntile] = mfma16x16x32(aq[ks], bk, qk[ntile]);
+                kk[ntile] = mfma16x16x32(bk, ak, kk[ntile]);
+                qk[ntile] = mfma16x16x32(bk, aq[ks], qk[ntile]);
             }
         }
         _Float16* P = ws.P + (static_cast<size_t>(id) * a.Hv + h) * C * C;
+        const int t = 16 * wave + r16;
+        const float gt = s_gam[t], bt = s_b[t];
 #pragma unroll
-        for (int ntile = 0; ntile < 4; ++ntile) {
+        for (int b5 = 0; b5 < 2; ++b5) {
+            f16x8 pv;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = 16 * wave + 4 * g + e, s = 16 * ntile + r16;
-                const float dec = (s <= t && t < nt) ? expf(s_gam[t] - s_gam[s]) : 0.f;
-                Am[t * AS + s] = (s < t) ? s_b[t] * dec * kk[ntile][e] : 0.f;
-                P[t * C + s] = static_cast<_Float16>(dec * qk[ntile][e]);
+            for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int s = 32 * b5 + 8 * g + 4 * hh + e;
+                    const float dec = (s <= t && t < nt) ? expf(gt - s_gam[s]) : 0.f;
+                    Am[t * AS + s] = (s < t) ? bt * dec * kk[2 * b5 + hh][e] : 0.f;
+                    pv[4 * hh + e] = static_cast<_Float16>(dec * qk[2 * b5 + hh][e]);
+                }
             }
+            *reinterpret_cast<f16x8*>(P + t * C + 32 * b5 + 8 * g) = pv;
         }
     }
     __syncthreads();
@@ -559,7 +578,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a, Ws ws) {
         vreg[q] = s < nt ? vl : z;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            KbT[(8 * j + e) * TS + s] = static_cast<_Float16>(fk * static_cast<float>(kv[e]));
+            KbT[perm_row(8 * j + e) * TS + s] = static_cast<_Float16>(fk * static_cast<float>(kv[e]));
             vmax = fmaxf(vmax, fabsf(s_b[s] * static_cast<float>(vreg[q][e])));
         }
     }
@@ -573,27 +592,39 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a, Ws ws) {
         const int j = wave + 4 * q;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-            VbT[(8 * j + e) * TS + s] = static_cast<_Float16>(s_b[s] * static_cast<float>(vreg[q][e]) * sV);
+            VbT[perm_row(8 * j + e) * TS + s] = static_cast<_Float16>(s_b[s] * static_cast<float>(vreg[q][e]) * sV);
     }
     __syncthreads();
 
-    // 5. W = T KbT^T and U = T VbT^T on MFMA: wave w owns token rows 16w..16w+15
+    // 5. W^T = KbT T^T and U^T = VbT T^T on MFMA (feature rows permuted as in step 2):
+    //    wave w owns token rows 16w..16w+15; element e of tile n = 2 b5 + hh is feature
+    //    32 b5 + 8 g + 4 hh + e, so a lane stores 8 consecutive features of its token
+    const int trow = 16 * wave + r16;
     _Float16* Wout = ws.W + (static_cast<size_t>(id) * a.Hv + h) * C * D;
     f32x4v uacc[8];
 #pragma unroll
-    for (int ntile = 0; ntile < 8; ++ntile) {
-        f32x4v wacc = f32x4v{0, 0, 0, 0};
-        uacc[ntile] = wacc;
+    for (int b5 = 0; b5 < 4; ++b5) {
+        f32x4v wacc[2];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const f16x8 bk = *reinterpret_cast<const f16x8*>(KbT + (16 * ntile + r16) * TS + 32 * ks + 8 * g);
-            const f16x8 bv = *reinterpret_cast<const f16x8*>(VbT + (16 * ntile + r16) * TS + 32 * ks + 8 * g);
-            wacc = mfma16x16x32(at[ks], bk, wacc);
-            uacc[ntile] = mfma16x16x32(at[ks], bv, uacc[ntile]);
+        for (int hh = 0; hh < 2; ++hh) {
+            const int ntile = 2 * b5 + hh;
+            wacc[hh] = f32x4v{0, 0, 0, 0};
+            uacc[ntile] = wacc[hh];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const f16x8 bk = *reinterpret_cast<const f16x8*>(KbT + (16 * ntile + r16) * TS + 32 * ks + 8 * g);
+                const f16x8 bv = *reinterpret_cast<const f16x8*>(VbT + (16 * ntile + r16) * TS + 32 * ks + 8 * g);
+                wacc[hh] = mfma16x16x32(bk, at[ks], wacc[hh]);
+                uacc[ntile] = mfma16x16x32(bv, at[ks], uacc[ntile]);
+            }
         }
+        f16x8 wv;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            Wout[(16 * wave + 4 * g + e) * D + 16 * ntile + r16] = static_cast<_Float16>(wacc[e]);
+        for (int e = 0; e < 4; ++e) {
+            wv[e] = static_cast<_Float16>(wacc[0][e]);
+            wv[4 + e] = static_cast<_Float16>(wacc[1][e]);
+        }
+        *reinterpret_cast<f16x8*>(Wout + trow * D + 32 * b5 + 8 * g) = wv;
     }
     float umax = 0.f;
 #pragma unroll
@@ -608,10 +639,15 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a, Ws ws) {
     const float sU = ldexpf(1.f, -eU);
     _Float16* Uout = ws.U + (static_cast<size_t>(id) * a.Hv + h) * C * D;
 #pragma unroll
-    for (int ntile = 0; ntile < 8; ++ntile)
+    for (int b5 = 0; b5 < 4; ++b5) {
+        f16x8 uv;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            Uout[(16 * wave + 4 * g + e) * D + 16 * ntile + r16] = static_cast<_Float16>(uacc[ntile][e] * sU);
+        for (int e = 0; e < 4; ++e) {
+            uv[e] = static_cast<_Float16>(uacc[2 * b5][e] * sU);
+            uv[4 + e] = static_cast<_Float16>(uacc[2 * b5 + 1][e] * sU);
+        }
+        *reinterpret_cast<f16x8*>(Uout + trow * D + 32 * b5 + 8 * g) = uv;
+    }
     float* cf = ws.coef + (static_cast<size_t>(id) * a.Hv + h) * COEF;
     if (tid < C) {
         const float glast = s_gam[nt - 1];
@@ -739,8 +775,8 @@ __device__ int sequence_of_rank(const PrefillArgs& a, int r) {
     return s_pick;
 }
 
-template <int NTW, int NW>
-__global__ __launch_bounds__(NW * 64) void carry_kernel(PrefillArgs a, Ws ws) {
+template <int NTW, int NW, bool LW>
+__global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws ws) {
     constexpr int CPW = NW * NTW * 16;
     // One wave per SIMD (NW <= 4) leaves registers to hold a whole phase's operands:
     // their LDS reads are then issued ahead of the phase's MFMAs under one wait (a
@@ -786,6 +822,9 @@ __global__ __launch_bounds__(NW * 64) void carry_kernel(PrefillArgs a, Ws ws) {
     if (a.cu != nullptr && a.N <= kSortMax) n = sequence_of_rank(a, n);
     const int f = a.Hv / a.Hk, hk = h / f;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // With LW an extra wave (wave NW) issues every stage load and waits for it, so the
+    // compute waves never stall on the memory pipeline's queue.
+    const bool loader = LW && wave == NW;
     const int g = lane >> 4, r16 = lane & 15;
     const int ucol0 = cs * CPW;                          // first column of this workgroup
     const int lcol0 = wave * 16 * NTW;                   // first column of this wave, inside the workgroup
@@ -818,23 +857,47 @@ __global__ __launch_bounds__(NW * 64) void carry_kernel(PrefillArgs a, Ws ws) {
     const size_t row_tok = static_cast<size_t>(seg.row) * a.L + seg.start;
     // outputs: o (token stride Hv * D), or for XMAP the per-chunk blocks of Y
     const size_t ts = xm ? static_cast<size_t>(D) : static_cast<size_t>(a.Hv) * D;
-    if (xm) {   // U = 0: the U regions of both stages are zeroed once and never loaded
+    if (xm && !loader) {   // U = 0: the U regions of both stages are zeroed once and never loaded
         for (int i = tid; i < 64 * SG::UG; i += NW * 64) {
             reinterpret_cast<uint4*>(g_stage + SG::U * 16)[i] = make_uint4(0, 0, 0, 0);
             reinterpret_cast<uint4*>(g_stage + SG::BYTES + SG::U * 16)[i] = make_uint4(0, 0, 0, 0);
         }
     }
-    if (xm)
-        issue_stage<CPW, NW, ST_ALL & ~ST_U>(a, ws, base + cb, row_tok + static_cast<size_t>(cb) * C,
-                                            min(C, seg.len - cb * C), h, hk, ucol0, 0, wave, lane);
-    else
-        issue_stage<CPW, NW, ST_ALL>(a, ws, base + cb, row_tok + static_cast<size_t>(cb) * C,
-                                     min(C, seg.len - cb * C), h, hk, ucol0, 0, wave, lane);
+    if (!LW || loader) {
+#pragma unroll
+        for (int w = LW ? 0 : wave; w < (LW ? NW : wave + 1); ++w) {
+            if (xm)
+                issue_stage<CPW, NW, ST_ALL & ~ST_U>(a, ws, base + cb, row_tok + static_cast<size_t>(cb) * C,
+                                                    min(C, seg.len - cb * C), h, hk, ucol0, 0, w, lane);
+            else
+                issue_stage<CPW, NW, ST_ALL>(a, ws, base + cb, row_tok + static_cast<size_t>(cb) * C,
+                                             min(C, seg.len - cb * C), h, hk, ucol0, 0, w, lane);
+        }
+    }
+    if (loader) {   // stage c + 1 is issued after the barrier that frees its buffer
+        for (int c = cb; c < ce; ++c) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (c + 1 < ce) {
+                const size_t tokn = row_tok + static_cast<size_t>(c + 1) * C;
+                const int ntn = min(C, seg.len - (c + 1) * C);
+                const int sbn = (c - cb + 1) & 1;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) {
+                    if (xm)
+                        issue_stage<CPW, NW, ST_ALL & ~ST_U>(a, ws, base + c + 1, tokn, ntn, h, hk, ucol0, sbn, w, lane);
+                    else
+                        issue_stage<CPW, NW, ST_ALL>(a, ws, base + c + 1, tokn, ntn, h, hk, ucol0, sbn, w, lane);
+                }
+            }
+        }
+        return;
+    }
     // The next chunk's stage is issued in three parts spread over this chunk's
     // phases (each part before the phase that would otherwise wait on the memory
     // pipeline), so that the vector-memory issue queue never backs up the MFMA work.
     for (int c = cb; c < ce; ++c) {
-        __builtin_amdgcn_s_waitcnt(0);   // this wave's share of the stage has landed
+        if constexpr (!LW) __builtin_amdgcn_s_waitcnt(0);   // this wave's share of the stage has landed
         __syncthreads();                 // ... and every wave's; the other stage is free
         const int id = base + c;
         const int ntc = min(C, seg.len - c * C);
@@ -842,7 +905,7 @@ __global__ __launch_bounds__(NW * 64) void carry_kernel(PrefillArgs a, Ws ws) {
         const bool more = c + 1 < ce;
         const int ntn = min(C, seg.len - (c + 1) * C);
         const int sb_ = (c - cb + 1) & 1;                // stage buffer of the next chunk
-        if (more) {
+        if (!LW && more) {
             if (xm)
                 issue_stage<CPW, NW, ST_W | ST_CF>(a, ws, id + 1, tok0 + C, ntn, h, hk, ucol0, sb_, wave, lane);
             else
@@ -950,7 +1013,7 @@ __global__ __launch_bounds__(NW * 64) void carry_kernel(PrefillArgs a, Ws ws) {
                     dp[nt][ks][e] = static_cast<_Float16>(v * cfr[t]);
                 }
 
-        if (more)
+        if (!LW && more)
             issue_stage<CPW, NW, ST_Q | ST_P>(a, ws, id + 1, tok0 + C, ntn, h, hk, ucol0, sb_, wave, lane);
 
         // O = diag(exp(Gam)) Q S + P Delta, stored as soon as it is formed. With four
@@ -966,33 +1029,40 @@ __global__ __launch_bounds__(NW * 64) void carry_kernel(PrefillArgs a, Ws ws) {
         float* ob = obase + col0 + r16 + 4 * g * ts;
         float* obuf = reinterpret_cast<float*>(g_stage + 2 * SG::BYTES + wave * 4096);
         const bool full = ntc == C;                            // uniform: every row stored
-        f16x8 aq[4][4], ap[4][2];   // read ahead of the MFMAs when BATCH, else inside the loop
+        // operands read ahead of the MFMAs when BATCH, OB row tiles at a time (one
+        // with a loader wave: 256 registers, and each tile's reads then overlap the
+        // previous tile's MFMAs: 237 -> 225 us at L = 4096), else inside the loop
+        constexpr int OB = LW ? 1 : 4;
+#pragma unroll
+        for (int m0 = 0; m0 < 4; m0 += OB) {
+        f16x8 aq[OB][4], ap[OB][2];
         if constexpr (BATCH) {
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
+            for (int mi = 0; mi < OB; ++mi) {
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) aq[mt][ks] = lds_a<16>(Ql, 16 * mt + r16, ks, g);
+                for (int ks = 0; ks < 4; ++ks) aq[mi][ks] = lds_a<16>(Ql, 16 * (m0 + mi) + r16, ks, g);
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) ap[mt][ks] = lds_a<8>(Pl, 16 * mt + r16, ks, g);
+                for (int ks = 0; ks < 2; ++ks) ap[mi][ks] = lds_a<8>(Pl, 16 * (m0 + mi) + r16, ks, g);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
+        for (int mi = 0; mi < OB; ++mi) {
+            const int mt = m0 + mi;
             f32x4v a1[NTW], a2[NTW];
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt) { a1[nt] = f32x4v{0, 0, 0, 0}; a2[nt] = a1[nt]; }
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                if constexpr (!BATCH) aq[mt][ks] = lds_a<16>(Ql, 16 * mt + r16, ks, g);
+                if constexpr (!BATCH) aq[mi][ks] = lds_a<16>(Ql, 16 * mt + r16, ks, g);
 #pragma unroll
-                for (int nt = 0; nt < NTW; ++nt) a1[nt] = mfma16x16x32(aq[mt][ks], sb[nt][ks], a1[nt]);
+                for (int nt = 0; nt < NTW; ++nt) a1[nt] = mfma16x16x32(aq[mi][ks], sb[nt][ks], a1[nt]);
             }
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                if constexpr (!BATCH) ap[mt][ks] = lds_a<8>(Pl, 16 * mt + r16, ks, g);
+                if constexpr (!BATCH) ap[mi][ks] = lds_a<8>(Pl, 16 * mt + r16, ks, g);
 #pragma unroll
-                for (int nt = 0; nt < NTW; ++nt) a2[nt] = mfma16x16x32(ap[mt][ks], db[nt][ks], a2[nt]);
+                for (int nt = 0; nt < NTW; ++nt) a2[nt] = mfma16x16x32(ap[mi][ks], db[nt][ks], a2[nt]);
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -1006,6 +1076,7 @@ __global__ __launch_bounds__(NW * 64) void carry_kernel(PrefillArgs a, Ws ws) {
                 }
             }
         }
+        }
         if constexpr (OT) {
             float* orow0 = obase + col0 + 4 * (lane & 3);
 #pragma unroll
@@ -1015,7 +1086,7 @@ __global__ __launch_bounds__(NW * 64) void carry_kernel(PrefillArgs a, Ws ws) {
                 if (full || t < ntc) *reinterpret_cast<float4*>(orow0 + t * ts) = v;
             }
         }
-        if (more)
+        if (!LW && more)
             issue_stage<CPW, NW, ST_KT>(a, ws, id + 1, tok0 + C, ntn, h, hk, ucol0, sb_, wave, lane);
 
         // S = exp(Gam_last) S + K^T diag(exp(Gam_last - Gam)) Delta; max|S| for the next chunk
@@ -1214,16 +1285,16 @@ static int device_cu_count() {
 }
 
 // The carry configurations: (tiles per wave, waves per workgroup).
-template <int NTW, int NW>
+template <int NTW, int NW, bool LW = false>
 static hipError_t launch_carry(void** args, long long heads, hipStream_t stream) {
     constexpr int CPW = NW * NTW * 16;
     constexpr size_t lds = 2 * pf2::Stage<CPW>::BYTES + (NTW == 1 && NW <= 4 ? NW * 4096 : 0);   // + output tiles
     static_assert(lds <= 160 * 1024, "LDS of one CU");
-    const void* k = reinterpret_cast<const void*>(&pf2::carry_kernel<NTW, NW>);
+    const void* k = reinterpret_cast<const void*>(&pf2::carry_kernel<NTW, NW, LW>);
     // dynamic LDS above 64 KB must be allowed per kernel before its first launch
     static const hipError_t allowed = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (allowed != hipSuccess) return allowed;
-    return hipLaunchKernel(k, dim3(static_cast<unsigned>(heads * (128 / CPW))), dim3(NW * 64), args, lds, stream);
+    return hipLaunchKernel(k, dim3(static_cast<unsigned>(heads * (128 / CPW))), dim3((NW + LW) * 64), args, lds, stream);
 }
 
 template <typename Tin>
@@ -1253,14 +1324,14 @@ static hipError_t launch_mfma_t(const PrefillArgs& a, int in_dtype, hipStream_t 
         const int cus = device_cu_count();
         const bool split = 2 * heads <= cus || (a.cu != nullptr && a.N <= pf2::kSortMax && heads <= cus);
         if (ws.seg) {   // two-segment carry: 3 kinds x 2 halves per head, then the corrections
-            e = launch_carry<1, 4>(args, 3 * heads, stream);
+            e = launch_carry<1, 4, true>(args, 3 * heads, stream);
             if (e != hipSuccess) return e;
             const int nch = (a.L + pf2::C - 1) / pf2::C;
             const int nob = (nch - nch / 2 + 3) / 4;
             e = hipLaunchKernel(reinterpret_cast<const void*>(&pf2::seg_fix_kernel),
                                 dim3(static_cast<unsigned>(heads * (nob + 2))), dim3(256), args, 0, stream);
         } else {
-            e = split ? launch_carry<1, 4>(args, heads, stream) : launch_carry<CARRY_NTW, CARRY_NW>(args, heads, stream);
+            e = split ? launch_carry<1, 4, true>(args, heads, stream) : launch_carry<CARRY_NTW, CARRY_NW>(args, heads, stream);
         }
         if (e != hipSuccess) return e;
     }
