@@ -46,14 +46,31 @@ constexpr int RAW = TT + 5;  // raw tile row stride (floats): TT + 3 used, odd s
 // 2C: exp(Gam_last); 2C + 1: 2^uexp, the scale of the stored U; padded to 40 granules
 constexpr int COEF = 160;
 
+// Contraction order of the carry's A operands. Its B operands are accumulator tiles
+// (a lane holds rows 4 g .. 4 g + 3 of every 16-row tile), so the eight k slots of
+// lane group g in step ks are the logical indices 32 ks + 4 g + (0..3) and
+// 32 ks + 16 + 4 g + (0..3). W and q_hat (contracted over the state's rows, i.e.
+// the key features), and K^T and P (contracted over tokens) are stored in that
+// order, so that a lane's eight halfs are one 16-byte read: logical index
+// k = 32 b + 16 h + 4 g + e sits at position kpos(k) = 32 b + 8 g + 4 h + e, and
+// position p holds kidx(p). k_hat is stored the same way (the Gram products only
+// need q_hat and k_hat to agree).
+__host__ __device__ __forceinline__ constexpr int kpos(int k) {
+    return (k & ~31) | (((k >> 2) & 3) << 3) | (((k >> 4) & 1) << 2) | (k & 3);
+}
+__host__ __device__ __forceinline__ constexpr int kidx(int p) {
+    return (p & ~31) | (((p >> 2) & 1) << 4) | (((p >> 3) & 3) << 2) | (p & 3);
+}
+static_assert(kidx(kpos(45)) == 45 && kpos(kidx(45)) == 45 && kpos(16) == 4 && kpos(4) == 8, "k order");
+
 struct Ws {
-    _Float16* qh;   // [Ttot, Hk, D] q_hat (normalised, scaled)
-    _Float16* kh;   // [Ttot, Hk, D] k_hat
+    _Float16* qh;   // [Ttot, Hk, D] q_hat (normalised, scaled), features in k order
+    _Float16* kh;   // [Ttot, Hk, D] k_hat, features in k order
     _Float16* vh;   // [Ttot, Hv, D] v
-    _Float16* W;    // [NC, Hv, C, D]
-    _Float16* U;    // [NC, Hv, C, D] scaled by 2^-uexp
-    _Float16* P;    // [NC, Hv, C, C]
-    _Float16* KT;   // [NC, Hk, D, C]  keys of the chunk, transposed
+    _Float16* W;    // [NC, Hv, C, D] features in k order
+    _Float16* U;    // [NC, Hv, D, C] transposed, scaled by 2^-uexp
+    _Float16* P;    // [NC, Hv, C, C] keys in k order
+    _Float16* KT;   // [NC, Hk, D, C] keys of the chunk, transposed, tokens in k order
     float* coef;    // [NC, Hv, COEF]: exp(Gam_t), exp(Gam_last - Gam_t), exp(Gam_last), 2^uexp
     // two-segment carry (see carry_kernel): per sequence the chunks split at cm = nch / 2
     _Float16* SmidT;  // [N, Hv, D, D] state after the first segment, transposed ([column][row]),
@@ -286,10 +303,12 @@ __global__ __launch_bounds__(256) void front_kernel(PrefillArgs a, Ws ws) {
         }
     }
     __syncthreads();
-#pragma unroll
-    for (int j = 0; j < TT / 2; ++j) buf[(th * (TT / 2) + j) * (D + 1) + c] = y[j];
-    __syncthreads();
     const bool is_q = u < a.Hk, is_k = !is_q && u < 2 * a.Hk;
+    // q and k channels are placed in k order here (the norms below do not depend on the order)
+    const int cpos = is_q || is_k ? kpos(c) : c;
+#pragma unroll
+    for (int j = 0; j < TT / 2; ++j) buf[(th * (TT / 2) + j) * (D + 1) + cpos] = y[j];
+    __syncthreads();
     // per-token sum of squares: thread (token tid % TT, channel part tid / TT)
     // reads its part column-wise (lanes run along tokens: conflict-free)
     constexpr int NPART = 256 / TT, PW = D / NPART;
@@ -364,17 +383,9 @@ __device__ __forceinline__ f32x4v mma16_f32_reg(const float* X, const f32x4v& m,
     return acc;
 }
 
-// Row placement of the chunk's LDS operands read as the A side of a transposed product:
-// row r (bits 4-5 block b5, bits 2-3 a, bit 2 h, bits 0-1 c: r = 32 b5 + 8 a + 4 h + c)
-// sits at 32 b5 + 16 h + 4 a + c, so 16-row tile n = 2 b5 + h of the permuted rows holds,
-// at its row 4 a + c, the row whose MFMA output element c of lane group a is. Each lane
-// group of the transposed product then holds 8 consecutive columns of one output row.
-__device__ __forceinline__ int perm_row(int r) {
-    return (r & ~31) | (((r >> 2) & 1) << 4) | (((r >> 3) & 3) << 2) | (r & 3);
-}
 
 template <typename Tin>
-__global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a, Ws ws) {
+__global__ __launch_bounds__(256, 4) void chunk_kernel(PrefillArgs a, Ws ws) {
     // region: {Kc [C][KS] halfs, Am [C][AS] floats} during the Gram phase,
     //         {Tm [C][AS] floats over Kc, Am} during the solve,
     //         {KbT [D][TS], VbT [D][TS] halfs} during the W/U phase.
@@ -414,7 +425,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a, Ws ws) {
 #pragma unroll
         for (int q = 0; q < C * (D / 8) / 256; ++q) {
             const int it = tid + 256 * q, r = it >> 4, j = it & 15;
-            *reinterpret_cast<uint4*>(Kc + perm_row(r) * KS + 8 * j) = r < nt ? v[q] : make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4*>(Kc + r * KS + 8 * j) = r < nt ? v[q] : make_uint4(0, 0, 0, 0);
         }
     }
     if (tid < C) {
@@ -444,26 +455,17 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a, Ws ws) {
         }
         s_gam[lane] = v;
     }
-    if ((h % f) == 0) {   // transposed keys for the carry: KT[i][s]
-        _Float16* kt = ws.KT + (static_cast<size_t>(id) * a.Hk + hk) * D * C;
-        for (int it = tid; it < D * (C / 8); it += 256) {
-            const int i = it >> 3, sg = it & 7;
-            f16x8 v;
-#pragma unroll
-            for (int q = 0; q < 8; ++q) v[q] = Kc[perm_row(8 * sg + q) * KS + i];
-            *reinterpret_cast<f16x8*>(kt + i * C + 8 * sg) = v;
-        }
-    }
     __syncthreads();
 
-    // 2. Gram matrices on MFMA, transposed (key rows as the A operand, in permuted order):
-    //    wave w owns token rows t = 16w..16w+15 (lane column r16); element e of tile
-    //    n = 2 b5 + hh is key s = 32 b5 + 8 g + 4 hh + e, so a lane holds P[t][32 b5 + 8 g ..]
+    // 2. Gram matrices on MFMA, transposed (key rows as the A operand): wave w owns token
+    //    rows t = 16w..16w+15 (lane column r16); element e of tile n = 2 b5 + hh is key
+    //    s = 32 b5 + 16 hh + 4 g + e, so the lane's eight keys of block b5 are positions
+    //    32 b5 + 8 g .. + 7 of P's row in k order: one 16-byte store
     {
         f32x4v kk[4], qk[4];
 #pragma unroll
         for (int ntile = 0; ntile < 4; ++ntile) { kk[ntile] = f32x4v{0, 0, 0, 0}; qk[ntile] = kk[ntile]; }
-        const int prow = perm_row(16 * wave + r16);
+        const int prow = 16 * wave + r16;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const f16x8 ak = *reinterpret_cast<const f16x8*>(Kc + prow * KS + 32 * ks + 8 * g);
@@ -484,13 +486,28 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a, Ws ws) {
             for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int s = 32 * b5 + 8 * g + 4 * hh + e;
+                    const int s = 32 * b5 + 16 * hh + 4 * g + e;
                     const float dec = (s <= t && t < nt) ? expf(gt - s_gam[s]) : 0.f;
                     Am[t * AS + s] = (s < t) ? bt * dec * kk[2 * b5 + hh][e] : 0.f;
                     pv[4 * hh + e] = static_cast<_Float16>(dec * qk[2 * b5 + hh][e]);
                 }
             }
             *reinterpret_cast<f16x8*>(P + t * C + 32 * b5 + 8 * g) = pv;
+        }
+    }
+    // keys of the chunk (still in LDS until T overwrites them) transposed for the carry
+    if ((h % f) == 0) {   // KT[i][s], tokens in k order
+        // thread: features 4 fa .. 4 fa + 3 (4 consecutive halfs of a key row, at
+        // kpos(4 fa)) of the 8 tokens at positions 8 sg .. 8 sg + 7
+        const int fa = tid >> 3, sg = tid & 7;
+        _Float16* kt = ws.KT + (static_cast<size_t>(id) * a.Hk + hk) * D * C;
+        f16x4 r[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) r[q] = *reinterpret_cast<const f16x4*>(Kc + kidx(8 * sg + q) * KS + kpos(4 * fa));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const f16x8 v = {r[0][e], r[1][e], r[2][e], r[3][e], r[4][e], r[5][e], r[6][e], r[7][e]};
+            *reinterpret_cast<f16x8*>(kt + (4 * fa + e) * C + 8 * sg) = v;
         }
     }
     __syncthreads();
@@ -578,7 +595,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a, Ws ws) {
         vreg[q] = s < nt ? vl : z;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            KbT[perm_row(8 * j + e) * TS + s] = static_cast<_Float16>(fk * static_cast<float>(kv[e]));
+            KbT[kidx(8 * j + e) * TS + s] = static_cast<_Float16>(fk * static_cast<float>(kv[e]));   // row: feature
             vmax = fmaxf(vmax, fabsf(s_b[s] * static_cast<float>(vreg[q][e])));
         }
     }
@@ -592,13 +609,14 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a, Ws ws) {
         const int j = wave + 4 * q;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-            VbT[perm_row(8 * j + e) * TS + s] = static_cast<_Float16>(s_b[s] * static_cast<float>(vreg[q][e]) * sV);
+            VbT[(8 * j + e) * TS + s] = static_cast<_Float16>(s_b[s] * static_cast<float>(vreg[q][e]) * sV);
     }
     __syncthreads();
 
-    // 5. W^T = KbT T^T and U^T = VbT T^T on MFMA (feature rows permuted as in step 2):
-    //    wave w owns token rows 16w..16w+15; element e of tile n = 2 b5 + hh is feature
-    //    32 b5 + 8 g + 4 hh + e, so a lane stores 8 consecutive features of its token
+    // 5. W^T = KbT T^T and U = T VbT^T on MFMA: wave w owns token rows 16w..16w+15.
+    //    In W^T element e of tile n = 2 b5 + hh is feature 32 b5 + 16 hh + 4 g + e, so a
+    //    lane holds positions 32 b5 + 8 g .. + 7 of its token's row in k order (one
+    //    16-byte store); U is stored transposed, 4 tokens of one feature per lane
     const int trow = 16 * wave + r16;
     _Float16* Wout = ws.W + (static_cast<size_t>(id) * a.Hv + h) * C * D;
     f32x4v uacc[8];
@@ -615,7 +633,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a, Ws ws) {
                 const f16x8 bk = *reinterpret_cast<const f16x8*>(KbT + (16 * ntile + r16) * TS + 32 * ks + 8 * g);
                 const f16x8 bv = *reinterpret_cast<const f16x8*>(VbT + (16 * ntile + r16) * TS + 32 * ks + 8 * g);
                 wacc[hh] = mfma16x16x32(bk, at[ks], wacc[hh]);
-                uacc[ntile] = mfma16x16x32(bv, at[ks], uacc[ntile]);
+                uacc[ntile] = mfma16x16x32(at[ks], bv, uacc[ntile]);   // U itself: rows 4 g + e, column r16
             }
         }
         f16x8 wv;
@@ -637,16 +655,23 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a, Ws ws) {
     __syncthreads();
     const int eU = pow2_exponent(fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3])));
     const float sU = ldexpf(1.f, -eU);
+    // U^T through LDS (the operand region is dead: every wave's MFMAs have consumed
+    // their reads before the barriers above), then stored in whole 128-byte rows
+    constexpr int UTS = C + 8;   // row stride (halfs) of U^T in LDS
+    static_assert(D * UTS * 2 <= REGION, "U^T fits the operand region");
+    _Float16* UT = reinterpret_cast<_Float16*>(region);
+#pragma unroll
+    for (int ntile = 0; ntile < 8; ++ntile) {   // feature 16 ntile + r16, tokens 16 w + 4 g ..
+        const f16x4 uv = {static_cast<_Float16>(uacc[ntile][0] * sU), static_cast<_Float16>(uacc[ntile][1] * sU),
+                          static_cast<_Float16>(uacc[ntile][2] * sU), static_cast<_Float16>(uacc[ntile][3] * sU)};
+        *reinterpret_cast<f16x4*>(UT + (16 * ntile + r16) * UTS + 16 * wave + 4 * g) = uv;
+    }
+    __syncthreads();
     _Float16* Uout = ws.U + (static_cast<size_t>(id) * a.Hv + h) * C * D;
 #pragma unroll
-    for (int b5 = 0; b5 < 4; ++b5) {
-        f16x8 uv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            uv[e] = static_cast<_Float16>(uacc[2 * b5][e] * sU);
-            uv[4 + e] = static_cast<_Float16>(uacc[2 * b5 + 1][e] * sU);
-        }
-        *reinterpret_cast<f16x8*>(Uout + trow * D + 32 * b5 + 8 * g) = uv;
+    for (int q = 0; q < D * C / 8 / 256; ++q) {
+        const int it = tid + 256 * q, row = it >> 3, j = it & 7;
+        *reinterpret_cast<uint4*>(Uout + row * C + 8 * j) = *reinterpret_cast<const uint4*>(UT + row * UTS + 8 * j);
     }
     float* cf = ws.coef + (static_cast<size_t>(id) * a.Hv + h) * COEF;
     if (tid < C) {
@@ -666,14 +691,14 @@ __global__ __launch_bounds__(256) void chunk_kernel(PrefillArgs a, Ws ws) {
 // 128 / CPW workgroups (more CUs when there are few sequences).
 //
 // One LDS stage holds, for one chunk and head, in 16-byte granules:
-//   W [64][16 granules]  Q [64][16]  KT [128][8]  P [64][8]  U [64][CPW/8] (this
-//   workgroup's columns)  coefficients [40]
-// Granule j of row r of W, Q, KT and P sits at position j ^ (r mod rowgranules) of its
-// row, which spreads the 16 rows one MFMA operand read touches over the banks.
+//   W [64][16 granules]  Q [64][16]  KT [128][8]  P [64][8]  U^T [CPW][8] (this
+//   workgroup's columns, tokens along the row)  coefficients [40]
+// Granule j of row r sits at position j ^ (r mod rowgranules) of its row, which
+// spreads the 16 rows one MFMA operand read touches over the banks.
 template <int CPW>
 struct Stage {
     static constexpr int W = 0, Q = 1024, KT = 2048, P = 3072, U = 3584;
-    static constexpr int UG = CPW / 8;                 // U granules per row
+    static constexpr int UG = CPW / 8;                 // U^T rows per 8 (the region is 64 x UG granules)
     static constexpr int CF = U + 64 * UG;
     static constexpr int END = CF + COEF / 4;
     static constexpr int INSTR = (END + 63) / 64;      // wave-wide 1 KB loads
@@ -681,18 +706,23 @@ struct Stage {
 };
 
 // Eight halfs of an A operand whose k slots (g, e) hold logical columns
-// 32ks + 4g + e (e < 4) and 32ks + 16 + 4g + (e - 4) (e >= 4), from a swizzled row.
+// 32ks + 4g + e (e < 4) and 32ks + 16 + 4g + (e - 4) (e >= 4): with the row stored in
+// k order these are granule 4 ks + g, one 16-byte read of a swizzled row.
 template <int RG>   // granules per row (16 or 8)
 __device__ __forceinline__ f16x8 lds_a(const _Float16* base, int row, int ks, int g) {
-    const int j1 = 4 * ks + (g >> 1), j2 = j1 + 2;
-    const int sw = row & (RG - 1);
-    const _Float16* r = base + row * RG * 8 + 4 * (g & 1);
-    const f16x4 lo = *reinterpret_cast<const f16x4*>(r + (j1 ^ sw) * 8);
-    const f16x4 hi = *reinterpret_cast<const f16x4*>(r + (j2 ^ sw) * 8);
-    return f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return *reinterpret_cast<const f16x8*>(base + row * RG * 8 + ((4 * ks + g) ^ (row & (RG - 1))) * 8);
 }
 
-extern __shared__ __align__(1024) unsigned char g_stage[];   // 2 stages (+ output tiles)
+// U^T in a stage: row = column of the workgroup (64 tokens, 8 granules, swizzled).
+// Tokens t .. t + 3 (t a multiple of 4) of one row, and one token.
+__device__ __forceinline__ f16x4 lds_u4(const _Float16* Ul, int row, int t) {
+    return *reinterpret_cast<const f16x4*>(Ul + row * 64 + (((t >> 3) ^ (row & 7)) << 3) + (t & 4));
+}
+__device__ __forceinline__ _Float16 lds_u1(const _Float16* Ul, int row, int t) {
+    return Ul[row * 64 + (((t >> 3) ^ (row & 7)) << 3) + (t & 7)];
+}
+
+extern __shared__ __align__(1024) unsigned char g_stage[];   // two stages
 
 // Issue the wave-wide 1 KB global->LDS loads of the regions of one stage that
 // PARTS selects (bits: W, Q, KT, P, U, coefficients). Every region starts on a
@@ -741,13 +771,11 @@ __device__ __forceinline__ void issue_stage(const PrefillArgs& a, const Ws& ws, 
 #pragma unroll
         for (int i = 0; i < 8 / NW; ++i) ld(src + i * 8 * NW * C, SG::P / 64 + wave + NW * i);
     }
-    // this workgroup's columns of U: UG granules per row, 64 / UG rows per instruction
+    // this workgroup's rows of U^T (its columns): 8 granules per row, like KT
     if constexpr ((PARTS & ST_U) != 0) {
-        constexpr int RPI = 64 / SG::UG;
-        const int t = RPI * wave + lane / SG::UG, j = lane % SG::UG;
-        const _Float16* src = ws.U + wbase + t * D + ucol0 + 8 * j;
+        const _Float16* src = ws.U + wbase + static_cast<size_t>(ucol0 + r8l) * C + 8 * j8;
 #pragma unroll
-        for (int i = 0; i < SG::UG / NW; ++i) ld(src + i * RPI * NW * D, SG::U / 64 + wave + NW * i);
+        for (int i = 0; i < CPW / 8 / NW; ++i) ld(src + i * 8 * NW * C, SG::U / 64 + wave + NW * i);
     }
     // coefficients (40 granules; lanes past the end land in padding)
     if constexpr ((PARTS & ST_CF) != 0) {
@@ -948,10 +976,11 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                for (int nt = 0; nt < NTW; ++nt)
+                for (int nt = 0; nt < NTW; ++nt) {
+                    const f16x4 u4 = lds_u4(Ul, lcol0 + 16 * nt + r16, 16 * mt + 4 * g);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        uh[mt][nt][e] = Ul[(16 * mt + 4 * g + e) * 8 * SG::UG + lcol0 + 16 * nt + r16];
+                    for (int e = 0; e < 4; ++e) uh[mt][nt][e] = u4[e];
+                }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
@@ -990,7 +1019,7 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
     #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int t = 16 * mt + 4 * g + e;
-                        const float u = static_cast<float>(Ul[t * 8 * SG::UG + lcol0 + 16 * nt + r16]);
+                        const float u = static_cast<float>(lds_u1(Ul, lcol0 + 16 * nt + r16, t));
                         const float d = (t < ntc) ? __fmaf_rn(u, uscale, -iS * acc[nt][e]) : 0.f;
                         dl[mt][nt][e] = d;
                         dmax = fmaxf(dmax, fabsf(d));
@@ -1016,18 +1045,16 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
         if (!LW && more)
             issue_stage<CPW, NW, ST_Q | ST_P>(a, ws, id + 1, tok0 + C, ntn, h, hk, ucol0, sb_, wave, lane);
 
-        // O = diag(exp(Gam)) Q S + P Delta, stored as soon as it is formed. With four
-        // waves of one tile each (LDS to spare past the two stages) a wave's 64 x 16
-        // tile is transposed through its own 4 KB of LDS and stored token-major, 16
-        // bytes per lane: 4 store instructions instead of 16 scattered dword stores
-        // (14.1k instead of 15.4k cycles per chunk). With eight waves there is no room
-        // and reusing the stage's dead W region needs a barrier, which cost more.
-        constexpr bool OT = NTW == 1 && NW <= 4;
+        // O = diag(exp(Gam)) Q S + P Delta, stored as soon as it is formed. With one
+        // tile per wave the products are formed transposed (S and Delta as the A
+        // operands, Q and P as the B operands: the same registers), so that a lane
+        // holds 4 consecutive columns of one token and stores them in one 16-byte
+        // store: 4 store instructions per tile instead of 16 scattered dword stores.
+        constexpr bool OT = NTW == 1;
         // this chunk's first output row: o, or for XMAP its block of Y
         float* obase = xm ? ws.Y + ((static_cast<size_t>(c - cm) * a.N + n) * a.Hv + h) * C * D
                           : a.o + (tok0 * a.Hv + h) * D;
         float* ob = obase + col0 + r16 + 4 * g * ts;
-        float* obuf = reinterpret_cast<float*>(g_stage + 2 * SG::BYTES + wave * 4096);
         const bool full = ntc == C;                            // uniform: every row stored
         // operands read ahead of the MFMAs when BATCH, OB row tiles at a time (one
         // with a loader wave: 256 registers, and each tile's reads then overlap the
@@ -1056,35 +1083,34 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
             for (int ks = 0; ks < 4; ++ks) {
                 if constexpr (!BATCH) aq[mi][ks] = lds_a<16>(Ql, 16 * mt + r16, ks, g);
 #pragma unroll
-                for (int nt = 0; nt < NTW; ++nt) a1[nt] = mfma16x16x32(aq[mi][ks], sb[nt][ks], a1[nt]);
+                for (int nt = 0; nt < NTW; ++nt)
+                    a1[nt] = OT ? mfma16x16x32(sb[nt][ks], aq[mi][ks], a1[nt]) : mfma16x16x32(aq[mi][ks], sb[nt][ks], a1[nt]);
             }
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 if constexpr (!BATCH) ap[mi][ks] = lds_a<8>(Pl, 16 * mt + r16, ks, g);
 #pragma unroll
-                for (int nt = 0; nt < NTW; ++nt) a2[nt] = mfma16x16x32(ap[mi][ks], db[nt][ks], a2[nt]);
+                for (int nt = 0; nt < NTW; ++nt)
+                    a2[nt] = OT ? mfma16x16x32(db[nt][ks], ap[mi][ks], a2[nt]) : mfma16x16x32(ap[mi][ks], db[nt][ks], a2[nt]);
             }
+            if constexpr (OT) {   // lane: token 16 mt + r16, columns col0 + 4 g .. + 3
+                const int t = 16 * mt + r16;
+                const float eg = cf[t] * iS;
+                const float4 v = make_float4(__fmaf_rn(eg, a1[0][0], iD * a2[0][0]), __fmaf_rn(eg, a1[0][1], iD * a2[0][1]),
+                                             __fmaf_rn(eg, a1[0][2], iD * a2[0][2]), __fmaf_rn(eg, a1[0][3], iD * a2[0][3]));
+                if (full || t < ntc) *reinterpret_cast<float4*>(obase + t * ts + col0 + 4 * g) = v;
+            } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float eg = cf[16 * mt + 4 * g + e] * iS;
-                if constexpr (OT) {
-                    obuf[(16 * mt + 4 * g + e) * 16 + r16] = __fmaf_rn(eg, a1[0][e], iD * a2[0][e]);
-                } else if (full || 16 * mt + 4 * g + e < ntc) {
-                    float* orow = ob + (16 * mt + e) * ts;
+                for (int e = 0; e < 4; ++e) {
+                    const float eg = cf[16 * mt + 4 * g + e] * iS;
+                    if (full || 16 * mt + 4 * g + e < ntc) {
+                        float* orow = ob + (16 * mt + e) * ts;
 #pragma unroll
-                    for (int nt = 0; nt < NTW; ++nt) orow[16 * nt] = __fmaf_rn(eg, a1[nt][e], iD * a2[nt][e]);
+                        for (int nt = 0; nt < NTW; ++nt) orow[16 * nt] = __fmaf_rn(eg, a1[nt][e], iD * a2[nt][e]);
+                    }
                 }
             }
         }
-        }
-        if constexpr (OT) {
-            float* orow0 = obase + col0 + 4 * (lane & 3);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 16 * i + (lane >> 2);
-                const float4 v = *reinterpret_cast<const float4*>(obuf + t * 16 + 4 * (lane & 3));
-                if (full || t < ntc) *reinterpret_cast<float4*>(orow0 + t * ts) = v;
-            }
         }
         if (!LW && more)
             issue_stage<CPW, NW, ST_KT>(a, ws, id + 1, tok0 + C, ntn, h, hk, ucol0, sb_, wave, lane);
@@ -1145,113 +1171,97 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
 }
 
 // Second-segment corrections of the two-segment carry on fp16 MFMA, with the
-// same power-of-two operand scaling as the carry: per head, ceil(n2 / 4)
-// workgroups add Y_c S_mid to the outputs of the second segment's n2 chunks (one
-// chunk of 64 rows per wave), two more write the final state M S_mid + R (16 rows
-// per wave). A rows (of Y or M, fp32) are scaled per 16-row tile, S_mid per
-// 16-column tile (stored that way by the first segment's workgroups); both scales
-// factor out of the tile's product, which is then added to acc (the local outputs,
-// or R) in fp32.
-template <int MT>
-__device__ __forceinline__ void fix_tiles(const float* A, int nrows, const _Float16* SmT, const int* sexp, int lane,
-                                          f32x4v (&acc)[MT][8]) {
+// same power-of-two operand scaling as the carry. Per (sequence, head): ceil(n2 /
+// FIX_CH) workgroups add Y_c S_mid to the outputs of FIX_CH chunks each, and one
+// more writes the final state M S_mid + R. A workgroup stages S_mid (fp16, stored
+// transposed and scaled per 16-column tile by the first segment's workgroups) in
+// LDS once; its waves take 16-row tiles of Y (or M) in turn. The products are
+// formed transposed (S_mid as the A operand), so a lane holds 4 consecutive
+// columns of one row: the accumulator start (the local outputs, or R), the result
+// and the stores are 16 bytes per lane. A rows (fp32) are scaled per 16-row tile;
+// both scales factor out of the tile's product, which is added in fp32.
+#ifndef FIX_CH_
+#define FIX_CH_ 2
+#endif
+constexpr int FIX_CH = FIX_CH_;           // chunks of outputs per workgroup
+constexpr int SMS = D + 8;                // row stride (halfs) of S_mid in LDS
+
+__device__ __forceinline__ void fix_tile(const float* A, int nrows, const _Float16* sm, const int* sexp,
+                                         const float* init, float* out, size_t stride, int lane) {
     const int g = lane >> 4, r16 = lane & 15;
-    f16x8 bop[8][4];
-    int eb[8];
+    const bool rv = r16 < nrows;          // rows past the end of a partial chunk were never written
+    const int rr = rv ? r16 : 0;
+    float4 av[8];
+    float amax = 0.f;
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-        eb[nt] = sexp[nt];
+    for (int q = 0; q < 8; ++q) {        // k = 32 (q / 2) + 8 g + 4 (q % 2) + 0..3
+        const float4 v = *reinterpret_cast<const float4*>(A + rr * D + 32 * (q >> 1) + 8 * g + 4 * (q & 1));
+        av[q] = rv ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(av[q].x), fabsf(av[q].y)), fmaxf(fabsf(av[q].z), fabsf(av[q].w))));
+    }
+    float4 iv[8];                         // accumulator start, token r16, columns 16 nt + 4 g ..
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            bop[nt][ks] = *reinterpret_cast<const f16x8*>(SmT + (16 * nt + r16) * D + 32 * ks + 8 * g);
+    for (int nt = 0; nt < 8; ++nt)
+        iv[nt] = rv ? *reinterpret_cast<const float4*>(init + rr * stride + 16 * nt + 4 * g) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const int ea = pow2_exponent(wave_max_nonneg(amax));
+    const float sa = ldexpf(1.f, -ea);
+    f16x8 bop[4];                         // the tile's rows as B operands (k = row of S_mid)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        const float4 lo = av[2 * ks], hi = av[2 * ks + 1];
+        bop[ks] = f16x8{static_cast<_Float16>(lo.x * sa), static_cast<_Float16>(lo.y * sa),
+                        static_cast<_Float16>(lo.z * sa), static_cast<_Float16>(lo.w * sa),
+                        static_cast<_Float16>(hi.x * sa), static_cast<_Float16>(hi.y * sa),
+                        static_cast<_Float16>(hi.z * sa), static_cast<_Float16>(hi.w * sa)};
     }
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        float4 av[8];
-        float amax = 0.f;
-        const bool rv = 16 * mt + r16 < nrows;   // rows past the end of a partial chunk were never written
-        const int rr = rv ? 16 * mt + r16 : 0;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {   // k = 32 (q / 2) + 8 g + 4 (q % 2) + 0..3
-            const float4 v = *reinterpret_cast<const float4*>(A + rr * D + 32 * (q >> 1) + 8 * g + 4 * (q & 1));
-            av[q] = rv ? v : make_float4(0.f, 0.f, 0.f, 0.f);
-            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(av[q].x), fabsf(av[q].y)), fmaxf(fabsf(av[q].z), fabsf(av[q].w))));
-        }
-        const int ea = pow2_exponent(wave_max_nonneg(amax));
-        const float sa = ldexpf(1.f, -ea);
-        f16x8 aop[4];
+    for (int nt = 0; nt < 8; ++nt) {
+        f32x4v prod = f32x4v{0, 0, 0, 0};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            const float4 lo = av[2 * ks], hi = av[2 * ks + 1];
-            aop[ks] = f16x8{static_cast<_Float16>(lo.x * sa), static_cast<_Float16>(lo.y * sa),
-                            static_cast<_Float16>(lo.z * sa), static_cast<_Float16>(lo.w * sa),
-                            static_cast<_Float16>(hi.x * sa), static_cast<_Float16>(hi.y * sa),
-                            static_cast<_Float16>(hi.z * sa), static_cast<_Float16>(hi.w * sa)};
+            const f16x8 aop = *reinterpret_cast<const f16x8*>(sm + (16 * nt + r16) * SMS + 32 * ks + 8 * g);
+            prod = mfma16x16x32(aop, bop[ks], prod);
         }
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-            f32x4v prod = f32x4v{0, 0, 0, 0};
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) prod = mfma16x16x32(aop[ks], bop[nt][ks], prod);
-            const float sc = ldexpf(1.f, ea + eb[nt]);   // may underflow to 0: the product is then negligible
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[mt][nt][e] = __fmaf_rn(prod[e], sc, acc[mt][nt][e]);
-        }
+        const float sc = ldexpf(1.f, ea + sexp[nt]);   // may underflow to 0: the product is then negligible
+        const float4 v = make_float4(__fmaf_rn(prod[0], sc, iv[nt].x), __fmaf_rn(prod[1], sc, iv[nt].y),
+                                     __fmaf_rn(prod[2], sc, iv[nt].z), __fmaf_rn(prod[3], sc, iv[nt].w));
+        if (rv) *reinterpret_cast<float4*>(out + rr * stride + 16 * nt + 4 * g) = v;
     }
 }
 
 __global__ __launch_bounds__(256) void seg_fix_kernel(PrefillArgs a, Ws ws) {
+    __shared__ __align__(16) _Float16 sm[D * SMS];
+    __shared__ int s_exp[D / 16];
     const int nch = (a.L + C - 1) / C, cm = nch / 2, n2 = nch - cm;
-    const int nob = (n2 + 3) / 4, per = nob + 2;
+    const int nob = (n2 + FIX_CH - 1) / FIX_CH, per = nob + 1;
     const int r = blockIdx.x % per, nhid = blockIdx.x / per;
     const int n = nhid / a.Hv, h = nhid % a.Hv;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, r16 = lane & 15;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const size_t tile = (static_cast<size_t>(n) * a.Hv + h) * D * D;
     const _Float16* SmT = ws.SmidT + tile;
-    const int* sexp = ws.Sexp + (static_cast<size_t>(n) * a.Hv + h) * (D / 16);
-    if (r < nob) {                                   // outputs of chunk cm + 4r + wave
-        const int k2 = 4 * r + wave;
-        if (k2 >= n2) return;                        // whole wave
-        const int c = cm + k2;
-        const int ntc = min(C, a.L - c * C);
-        float* ob = a.o + ((static_cast<size_t>(n) * a.L + static_cast<size_t>(c) * C) * a.Hv + h) * D;
+#pragma unroll
+    for (int q = 0; q < D * D / 8 / 256; ++q) {
+        const int it = tid + 256 * q, row = it >> 4, j = it & 15;
+        *reinterpret_cast<uint4*>(sm + row * SMS + 8 * j) = *reinterpret_cast<const uint4*>(SmT + row * D + 8 * j);
+    }
+    if (tid < D / 16) s_exp[tid] = ws.Sexp[(static_cast<size_t>(n) * a.Hv + h) * (D / 16) + tid];
+    __syncthreads();
+    if (r < nob) {                        // 16-row tiles of the outputs of chunks cm + FIX_CH r ..
         const size_t ts = static_cast<size_t>(a.Hv) * D;
-        // the local outputs start the accumulators; all loaded up front (rows past
-        // the end of a partial chunk read row 0 and are not stored back)
-        f32x4v acc[4][8];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = 16 * mt + 4 * g + e, tc = t < ntc ? t : 0;
-#pragma unroll
-                for (int nt = 0; nt < 8; ++nt) acc[mt][nt][e] = ob[tc * ts + 16 * nt + r16];
-            }
-        fix_tiles<4>(ws.Y + ((static_cast<size_t>(k2) * a.N + n) * a.Hv + h) * C * D, ntc, SmT, sexp, lane, acc);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = 16 * mt + 4 * g + e;
-                if (t < ntc) {
-#pragma unroll
-                    for (int nt = 0; nt < 8; ++nt) ob[t * ts + 16 * nt + r16] = acc[mt][nt][e];
-                }
-            }
-    } else {                                         // final state rows 64 (r - nob) + 16 wave ..
-        const int i0 = 64 * (r - nob) + 16 * wave;
-        const float* Rb = ws.R + tile;
-        float* Sb = a.S + tile;
-        f32x4v acc[1][8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-            for (int nt = 0; nt < 8; ++nt) acc[0][nt][e] = Rb[(i0 + 4 * g + e) * D + 16 * nt + r16];
-        fix_tiles<1>(ws.M + tile + static_cast<size_t>(i0) * D, 16, SmT, sexp, lane, acc);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-            for (int nt = 0; nt < 8; ++nt) Sb[(i0 + 4 * g + e) * D + 16 * nt + r16] = acc[0][nt][e];
+        for (int ti = wave; ti < 4 * FIX_CH; ti += 4) {
+            const int k2 = FIX_CH * r + ti / 4, mt = ti % 4;
+            if (k2 >= n2) break;
+            const int c = cm + k2;
+            const int nrows = min(C, a.L - c * C) - 16 * mt;
+            if (nrows <= 0) continue;
+            float* ob = a.o + ((static_cast<size_t>(n) * a.L + static_cast<size_t>(c) * C + 16 * mt) * a.Hv + h) * D;
+            fix_tile(ws.Y + ((static_cast<size_t>(k2) * a.N + n) * a.Hv + h) * C * D + 16 * mt * D, nrows, sm, s_exp,
+                     ob, ob, ts, lane);
+        }
+    } else {                              // final state, 16-row tiles
+        for (int mt = wave; mt < D / 16; mt += 4)
+            fix_tile(ws.M + tile + 16 * mt * D, 16, sm, s_exp, ws.R + tile + 16 * mt * D, a.S + tile + 16 * mt * D, D, lane);
     }
 }
 
@@ -1288,7 +1298,7 @@ static int device_cu_count() {
 template <int NTW, int NW, bool LW = false>
 static hipError_t launch_carry(void** args, long long heads, hipStream_t stream) {
     constexpr int CPW = NW * NTW * 16;
-    constexpr size_t lds = 2 * pf2::Stage<CPW>::BYTES + (NTW == 1 && NW <= 4 ? NW * 4096 : 0);   // + output tiles
+    constexpr size_t lds = 2 * pf2::Stage<CPW>::BYTES;
     static_assert(lds <= 160 * 1024, "LDS of one CU");
     const void* k = reinterpret_cast<const void*>(&pf2::carry_kernel<NTW, NW, LW>);
     // dynamic LDS above 64 KB must be allowed per kernel before its first launch
@@ -1327,9 +1337,9 @@ static hipError_t launch_mfma_t(const PrefillArgs& a, int in_dtype, hipStream_t 
             e = launch_carry<1, 4, true>(args, 3 * heads, stream);
             if (e != hipSuccess) return e;
             const int nch = (a.L + pf2::C - 1) / pf2::C;
-            const int nob = (nch - nch / 2 + 3) / 4;
+            const int nob = (nch - nch / 2 + pf2::FIX_CH - 1) / pf2::FIX_CH;
             e = hipLaunchKernel(reinterpret_cast<const void*>(&pf2::seg_fix_kernel),
-                                dim3(static_cast<unsigned>(heads * (nob + 2))), dim3(256), args, 0, stream);
+                                dim3(static_cast<unsigned>(heads * (nob + 1))), dim3(256), args, 0, stream);
         } else {
             e = split ? launch_carry<1, 4, true>(args, heads, stream) : launch_carry<CARRY_NTW, CARRY_NW>(args, heads, stream);
         }
