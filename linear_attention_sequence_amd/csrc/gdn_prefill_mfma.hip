@@ -400,12 +400,28 @@ __global__ __launch_bounds__(256, 4) void chunk_kernel(PrefillArgs a, Ws ws) {
     _Float16* KbT = reinterpret_cast<_Float16*>(region);
     _Float16* VbT = reinterpret_cast<_Float16*>(region + D * TS * 2);
 
-    const int h = blockIdx.x % a.Hv;
-    const int id = blockIdx.x / a.Hv;
+    // blockIdx -> (chunk, V head). The f V heads of a K head read the same keys and
+    // queries: they are dispatched 8 blockIdx apart, i.e. to one XCD, whose L2 then
+    // serves the second read; the tail that does not fill a group of 8 (chunk, K head)
+    // units is laid out unit-major.
+    const int f = a.Hv / a.Hk;
+    int u, hl;
+    {
+        const int units = ws.nc_max * a.Hk, grp = units / 8, full = 8 * f * grp;
+        const int b = blockIdx.x;
+        if (b < full) {
+            u = (b / (8 * f)) * 8 + b % 8;
+            hl = (b / 8) % f;
+        } else {
+            const int rem = b - full, tail = units - 8 * grp;
+            u = 8 * grp + rem % tail;
+            hl = rem / tail;
+        }
+    }
+    const int hk = u % a.Hk, id = u / a.Hk, h = hk * f + hl;
     int n, c;
     Seg seg;
     if (id >= ws.nc_max || !find_chunk(id, a, &n, &c, &seg)) return;
-    const int f = a.Hv / a.Hk, hk = h / f;
     const int nt = min(C, seg.len - c * C);
     const size_t tok0 = static_cast<size_t>(seg.row) * a.L + seg.start + static_cast<size_t>(c) * C;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -413,20 +429,18 @@ __global__ __launch_bounds__(256, 4) void chunk_kernel(PrefillArgs a, Ws ws) {
     const Tin* gate = static_cast<const Tin*>(a.gate);
     const Tin* beta = static_cast<const Tin*>(a.beta);
 
-    // 1. keys of the chunk (zero rows past the end), gate, beta
+    // 1. keys of the chunk (zero rows past the end), gate, beta. Lane = token, granules
+    //    wave + 4 q: the registers also serve step 4 (the keys are not read twice)
+    f16x8 kreg[4];
     {
-        uint4 v[C * (D / 8) / 256];
+        const int r = lane, rc = r < nt ? r : nt - 1;   // clamped row, masked below
 #pragma unroll
-        for (int q = 0; q < C * (D / 8) / 256; ++q) {
-            const int it = tid + 256 * q, r = it >> 4, j = it & 15;
-            const int rc = r < nt ? r : nt - 1;   // clamped row, masked below
-            v[q] = *reinterpret_cast<const uint4*>(ws.kh + ((tok0 + rc) * a.Hk + hk) * D + 8 * j);
+        for (int q = 0; q < 4; ++q) {
+            const f16x8 v = *reinterpret_cast<const f16x8*>(ws.kh + ((tok0 + rc) * a.Hk + hk) * D + 8 * (wave + 4 * q));
+            kreg[q] = r < nt ? v : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
         }
 #pragma unroll
-        for (int q = 0; q < C * (D / 8) / 256; ++q) {
-            const int it = tid + 256 * q, r = it >> 4, j = it & 15;
-            *reinterpret_cast<uint4*>(Kc + r * KS + 8 * j) = r < nt ? v[q] : make_uint4(0, 0, 0, 0);
-        }
+        for (int q = 0; q < 4; ++q) *reinterpret_cast<f16x8*>(Kc + r * KS + 8 * (wave + 4 * q)) = kreg[q];
     }
     if (tid < C) {
         float gv = 0.f, bv = 0.f;
@@ -512,6 +526,17 @@ __global__ __launch_bounds__(256, 4) void chunk_kernel(PrefillArgs a, Ws ws) {
     }
     __syncthreads();
 
+    // values of step 4, loaded now so that the solve hides their latency
+    f16x8 vreg[4];
+    {
+        const int sc = lane < nt ? lane : nt - 1;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f16x8 vl = *reinterpret_cast<const f16x8*>(ws.vh + ((tok0 + sc) * a.Hv + h) * D + 8 * (wave + 4 * q));
+            vreg[q] = lane < nt ? vl : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        }
+    }
+
     // 3. T = (I + A)^-1, fp32. Diagonal 16x16 blocks by forward substitution
     //    (lane = (block, column)); off-diagonal blocks by merging inverses of
     //    lower-triangular halves, [[P, 0], [Q, R]]^-1 = [[P^-1, 0], [-R^-1 Q P^-1, R^-1]]:
@@ -581,18 +606,12 @@ __global__ __launch_bounds__(256, 4) void chunk_kernel(PrefillArgs a, Ws ws) {
     // lanes run along tokens, so the transposed LDS writes of a wave hit
     // consecutive halfs (no bank conflicts); item (s, j) = granule j of token s
     float vmax = 0.f;
-    f16x8 vreg[4];
     const int s = lane;
     const float fk = s_b[s] * expf(s_gam[s]);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int j = wave + 4 * q;
-        const int sc = s < nt ? s : nt - 1;
-        const f16x8 z = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
-        const f16x8 kl = *reinterpret_cast<const f16x8*>(ws.kh + ((tok0 + sc) * a.Hk + hk) * D + 8 * j);
-        const f16x8 vl = *reinterpret_cast<const f16x8*>(ws.vh + ((tok0 + sc) * a.Hv + h) * D + 8 * j);
-        const f16x8 kv = s < nt ? kl : z;
-        vreg[q] = s < nt ? vl : z;
+        const f16x8 kv = kreg[q];   // zero past the end, as vreg
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             KbT[kidx(8 * j + e) * TS + s] = static_cast<_Float16>(fk * static_cast<float>(kv[e]));   // row: feature
