@@ -332,11 +332,24 @@ __global__ __launch_bounds__(256) void commit_kernel(CommitArgs a) {
     const int h = bh - b * a.Hv;
     int acc = a.accept[b];
     acc = acc < 0 ? 0 : (acc > a.T - 1 ? a.T - 1 : acc);
-    if (a.S_out != nullptr) {
-        const float4* src = reinterpret_cast<const float4*>(
+    if (a.S_out != nullptr) {   // every load in flight before the (non-temporal) stores
+        const f32x4* src = reinterpret_cast<const f32x4*>(
             a.S_snap + ((static_cast<size_t>(b) * a.T + acc) * a.Hv + h) * DK * DV);
-        float4* dst = reinterpret_cast<float4*>(a.S_out + static_cast<size_t>(bh) * DK * DV);
-        for (int e = threadIdx.x; e < DK * DV / 4; e += 256) dst[e] = src[e];
+        f32x4* dst = reinterpret_cast<f32x4*>(a.S_out + static_cast<size_t>(bh) * DK * DV);
+        constexpr int NV = DK * DV / 4;
+        constexpr int PER = NV >= 256 ? NV / 256 : 1;
+        static_assert(NV < 256 || NV % 256 == 0, "tile must split evenly over the workgroup");
+        f32x4 r[PER];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = threadIdx.x + 256 * i;
+            if (e < NV) r[i] = src[e];
+        }
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = threadIdx.x + 256 * i;
+            if (e < NV) __builtin_nontemporal_store(r[i], dst + e);
+        }
     }
 
     const Tin* x = static_cast<const Tin*>(a.qkv);
