@@ -1190,44 +1190,51 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
 }
 
 // Second-segment corrections of the two-segment carry on fp16 MFMA, with the
-// same power-of-two operand scaling as the carry. Per (sequence, head): ceil(n2 /
-// FIX_CH) workgroups add Y_c S_mid to the outputs of FIX_CH chunks each, and one
-// more writes the final state M S_mid + R. A workgroup stages S_mid (fp16, stored
-// transposed and scaled per 16-column tile by the first segment's workgroups) in
-// LDS once; its waves take 16-row tiles of Y (or M) in turn. The products are
+// same power-of-two operand scaling as the carry. Per (sequence, head): n2
+// workgroups add Y_c S_mid to the outputs of one chunk each (a wave per 16-row
+// tile), and two more write the final state M S_mid + R. A wave issues its tile's
+// loads (rows of Y or M, fp32, and the accumulator start: the local outputs or R)
+// first, then the workgroup stages S_mid (fp16, stored transposed and scaled per
+// 16-column tile by the first segment's workgroups) in LDS. The products are
 // formed transposed (S_mid as the A operand), so a lane holds 4 consecutive
-// columns of one row: the accumulator start (the local outputs, or R), the result
-// and the stores are 16 bytes per lane. A rows (fp32) are scaled per 16-row tile;
-// both scales factor out of the tile's product, which is added in fp32.
-#ifndef FIX_CH_
-#define FIX_CH_ 2
-#endif
-constexpr int FIX_CH = FIX_CH_;           // chunks of outputs per workgroup
+// columns of one row: the accumulator start, the result and the stores are 16
+// bytes per lane. A rows are scaled per 16-row tile; both scales factor out of the
+// tile's product, which is added in fp32.
 constexpr int SMS = D + 8;                // row stride (halfs) of S_mid in LDS
 
-__device__ __forceinline__ void fix_tile(const float* A, int nrows, const _Float16* sm, const int* sexp,
-                                         const float* init, float* out, size_t stride, int lane) {
+struct FixTile {
+    float4 av[8];                         // the tile's row r16: k = 32 (q / 2) + 8 g + 4 (q % 2) + 0..3
+    float4 iv[8];                         // accumulator start, row r16, columns 16 nt + 4 g ..
+};
+
+__device__ __forceinline__ void fix_load(FixTile& ft, const float* A, int nrows, const float* init, size_t stride, int lane) {
     const int g = lane >> 4, r16 = lane & 15;
     const bool rv = r16 < nrows;          // rows past the end of a partial chunk were never written
     const int rr = rv ? r16 : 0;
-    float4 av[8];
-    float amax = 0.f;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {        // k = 32 (q / 2) + 8 g + 4 (q % 2) + 0..3
+    for (int q = 0; q < 8; ++q) {
         const float4 v = *reinterpret_cast<const float4*>(A + rr * D + 32 * (q >> 1) + 8 * g + 4 * (q & 1));
-        av[q] = rv ? v : make_float4(0.f, 0.f, 0.f, 0.f);
-        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(av[q].x), fabsf(av[q].y)), fmaxf(fabsf(av[q].z), fabsf(av[q].w))));
+        ft.av[q] = rv ? v : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    float4 iv[8];                         // accumulator start, token r16, columns 16 nt + 4 g ..
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt)
-        iv[nt] = rv ? *reinterpret_cast<const float4*>(init + rr * stride + 16 * nt + 4 * g) : make_float4(0.f, 0.f, 0.f, 0.f);
+        ft.iv[nt] = *reinterpret_cast<const float4*>(init + rr * stride + 16 * nt + 4 * g);
+}
+
+__device__ __forceinline__ void fix_compute(const FixTile& ft, int nrows, const _Float16* sm, const int* sexp, float* out,
+                                            size_t stride, int lane) {
+    const int g = lane >> 4, r16 = lane & 15;
+    const bool rv = r16 < nrows;
+    float amax = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(ft.av[q].x), fabsf(ft.av[q].y)), fmaxf(fabsf(ft.av[q].z), fabsf(ft.av[q].w))));
     const int ea = pow2_exponent(wave_max_nonneg(amax));
     const float sa = ldexpf(1.f, -ea);
     f16x8 bop[4];                         // the tile's rows as B operands (k = row of S_mid)
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-        const float4 lo = av[2 * ks], hi = av[2 * ks + 1];
+        const float4 lo = ft.av[2 * ks], hi = ft.av[2 * ks + 1];
         bop[ks] = f16x8{static_cast<_Float16>(lo.x * sa), static_cast<_Float16>(lo.y * sa),
                         static_cast<_Float16>(lo.z * sa), static_cast<_Float16>(lo.w * sa),
                         static_cast<_Float16>(hi.x * sa), static_cast<_Float16>(hi.y * sa),
@@ -1242,9 +1249,9 @@ __device__ __forceinline__ void fix_tile(const float* A, int nrows, const _Float
             prod = mfma16x16x32(aop, bop[ks], prod);
         }
         const float sc = ldexpf(1.f, ea + sexp[nt]);   // may underflow to 0: the product is then negligible
-        const float4 v = make_float4(__fmaf_rn(prod[0], sc, iv[nt].x), __fmaf_rn(prod[1], sc, iv[nt].y),
-                                     __fmaf_rn(prod[2], sc, iv[nt].z), __fmaf_rn(prod[3], sc, iv[nt].w));
-        if (rv) *reinterpret_cast<float4*>(out + rr * stride + 16 * nt + 4 * g) = v;
+        const float4 v = make_float4(__fmaf_rn(prod[0], sc, ft.iv[nt].x), __fmaf_rn(prod[1], sc, ft.iv[nt].y),
+                                     __fmaf_rn(prod[2], sc, ft.iv[nt].z), __fmaf_rn(prod[3], sc, ft.iv[nt].w));
+        if (rv) *reinterpret_cast<float4*>(out + r16 * stride + 16 * nt + 4 * g) = v;
     }
 }
 
@@ -1252,12 +1259,24 @@ __global__ __launch_bounds__(256) void seg_fix_kernel(PrefillArgs a, Ws ws) {
     __shared__ __align__(16) _Float16 sm[D * SMS];
     __shared__ int s_exp[D / 16];
     const int nch = (a.L + C - 1) / C, cm = nch / 2, n2 = nch - cm;
-    const int nob = (n2 + FIX_CH - 1) / FIX_CH, per = nob + 1;
+    const int per = n2 + 2;
     const int r = blockIdx.x % per, nhid = blockIdx.x / per;
     const int n = nhid / a.Hv, h = nhid % a.Hv;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const size_t tile = (static_cast<size_t>(n) * a.Hv + h) * D * D;
+    // this wave's tile: rows 16 wave.. of chunk cm + r's outputs, or of the final state
+    const bool outs = r < n2;
+    const int c = cm + r;
+    const int nrows = outs ? min(C, a.L - c * C) - 16 * wave : 16;
+    float* ob = outs ? a.o + ((static_cast<size_t>(n) * a.L + static_cast<size_t>(c) * C + 16 * wave) * a.Hv + h) * D
+                     : a.S + tile + static_cast<size_t>(64 * (r - n2) + 16 * wave) * D;
+    const float* Ab = outs ? ws.Y + ((static_cast<size_t>(r) * a.N + n) * a.Hv + h) * C * D + 16 * wave * D
+                           : ws.M + tile + static_cast<size_t>(64 * (r - n2) + 16 * wave) * D;
+    const float* ib = outs ? ob : ws.R + tile + static_cast<size_t>(64 * (r - n2) + 16 * wave) * D;
+    const size_t stride = outs ? static_cast<size_t>(a.Hv) * D : static_cast<size_t>(D);
+    FixTile ft;
+    if (nrows > 0) fix_load(ft, Ab, nrows, ib, stride, lane);
     const _Float16* SmT = ws.SmidT + tile;
 #pragma unroll
     for (int q = 0; q < D * D / 8 / 256; ++q) {
@@ -1266,22 +1285,7 @@ __global__ __launch_bounds__(256) void seg_fix_kernel(PrefillArgs a, Ws ws) {
     }
     if (tid < D / 16) s_exp[tid] = ws.Sexp[(static_cast<size_t>(n) * a.Hv + h) * (D / 16) + tid];
     __syncthreads();
-    if (r < nob) {                        // 16-row tiles of the outputs of chunks cm + FIX_CH r ..
-        const size_t ts = static_cast<size_t>(a.Hv) * D;
-        for (int ti = wave; ti < 4 * FIX_CH; ti += 4) {
-            const int k2 = FIX_CH * r + ti / 4, mt = ti % 4;
-            if (k2 >= n2) break;
-            const int c = cm + k2;
-            const int nrows = min(C, a.L - c * C) - 16 * mt;
-            if (nrows <= 0) continue;
-            float* ob = a.o + ((static_cast<size_t>(n) * a.L + static_cast<size_t>(c) * C + 16 * mt) * a.Hv + h) * D;
-            fix_tile(ws.Y + ((static_cast<size_t>(k2) * a.N + n) * a.Hv + h) * C * D + 16 * mt * D, nrows, sm, s_exp,
-                     ob, ob, ts, lane);
-        }
-    } else {                              // final state, 16-row tiles
-        for (int mt = wave; mt < D / 16; mt += 4)
-            fix_tile(ws.M + tile + 16 * mt * D, 16, sm, s_exp, ws.R + tile + 16 * mt * D, a.S + tile + 16 * mt * D, D, lane);
-    }
+    if (nrows > 0) fix_compute(ft, nrows, sm, s_exp, ob, stride, lane);
 }
 
 }  // namespace pf2
@@ -1356,9 +1360,9 @@ static hipError_t launch_mfma_t(const PrefillArgs& a, int in_dtype, hipStream_t 
             e = launch_carry<1, 4, true>(args, 3 * heads, stream);
             if (e != hipSuccess) return e;
             const int nch = (a.L + pf2::C - 1) / pf2::C;
-            const int nob = (nch - nch / 2 + pf2::FIX_CH - 1) / pf2::FIX_CH;
+            const int n2 = nch - nch / 2;   // a workgroup per second-segment chunk, two for the state
             e = hipLaunchKernel(reinterpret_cast<const void*>(&pf2::seg_fix_kernel),
-                                dim3(static_cast<unsigned>(heads * (nob + 1))), dim3(256), args, 0, stream);
+                                dim3(static_cast<unsigned>(heads * (n2 + 2))), dim3(256), args, 0, stream);
         } else {
             e = split ? launch_carry<1, 4, true>(args, heads, stream) : launch_carry<CARRY_NTW, CARRY_NW>(args, heads, stream);
         }
