@@ -168,7 +168,7 @@ __device__ __forceinline__ int owner_of(int p, int row, const PrefillArgs& a, in
 // SiLU with the hardware exp2 and reciprocal (about 1e-6 relative): the result is
 // rounded to fp16 (2^-11) right after, so the accurate library forms would buy nothing.
 __device__ __forceinline__ float fast_silu(float x) {
-    return x * __frcp_rn(1.0f + __expf(-x));
+    return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));   // v_exp_f32, v_rcp_f32
 }
 
 // ---- steps 1-4 ------------------------------------------------------------------
