@@ -165,6 +165,14 @@ __device__ __forceinline__ int owner_of(int p, int row, const PrefillArgs& a, in
     return n;
 }
 
+// An input value back in its storage type, from fp32 holding a value that was
+// widened from that type (so the bf16 case, dropping the low 16 zero bits, is exact).
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
+    return bf16_t{static_cast<uint16_t>(__float_as_uint(x) >> 16)};
+}
+
 // SiLU with the hardware exp2 and reciprocal (about 1e-6 relative): the result is
 // rounded to fp16 (2^-11) right after, so the accurate library forms would buy nothing.
 __device__ __forceinline__ float fast_silu(float x) {
@@ -176,6 +184,7 @@ template <typename Tin>
 __global__ __launch_bounds__(256) void front_kernel(PrefillArgs a, Ws ws) {
     __shared__ float buf[D * RAW];           // raw[c][m] (window of TT + 3 tokens), then ys[t][c] (stride 129)
     __shared__ int s_n[TT], s_start[TT];
+    __shared__ unsigned s_endmask;           // bit t: token t is the last of its sequence
     static_assert(TT * (D + 1) <= D * RAW, "the transposed outputs reuse the raw tile");
     const int units = 2 * a.Hk + a.Hv;
     const int tiles = (a.L + TT - 1) / TT;
@@ -229,7 +238,7 @@ __global__ __launch_bounds__(256) void front_kernel(PrefillArgs a, Ws ws) {
     }
     if (tid < TT) {
         const int p = p0 + tid;
-        int start = 0, n = -1;
+        int start = 0, end = 0, n = -1;
         if (p < a.L) {
             if (cu_lds) {
                 const int* scu = reinterpret_cast<const int*>(buf);
@@ -240,14 +249,22 @@ __global__ __launch_bounds__(256) void front_kernel(PrefillArgs a, Ws ws) {
                 }
                 if (n >= 0) {
                     start = scu[n];
-                    if (p >= scu[n + 1]) n = -1;            // past the end (or an empty pair)
+                    end = scu[n + 1];
+                    if (p >= end) n = -1;                   // past the end (or an empty pair)
                 }
             } else {
                 n = owner_of(p, row, a, &start);
+                if (n >= 0) {
+                    const Seg sg = segment_of(n, a.L, a.cu);
+                    end = sg.start + sg.len;
+                }
             }
         }
         s_n[tid] = n;
         s_start[tid] = start;
+        static_assert(TT <= 32 && TT <= kWave, "the end mask is one wave's ballot");
+        const unsigned long long m = __ballot(n >= 0 && p + 1 == end);
+        if (tid == 0) s_endmask = static_cast<unsigned>(m);
     }
     if (cu_lds) __syncthreads();                            // the table is read before buf is reused
 #pragma unroll
@@ -300,6 +317,33 @@ __global__ __launch_bounds__(256) void front_kernel(PrefillArgs a, Ws ws) {
             acc = __fmaf_rn(wv[2], win[2], acc);
             acc = __fmaf_rn(wv[3], win[3], acc);
             y[j] = fast_silu(acc);
+        }
+    }
+    // step 2's conv-state update: for every sequence whose last token lies in this
+    // half of the tile, its K-1 most recent raw inputs (in the tile or its 3-token
+    // halo, exact in fp32), or the incoming state for a sequence shorter than K-1
+    {
+        Tin* co = static_cast<Tin*>(a.conv_out);
+        for (unsigned em = (s_endmask >> t0) & ((1u << (TT / 2)) - 1); em != 0; em &= em - 1) {   // usually none
+            const int t = t0 + __builtin_ctz(em);
+            const int n = s_n[t];
+            const int len = p0 + t + 1 - s_start[t];
+            const size_t base = (static_cast<size_t>(n) * a.D + ch0 + c) * (kConvK - 1);
+#pragma unroll
+            for (int j = 0; j < kConvK - 1; ++j) {
+                const int m = len + j;                         // position in concat(state, x[seq])
+                co[base + j] = m < kConvK - 1 ? cin[base + m] : from_f32<Tin>(buf[c * RAW + t + 1 + j]);
+            }
+        }
+        if (a.cu != nullptr && tile == 0 && row == 0) {        // empty sequences keep their state
+            for (int n = 0; n < a.N; ++n) {
+                if (segment_of(n, a.L, a.cu).len != 0) continue;
+                const size_t base = (static_cast<size_t>(n) * a.D + ch0 + c) * (kConvK - 1);
+                if (th == 0) {
+#pragma unroll
+                    for (int j = 0; j < kConvK - 1; ++j) co[base + j] = cin[base + j];
+                }
+            }
         }
     }
     __syncthreads();
@@ -1371,6 +1415,7 @@ static hipError_t launch_mfma_t(const PrefillArgs& a, int in_dtype, hipStream_t 
         }
         if (e != hipSuccess) return e;
     }
+    if (fblocks > 0) return hipSuccess;   // the front kernel wrote the conv state
     ConvArgs ca{a.B, a.L, a.D, a.N, a.qkv, a.w, a.conv_in, a.conv_out, nullptr, a.cu};
     return launch_conv_state(ca, in_dtype, stream);
 }
