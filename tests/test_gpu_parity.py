@@ -101,6 +101,38 @@ def test_prefill_ragged_small():
     assert np.array_equal(got["conv_out"].float().cpu().numpy(), ref["conv_out"])
 
 
+@pytest.mark.parametrize("B,L", [(2, 150), (5, 130)], ids=["split_heads_B2", "whole_heads_B5"])
+def test_prefill_carry_launch_paths(B, L):
+    """The full 16/32-head, d = 128 shape unpacked: B = 2 (64 heads) runs the carry with two
+    workgroups per head and a loader wave; B = 5 (160 heads, more than half the CUs' worth of
+    half-head workgroups) runs whole-head workgroups of 8 waves."""
+    shape, dtype = gi.QWEN, "bf16"
+    _say(f"prefill carry path B={B} L={L}")
+    inp = layer_inputs(shape, B, L, 14 + B, dtype, s0_std=0.1, conv_std=1.0)
+    got = run_prefill(shape, dtype, inp)
+    ref = oracle.gdn_forward(oparams(shape), inp["qkv"], inp["gate"], inp["beta"], inp["w"],
+                             inp["conv0"], inp["S0"])
+    assert rel_err(got["o"], ref["o"]) <= TOL[dtype]
+    assert rel_err(got["S"], ref["S"]) <= TOL[dtype]
+    assert np.array_equal(got["conv_out"].float().cpu().numpy(), ref["conv_out"])
+
+
+def test_prefill_ragged_many_sequences():
+    """Nine packed sequences of the 16/32-head shape: 288 heads, more than the CUs, so the
+    carry runs whole-head workgroups (longest sequence first)."""
+    shape, dtype = gi.QWEN, "bf16"
+    lens = [20, 65, 0, 130, 1, 64, 3, 70, 40]
+    cu = gi.cu_seqlens(lens)
+    _say(f"prefill ragged, {len(lens)} sequences of the full head shape")
+    inp = layer_inputs(shape, 1, int(cu[-1]), 21, dtype, N=len(lens), s0_std=0.1, conv_std=1.0)
+    got = run_prefill(shape, dtype, inp, cu=cu)
+    ref = oracle.gdn_forward(oparams(shape), inp["qkv"], inp["gate"], inp["beta"], inp["w"],
+                             inp["conv0"], inp["S0"], cu_seqlens=cu)
+    assert rel_err(got["o"], ref["o"]) <= TOL[dtype]
+    assert rel_err(got["S"], ref["S"]) <= TOL[dtype]
+    assert np.array_equal(got["conv_out"].float().cpu().numpy(), ref["conv_out"])
+
+
 def test_prefill_long_memory():
     """Weak decay (gate scaled by 0.01) so early errors do not fade; beta near 1."""
     shape, dtype = SMALL128, "bf16"
