@@ -11,7 +11,7 @@
 // (exact to apply and to undo); q and k are unit-norm and P, W are bounded by
 // them.
 //
-//   front_kernel   steps 1-4 on a (64-token, 128-channel) tile: coalesced
+//   front_kernel   steps 1-4 on a (32-token, 128-channel) tile: coalesced
 //                  channel-major loads, conv + SiLU, transpose through LDS,
 //                  per-token L2 norms and the q scale; fp16 token-major q, k, v.
 //   chunk_kernel   per (chunk, V head), all chunks in parallel: Gam (cumulative
@@ -30,7 +30,13 @@
 //                  half of a double-buffered LDS stage with global_load_lds
 //                  while the current chunk computes. Accumulator tiles are fed
 //                  back as B operands without data movement by pairing the k
-//                  slots of the MFMA with the accumulator rows they hold.
+//                  slots of the MFMA with the accumulator rows they hold. A lone
+//                  prompt with few heads runs in segments: a first pass (segment
+//                  0, and each middle segment's state map and zero-entry state),
+//                  seg_chain_kernel (the entry state of every later segment),
+//                  and a second pass over segments 1 .. nseg - 1.
+#include <algorithm>
+
 #include "gdn_common.hpp"
 #include "gdn_launch.hpp"
 #include "gdn_mfma.hpp"
@@ -72,15 +78,15 @@ struct Ws {
     _Float16* P;    // [NC, Hv, C, C] keys in k order
     _Float16* KT;   // [NC, Hk, D, C] keys of the chunk, transposed, tokens in k order
     float* coef;    // [NC, Hv, COEF]: exp(Gam_t), exp(Gam_last - Gam_t), exp(Gam_last), 2^uexp
-    // two-segment carry (see carry_kernel): per sequence the chunks split at cm = nch / 2
-    _Float16* SmidT;  // [N, Hv, D, D] state after the first segment, transposed ([column][row]),
-                      // scaled per 16-column tile by 2^-Sexp
-    int* Sexp;        // [N, Hv, D / 16] those scale exponents
-    float* R;       // [N, Hv, D, D] second segment's end state from a zero entry state
-    float* M;       // [N, Hv, D, D] second segment's state map (its end state from the identity)
-    float* Y;       // [nch - cm, N, Hv, C, D] outputs of the identity columns
+    // segmented carry (see carry_kernel): the chunks of a sequence split into nseg segments
+    float* Sent;    // [nseg - 1, N, Hv, D, D] entry states of segments 1 .. nseg - 1
+    _Float16* Mhl;  // [nseg - 2, N, Hv, 2, D, D] state maps of segments 1 .. nseg - 2 (S_end = M S_entry + R):
+                    // M = hi + lo, fp16 planes, column tile t scaled by 2^-Mexp[t]
+    int* Mexp;      // [nseg - 2, N, Hv, D / 16]
+    float* Rseg;    // [nseg - 2, N, Hv, D, D] their end states from a zero entry state
     int nc_max;
-    int seg;        // 1: the two-segment carry is in use
+    int nseg;       // segments per sequence (1: one chain per sequence)
+    int pass;       // segmented carry: which of its two carry passes a launch runs
     size_t bytes;
 };
 
@@ -91,12 +97,32 @@ static int max_chunks(int B, int L, int N, bool ragged) {
     return ragged ? per + N : B * per;
 }
 
-// Unpacked prompts whose heads leave the CUs idle run the carry in two segments:
-// 6 workgroups per head (3 kinds x 2 column halves) must fit one round of the
-// CUs (6 x 42 = 252 <= 256) and each sequence needs at least two chunks.
-constexpr int kSegHeads = 42;
-static bool use_segments(int B, int L, int N, int Hv, bool ragged) {
-    return !ragged && static_cast<long long>(N) * Hv <= kSegHeads && (L + C - 1) / C >= 2 && B == N;
+// Unpacked prompts whose heads leave the CUs idle run the carry in segments (see
+// carry_kernel). Its second pass runs 2 (nseg - 1) half-head workgroups per head and
+// its first 2 nseg - 3 whole-head ones, each pass in one round of the CUs; a segment
+// averages at least kMinSegChunks chunks, and nseg >= 3 (with two segments the two
+// passes are one chain cut in two).
+constexpr int kMaxSeg = 8;
+constexpr int kMinSegChunks = 4;
+constexpr int kLayoutCUs = 256;   // the workspace is sized for this many CUs at most
+static int segments(int B, int L, int N, int Hv, bool ragged, int cus) {
+    if (ragged || B != N || N <= 0 || Hv <= 0) return 1;
+    const long long heads = static_cast<long long>(N) * Hv;
+    long long ks = cus / (2 * heads) + 1;
+    ks = std::min<long long>(ks, kMaxSeg);
+    ks = std::min<long long>(ks, ((L + C - 1) / C) / kMinSegChunks);
+    return ks >= 3 ? static_cast<int>(ks) : 1;
+}
+
+// First chunk of segment j (0 <= j <= nseg) of a sequence of nch chunks. Segment 0
+// alone also forms its outputs in the first pass, at whole-head speed, so it gets
+// kSeg0 / 8 of the share of each other segment.
+constexpr int kSeg0 = 5;
+__host__ __device__ __forceinline__ int seg_begin(int nch, int nseg, int j) {
+    if (j <= 0) return 0;
+    if (j >= nseg) return nch;
+    const int den = kSeg0 + 8 * (nseg - 1);
+    return (nch * (kSeg0 + 8 * (j - 1)) + den / 2) / den;
 }
 
 static Ws layout(void* base, int B, int L, int N, int Hk, int Hv, bool ragged) {
@@ -117,18 +143,17 @@ static Ws layout(void* base, int B, int L, int N, int Hk, int Hv, bool ragged) {
     w.P = static_cast<_Float16*>(take(nc * Hv * C * C * 2));
     w.KT = static_cast<_Float16*>(take(nc * Hk * D * C * 2));
     w.coef = static_cast<float*>(take(nc * Hv * COEF * 4));
-    w.seg = use_segments(B, L, N, Hv, ragged) ? 1 : 0;
-    w.SmidT = nullptr;
-    w.Sexp = nullptr;
-    w.R = w.M = w.Y = nullptr;
-    if (w.seg) {
-        const int nch = (L + C - 1) / C, n2 = nch - nch / 2;
+    w.nseg = segments(B, L, N, Hv, ragged, kLayoutCUs);
+    w.pass = 0;
+    w.Sent = w.Rseg = nullptr;
+    w.Mhl = nullptr;
+    w.Mexp = nullptr;
+    if (w.nseg > 1) {
         const size_t tiles = static_cast<size_t>(N) * Hv * D * D;
-        w.SmidT = static_cast<_Float16*>(take(tiles * 2));
-        w.Sexp = static_cast<int*>(take(static_cast<size_t>(N) * Hv * (D / 16) * 4));
-        w.R = static_cast<float*>(take(tiles * 4));
-        w.M = static_cast<float*>(take(tiles * 4));
-        w.Y = static_cast<float*>(take(static_cast<size_t>(n2) * N * Hv * C * D * 4));
+        w.Sent = static_cast<float*>(take(static_cast<size_t>(w.nseg - 1) * tiles * 4));
+        w.Mhl = static_cast<_Float16*>(take(static_cast<size_t>(w.nseg - 2) * tiles * 2 * 2));
+        w.Mexp = static_cast<int*>(take(static_cast<size_t>(w.nseg - 2) * N * Hv * (D / 16) * 4));
+        w.Rseg = static_cast<float*>(take(static_cast<size_t>(w.nseg - 2) * tiles * 4));
     }
     w.nc_max = static_cast<int>(nc);
     w.bytes = off;
@@ -882,14 +907,16 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
     constexpr int NS = 128 / CPW;                        // workgroups per head
     const int nh = a.N * a.Hv;
     const int tid = threadIdx.x, lane = tid & 63;
-    // Two-segment mode (ws.seg): the chunks of each sequence split at cm = nch / 2 and
-    // three kinds of workgroup run at once: FIRST carries the first segment from the
-    // entry state; LOCAL carries the second from a zero state; XMAP carries the
-    // identity through the second with U = 0, so that its columns are the segment's
-    // state map M (S_end = M S_mid + R, the chunk maps being affine in the entry
-    // state) and its outputs Y give the entry state's share of every output
-    // (o = o_local + Y S_mid). seg_fix_kernel adds those shares afterwards.
-    const int NK = ws.seg ? 3 : 1;                       // kinds per head
+    // Segmented mode (ws.nseg > 1): the chunks of each sequence split into nseg
+    // segments and the carry runs in two passes. A chunk step is affine in the state
+    // (S' = A_c S + B_c, each column on its own), so over a segment j the end state is
+    // M_j S_entry + R_j. Pass 1 runs at once: FIRST, segment 0 from the entry state
+    // with its outputs, ending in the entry state of segment 1; and for each middle
+    // segment, LOCAL (from a zero state: R_j) and XMAP (the identity carried with
+    // U = 0: M_j), neither forming outputs. seg_chain_kernel then forms the entry
+    // state of every later segment, and pass 2 carries segments 1 .. nseg - 1 from
+    // their entry states with outputs; the last one ends in the final state.
+    const int NK = ws.nseg <= 1 ? 1 : (ws.pass == 1 ? 2 * ws.nseg - 3 : ws.nseg - 1);   // kinds per head
     // blockIdx -> (slice, slot): the NK * NS slices of a slot are dispatched together
     // and 8 blockIdx apart, i.e. on one XCD, sharing its L2 for the operands they
     // read; the tail that does not fill a group of 8 slots is laid out slice-major.
@@ -907,8 +934,7 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
         }
     }
     const int cs = slice % NS;
-    const int kind = slice / NS;                         // 0 FIRST (or the whole chain), 1 LOCAL, 2 XMAP
-    const bool xm = kind == 2;
+    const int kind = slice / NS;
     const int h = slot % a.Hv;
     int n = slot / a.Hv;
     // Packed prompts: slots go to sequences longest first, so that the in-order
@@ -929,12 +955,36 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
     int nch = chunks_of(seg);
     if (base + nch > ws.nc_max) nch = ws.nc_max - base;   // only malformed cu_seqlens get here
     if (nch <= 0) return;
-    const int cm = nch / 2;                              // segment boundary (two-segment mode)
-    const int cb = (ws.seg && kind > 0) ? cm : 0;        // chunks [cb, ce) of this workgroup
-    const int ce = (ws.seg && kind == 0) ? cm : nch;
-
+    // this workgroup's job: segment sj (chunks [cb, ce)), its entry state, whether it
+    // forms outputs and loads U, and where its end state goes (nowhere if null)
     const size_t tile = (static_cast<size_t>(n) * a.Hv + h) * D * D;
-    float* Sg = a.S + tile;
+    const size_t tiles = static_cast<size_t>(a.N) * a.Hv * D * D;
+    enum { FROM, ZERO, IDENT };
+    int sj = 0, entry = FROM;
+    bool outs = true, useU = true;
+    const float* Sin = a.S + tile;
+    float* Send = a.S + tile;
+    size_t mapo = 0;                                     // XMAP: its map's offset in Mhl, Mexp (+ 1)
+    if (ws.nseg > 1) {
+        if (ws.pass == 1) {
+            if (kind == 0) {
+                Send = ws.Sent + tile;
+            } else {
+                sj = (kind + 1) / 2;
+                outs = false;
+                const size_t off = static_cast<size_t>(sj - 1) * tiles + tile;
+                if (kind & 1) { entry = ZERO; Send = ws.Rseg + off; }
+                else { entry = IDENT; useU = false; Send = nullptr; mapo = off / (D * D) + 1; }
+            }
+        } else {
+            sj = kind + 1;
+            Sin = ws.Sent + static_cast<size_t>(sj - 1) * tiles + tile;
+            if (sj != ws.nseg - 1) Send = nullptr;
+        }
+    }
+    const int cb = ws.nseg > 1 ? seg_begin(nch, ws.nseg, sj) : 0;
+    const int ce = ws.nseg > 1 ? seg_begin(nch, ws.nseg, sj + 1) : nch;
+
     float S[8][NTW][4];
     float smax = 0.f;
 #pragma unroll
@@ -944,29 +994,32 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 16 * mt + 4 * g + e, j = col0 + 16 * nt + r16;
-                S[mt][nt][e] = kind == 0 ? Sg[i * D + j] : (xm && i == j ? 1.f : 0.f);
+                S[mt][nt][e] = entry == FROM ? Sin[i * D + j] : (entry == IDENT && i == j ? 1.f : 0.f);
                 smax = fmaxf(smax, fabsf(S[mt][nt][e]));
             }
 
     const size_t row_tok = static_cast<size_t>(seg.row) * a.L + seg.start;
-    // outputs: o (token stride Hv * D), or for XMAP the per-chunk blocks of Y
-    const size_t ts = xm ? static_cast<size_t>(D) : static_cast<size_t>(a.Hv) * D;
-    if (xm && !loader) {   // U = 0: the U regions of both stages are zeroed once and never loaded
+    const size_t ts = static_cast<size_t>(a.Hv) * D;     // token stride of o
+    if (!useU && !loader) {   // U = 0: the U regions of both stages are zeroed once and never loaded
         for (int i = tid; i < 64 * SG::UG; i += NW * 64) {
             reinterpret_cast<uint4*>(g_stage + SG::U * 16)[i] = make_uint4(0, 0, 0, 0);
             reinterpret_cast<uint4*>(g_stage + SG::BYTES + SG::U * 16)[i] = make_uint4(0, 0, 0, 0);
         }
     }
-    if (!LW || loader) {
-#pragma unroll
-        for (int w = LW ? 0 : wave; w < (LW ? NW : wave + 1); ++w) {
-            if (xm)
-                issue_stage<CPW, NW, ST_ALL & ~ST_U>(a, ws, base + cb, row_tok + static_cast<size_t>(cb) * C,
-                                                    min(C, seg.len - cb * C), h, hk, ucol0, 0, w, lane);
-            else
-                issue_stage<CPW, NW, ST_ALL>(a, ws, base + cb, row_tok + static_cast<size_t>(cb) * C,
-                                             min(C, seg.len - cb * C), h, hk, ucol0, 0, w, lane);
+    // a whole stage: every region this job reads (no Q and P without outputs, no U when it is 0)
+    auto issue_all = [&](int id, size_t tok, int nt, int buf, int w) {
+        if (outs) {
+            if (useU) issue_stage<CPW, NW, ST_ALL>(a, ws, id, tok, nt, h, hk, ucol0, buf, w, lane);
+            else issue_stage<CPW, NW, ST_ALL & ~ST_U>(a, ws, id, tok, nt, h, hk, ucol0, buf, w, lane);
+        } else {
+            if (useU) issue_stage<CPW, NW, ST_W | ST_KT | ST_U | ST_CF>(a, ws, id, tok, nt, h, hk, ucol0, buf, w, lane);
+            else issue_stage<CPW, NW, ST_W | ST_KT | ST_CF>(a, ws, id, tok, nt, h, hk, ucol0, buf, w, lane);
         }
+    };
+    if ((!LW || loader) && cb < ce) {
+#pragma unroll
+        for (int w = LW ? 0 : wave; w < (LW ? NW : wave + 1); ++w)
+            issue_all(base + cb, row_tok + static_cast<size_t>(cb) * C, min(C, seg.len - cb * C), 0, w);
     }
     if (loader) {   // stage c + 1 is issued after the barrier that frees its buffer
         for (int c = cb; c < ce; ++c) {
@@ -977,12 +1030,7 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
                 const int ntn = min(C, seg.len - (c + 1) * C);
                 const int sbn = (c - cb + 1) & 1;
 #pragma unroll
-                for (int w = 0; w < NW; ++w) {
-                    if (xm)
-                        issue_stage<CPW, NW, ST_ALL & ~ST_U>(a, ws, base + c + 1, tokn, ntn, h, hk, ucol0, sbn, w, lane);
-                    else
-                        issue_stage<CPW, NW, ST_ALL>(a, ws, base + c + 1, tokn, ntn, h, hk, ucol0, sbn, w, lane);
-                }
+                for (int w = 0; w < NW; ++w) issue_all(base + c + 1, tokn, ntn, sbn, w);
             }
         }
         return;
@@ -1000,10 +1048,10 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
         const int ntn = min(C, seg.len - (c + 1) * C);
         const int sb_ = (c - cb + 1) & 1;                // stage buffer of the next chunk
         if (!LW && more) {
-            if (xm)
-                issue_stage<CPW, NW, ST_W | ST_CF>(a, ws, id + 1, tok0 + C, ntn, h, hk, ucol0, sb_, wave, lane);
-            else
+            if (useU)
                 issue_stage<CPW, NW, ST_W | ST_U | ST_CF>(a, ws, id + 1, tok0 + C, ntn, h, hk, ucol0, sb_, wave, lane);
+            else
+                issue_stage<CPW, NW, ST_W | ST_CF>(a, ws, id + 1, tok0 + C, ntn, h, hk, ucol0, sb_, wave, lane);
         }
         const unsigned char* st = g_stage + ((c - cb) & 1) * SG::BYTES;
         const _Float16* Wl = reinterpret_cast<const _Float16*>(st + SG::W * 16);
@@ -1108,7 +1156,7 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
                     dp[nt][ks][e] = static_cast<_Float16>(v * cfr[t]);
                 }
 
-        if (!LW && more)
+        if (!LW && more && outs)
             issue_stage<CPW, NW, ST_Q | ST_P>(a, ws, id + 1, tok0 + C, ntn, h, hk, ucol0, sb_, wave, lane);
 
         // O = diag(exp(Gam)) Q S + P Delta, stored as soon as it is formed. With one
@@ -1117,15 +1165,14 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
         // holds 4 consecutive columns of one token and stores them in one 16-byte
         // store: 4 store instructions per tile instead of 16 scattered dword stores.
         constexpr bool OT = NTW == 1;
-        // this chunk's first output row: o, or for XMAP its block of Y
-        float* obase = xm ? ws.Y + ((static_cast<size_t>(c - cm) * a.N + n) * a.Hv + h) * C * D
-                          : a.o + (tok0 * a.Hv + h) * D;
+        float* obase = a.o + (tok0 * a.Hv + h) * D;              // this chunk's first output row
         float* ob = obase + col0 + r16 + 4 * g * ts;
         const bool full = ntc == C;                            // uniform: every row stored
         // operands read ahead of the MFMAs when BATCH, OB row tiles at a time (one
         // with a loader wave: 256 registers, and each tile's reads then overlap the
         // previous tile's MFMAs: 237 -> 225 us at L = 4096), else inside the loop
         constexpr int OB = LW ? 1 : 4;
+        if (outs) {
 #pragma unroll
         for (int m0 = 0; m0 < 4; m0 += OB) {
         f16x8 aq[OB][4], ap[OB][2];
@@ -1164,7 +1211,8 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
                 const float eg = cf[t] * iS;
                 const float4 v = make_float4(__fmaf_rn(eg, a1[0][0], iD * a2[0][0]), __fmaf_rn(eg, a1[0][1], iD * a2[0][1]),
                                              __fmaf_rn(eg, a1[0][2], iD * a2[0][2]), __fmaf_rn(eg, a1[0][3], iD * a2[0][3]));
-                if (full || t < ntc) *reinterpret_cast<float4*>(obase + t * ts + col0 + 4 * g) = v;
+                if (full || t < ntc)
+                    __builtin_nontemporal_store(f32x4v{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4v*>(obase + t * ts + col0 + 4 * g));
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -1172,10 +1220,12 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
                     if (full || 16 * mt + 4 * g + e < ntc) {
                         float* orow = ob + (16 * mt + e) * ts;
 #pragma unroll
-                        for (int nt = 0; nt < NTW; ++nt) orow[16 * nt] = __fmaf_rn(eg, a1[nt][e], iD * a2[nt][e]);
+                        for (int nt = 0; nt < NTW; ++nt)
+                            __builtin_nontemporal_store(__fmaf_rn(eg, a1[nt][e], iD * a2[nt][e]), orow + 16 * nt);
                     }
                 }
             }
+        }
         }
         }
         if (!LW && more)
@@ -1211,128 +1261,157 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
                 }
         }
     }
-    // end state: S, or in two-segment mode S_mid (transposed, [column][row]), R or M
-    if (ws.seg && kind == 0) {   // fp16, scaled per wave (its 16-column tiles), the exponent beside it
-        const int ef = pow2_exponent(wave_max_nonneg(smax));
-        const float sf = ldexpf(1.f, -ef);
-        _Float16* dst = ws.SmidT + tile;
+    // end state: S, or in segmented mode an entry state, R_j or M_j (or nothing). M_j
+    // goes out split into fp16 high and low parts scaled per 16-column tile (a wave's
+    // columns), staged through LDS into row-major planes.
+    if constexpr (!LW && NTW == 1) {
+        if (mapo != 0) {
+            const size_t m = mapo - 1;                   // (segment, sequence, head) of the map
+            const int eC = pow2_exponent(wave_max_nonneg(smax));
+            const float sC = ldexpf(1.f, -eC);
+            constexpr int MS = D + 8;                    // LDS row stride (halfs)
+            _Float16* lh = reinterpret_cast<_Float16*>(g_stage);
+            _Float16* ll = lh + D * MS;
+            __syncthreads();                             // every wave is done with the stages
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
+            for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) {
-                const f16x4 v = {static_cast<_Float16>(S[mt][nt][0] * sf), static_cast<_Float16>(S[mt][nt][1] * sf),
-                                 static_cast<_Float16>(S[mt][nt][2] * sf), static_cast<_Float16>(S[mt][nt][3] * sf)};
-                *reinterpret_cast<f16x4*>(dst + (col0 + 16 * nt + r16) * D + 16 * mt + 4 * g) = v;
+                for (int e = 0; e < 4; ++e) {
+                    const float x = S[mt][0][e] * sC;
+                    const _Float16 hi = static_cast<_Float16>(x);
+                    lh[(16 * mt + 4 * g + e) * MS + col0 + r16] = hi;
+                    ll[(16 * mt + 4 * g + e) * MS + col0 + r16] = static_cast<_Float16>(x - static_cast<float>(hi));
+                }
+            if (lane == 0) ws.Mexp[m * (D / 16) + col0 / 16] = eC;
+            __syncthreads();
+            _Float16* dst = ws.Mhl + m * 2 * D * D;
+            for (int q = tid; q < 2 * D * (D / 8); q += NW * 64) {   // 16-byte granules of both planes
+                const int pl = q / (D * D / 8), row = (q / (D / 8)) % D, j8 = q % (D / 8);
+                const uint4 v = *reinterpret_cast<const uint4*>(lh + pl * D * MS + row * MS + 8 * j8);
+                *reinterpret_cast<uint4*>(dst + static_cast<size_t>(pl) * D * D + row * D + 8 * j8) = v;
             }
-        if (lane < NTW) ws.Sexp[(static_cast<size_t>(n) * a.Hv + h) * (D / 16) + col0 / 16 + lane] = ef;
-    } else {
-        float* dst = !ws.seg ? Sg : (xm ? ws.M + tile : ws.R + tile);
+        }
+    }
+    if (Send != nullptr) {
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
             for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) dst[(16 * mt + 4 * g + e) * D + col0 + 16 * nt + r16] = S[mt][nt][e];
+                for (int e = 0; e < 4; ++e)
+                    __builtin_nontemporal_store(S[mt][nt][e], Send + (16 * mt + 4 * g + e) * D + col0 + 16 * nt + r16);
     }
 }
 
-// Second-segment corrections of the two-segment carry on fp16 MFMA, with the
-// same power-of-two operand scaling as the carry. Per (sequence, head): n2
-// workgroups add Y_c S_mid to the outputs of one chunk each (a wave per 16-row
-// tile), and two more write the final state M S_mid + R. A wave issues its tile's
-// loads (rows of Y or M, fp32, and the accumulator start: the local outputs or R)
-// first, then the workgroup stages S_mid (fp16, stored transposed and scaled per
-// 16-column tile by the first segment's workgroups) in LDS. The products are
-// formed transposed (S_mid as the A operand), so a lane holds 4 consecutive
-// columns of one row: the accumulator start, the result and the stores are 16
-// bytes per lane. A rows are scaled per 16-row tile; both scales factor out of the
-// tile's product, which is added in fp32.
-constexpr int SMS = D + 8;                // row stride (halfs) of S_mid in LDS
-
-struct FixTile {
-    float4 av[8];                         // the tile's row r16: k = 32 (q / 2) + 8 g + 4 (q % 2) + 0..3
-    float4 iv[8];                         // accumulator start, row r16, columns 16 nt + 4 g ..
-};
-
-__device__ __forceinline__ void fix_load(FixTile& ft, const float* A, int nrows, const float* init, size_t stride, int lane) {
-    const int g = lane >> 4, r16 = lane & 15;
-    const bool rv = r16 < nrows;          // rows past the end of a partial chunk were never written
-    const int rr = rv ? r16 : 0;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const float4 v = *reinterpret_cast<const float4*>(A + rr * D + 32 * (q >> 1) + 8 * g + 4 * (q & 1));
-        ft.av[q] = rv ? v : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
-        ft.iv[nt] = *reinterpret_cast<const float4*>(init + rr * stride + 16 * nt + 4 * g);
-}
-
-__device__ __forceinline__ void fix_compute(const FixTile& ft, int nrows, const _Float16* sm, const int* sexp, float* out,
-                                            size_t stride, int lane) {
-    const int g = lane >> 4, r16 = lane & 15;
-    const bool rv = r16 < nrows;
-    float amax = 0.f;
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(ft.av[q].x), fabsf(ft.av[q].y)), fmaxf(fabsf(ft.av[q].z), fabsf(ft.av[q].w))));
-    const int ea = pow2_exponent(wave_max_nonneg(amax));
-    const float sa = ldexpf(1.f, -ea);
-    f16x8 bop[4];                         // the tile's rows as B operands (k = row of S_mid)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        const float4 lo = ft.av[2 * ks], hi = ft.av[2 * ks + 1];
-        bop[ks] = f16x8{static_cast<_Float16>(lo.x * sa), static_cast<_Float16>(lo.y * sa),
-                        static_cast<_Float16>(lo.z * sa), static_cast<_Float16>(lo.w * sa),
-                        static_cast<_Float16>(hi.x * sa), static_cast<_Float16>(hi.y * sa),
-                        static_cast<_Float16>(hi.z * sa), static_cast<_Float16>(hi.w * sa)};
-    }
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-        f32x4v prod = f32x4v{0, 0, 0, 0};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const f16x8 aop = *reinterpret_cast<const f16x8*>(sm + (16 * nt + r16) * SMS + 32 * ks + 8 * g);
-            prod = mfma16x16x32(aop, bop[ks], prod);
-        }
-        const float sc = ldexpf(1.f, ea + sexp[nt]);   // may underflow to 0: the product is then negligible
-        const float4 v = make_float4(__fmaf_rn(prod[0], sc, ft.iv[nt].x), __fmaf_rn(prod[1], sc, ft.iv[nt].y),
-                                     __fmaf_rn(prod[2], sc, ft.iv[nt].z), __fmaf_rn(prod[3], sc, ft.iv[nt].w));
-        if (rv) *reinterpret_cast<float4*>(out + r16 * stride + 16 * nt + 4 * g) = v;
-    }
-}
-
-__global__ __launch_bounds__(256) void seg_fix_kernel(PrefillArgs a, Ws ws) {
-    __shared__ __align__(16) _Float16 sm[D * SMS];
-    __shared__ int s_exp[D / 16];
-    const int nch = (a.L + C - 1) / C, cm = nch / 2, n2 = nch - cm;
-    const int per = n2 + 2;
-    const int r = blockIdx.x % per, nhid = blockIdx.x / per;
-    const int n = nhid / a.Hv, h = nhid % a.Hv;
+// Entry states of the segmented carry: S_1 (the first pass's end state of segment 0)
+// and, for j = 1 .. nseg - 2, S_{j+1} = M_j S_j + R_j. The columns of a state evolve
+// independently, so a workgroup owns 16 columns of one (sequence, head) and chains
+// them through every segment; the 8 column blocks of a head are dispatched 8 apart,
+// i.e. on one XCD. The products run on fp16 MFMA with both operands split into a high
+// and a low fp16 part (x = hi + lo after a power-of-two scale into fp16's range: 22
+// significant bits) and hi*hi + hi*lo + lo*hi accumulated in fp32, close to an fp32
+// product, so the chain does not degrade the entry states of later segments. The maps
+// come split already (scaled per 16-column tile, which is undone on the rows of S_j
+// it multiplies). Wave w forms rows 16 w .. 16 w + 15 of every product: its rows of
+// the maps are A operands held in registers, loaded CHPF maps ahead (the products
+// are short and each depends on the last, so the load latency is paid about once),
+// and the block (in LDS, transposed) gives the B operands.
+constexpr int CBS = D + 4;   // row stride (floats) of a transposed column block
+constexpr int CHPF = 3;      // maps in flight per wave
+__global__ __launch_bounds__(512) void seg_chain_kernel(PrefillArgs a, Ws ws) {
+    __shared__ __align__(16) float blk[2][16 * CBS];
+    const int heads = a.N * a.Hv;
+    const int cbk = (blockIdx.x % 64) / 8, hd = 8 * (blockIdx.x / 64) + blockIdx.x % 8;
+    if (hd >= heads) return;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const size_t tile = (static_cast<size_t>(n) * a.Hv + h) * D * D;
-    // this wave's tile: rows 16 wave.. of chunk cm + r's outputs, or of the final state
-    const bool outs = r < n2;
-    const int c = cm + r;
-    const int nrows = outs ? min(C, a.L - c * C) - 16 * wave : 16;
-    float* ob = outs ? a.o + ((static_cast<size_t>(n) * a.L + static_cast<size_t>(c) * C + 16 * wave) * a.Hv + h) * D
-                     : a.S + tile + static_cast<size_t>(64 * (r - n2) + 16 * wave) * D;
-    const float* Ab = outs ? ws.Y + ((static_cast<size_t>(r) * a.N + n) * a.Hv + h) * C * D + 16 * wave * D
-                           : ws.M + tile + static_cast<size_t>(64 * (r - n2) + 16 * wave) * D;
-    const float* ib = outs ? ob : ws.R + tile + static_cast<size_t>(64 * (r - n2) + 16 * wave) * D;
-    const size_t stride = outs ? static_cast<size_t>(a.Hv) * D : static_cast<size_t>(D);
-    FixTile ft;
-    if (nrows > 0) fix_load(ft, Ab, nrows, ib, stride, lane);
-    const _Float16* SmT = ws.SmidT + tile;
+    const int g = lane >> 4, r16 = lane & 15;
+    const size_t tiles = static_cast<size_t>(heads) * D * D, tile = static_cast<size_t>(hd) * D * D;
+    const int cw = 16 * cbk + r16;                       // this lane's column (B operand, accumulator)
+    const int nprod = ws.nseg - 2;
+    // A operands: row 16 wave + r16, k = 32 ks + 8 g + 0..7, both planes; R at the
+    // accumulator positions (rows 16 wave + 4 g + e, column cw)
+    f16x8 mh[CHPF][4], ml[CHPF][4];
+    float rv[CHPF][4];
+#define GDN_CHAIN_LOAD(J, SL)                                                                          \
+    do {                                                                                               \
+        const size_t m_ = static_cast<size_t>((J) - 1) * heads + hd;                                   \
+        const _Float16* Mh_ = ws.Mhl + m_ * 2 * D * D + static_cast<size_t>(16 * wave + r16) * D + 8 * g; \
+        const float* R_ = ws.Rseg + m_ * D * D;                                                        \
+        _Pragma("unroll") for (int ks = 0; ks < 4; ++ks) {                                             \
+            mh[SL][ks] = *reinterpret_cast<const f16x8*>(Mh_ + 32 * ks);                               \
+            ml[SL][ks] = *reinterpret_cast<const f16x8*>(Mh_ + D * D + 32 * ks);                       \
+        }                                                                                              \
+        _Pragma("unroll") for (int e = 0; e < 4; ++e)                                                  \
+            rv[SL][e] = R_[static_cast<size_t>(16 * wave + 4 * g + e) * D + cw];                       \
+    } while (0)
+    // S_1's block first (the loads return in order), then the first maps
+    const int row1 = tid >> 2, q1 = tid & 3;   // thread -> row tid / 4, columns 4 (tid % 4) ..
+    const float4 s1 = *reinterpret_cast<const float4*>(ws.Sent + tile + static_cast<size_t>(row1) * D + 16 * cbk + 4 * q1);
 #pragma unroll
-    for (int q = 0; q < D * D / 8 / 256; ++q) {
-        const int it = tid + 256 * q, row = it >> 4, j = it & 15;
-        *reinterpret_cast<uint4*>(sm + row * SMS + 8 * j) = *reinterpret_cast<const uint4*>(SmT + row * D + 8 * j);
+    for (int u = 0; u < CHPF; ++u)
+        if (u < nprod) GDN_CHAIN_LOAD(1 + u, u);
+    blk[0][(4 * q1 + 0) * CBS + row1] = s1.x;   // transposed into LDS
+    blk[0][(4 * q1 + 1) * CBS + row1] = s1.y;
+    blk[0][(4 * q1 + 2) * CBS + row1] = s1.z;
+    blk[0][(4 * q1 + 3) * CBS + row1] = s1.w;
+    for (int j0 = 1; j0 <= nprod; j0 += CHPF) {
+#pragma unroll
+        for (int u = 0; u < CHPF; ++u) {
+            const int j = j0 + u;
+            if (j > nprod) break;
+            float* Snext = ws.Sent + static_cast<size_t>(j) * tiles + tile;
+            const int* ek = ws.Mexp + (static_cast<size_t>(j - 1) * heads + hd) * (D / 16);
+            __syncthreads();   // S_j's block is in blk[(j - 1) & 1]
+            const float* cur = blk[(j - 1) & 1] + r16 * CBS;
+            float* nxt = blk[j & 1] + r16 * CBS;
+            // B operands: S_j[k][cw] 2^(e of k's column tile of M_j), k = 32 ks + 8 g + 0..7
+            float bv[4][8];
+            float smax = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const float sk = ldexpf(1.f, (g >> 1) ? ek[2 * ks + 1] : ek[2 * ks]);
+                const float4 lo = *reinterpret_cast<const float4*>(cur + 32 * ks + 8 * g);
+                const float4 hi = *reinterpret_cast<const float4*>(cur + 32 * ks + 8 * g + 4);
+                const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    bv[ks][e] = v[e] * sk;
+                    smax = fmaxf(smax, fabsf(bv[ks][e]));
+                }
+            }
+            const int eS = pow2_exponent(wave_max_nonneg(smax));
+            const float sS = ldexpf(1.f, -eS);
+            f32x4v acc = f32x4v{0, 0, 0, 0};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                f16x8 bh, bl;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float x = bv[ks][e] * sS;
+                    bh[e] = static_cast<_Float16>(x);
+                    bl[e] = static_cast<_Float16>(x - static_cast<float>(bh[e]));
+                }
+                acc = mfma16x16x32(mh[u][ks], bh, acc);
+                acc = mfma16x16x32(mh[u][ks], bl, acc);
+                acc = mfma16x16x32(ml[u][ks], bh, acc);
+            }
+            const float sc = ldexpf(1.f, eS);
+            const int row0 = 16 * wave + 4 * g;          // lane: rows row0 .. row0 + 3, column cw
+            float4 o;
+            o.x = __fmaf_rn(acc[0], sc, rv[u][0]);
+            o.y = __fmaf_rn(acc[1], sc, rv[u][1]);
+            o.z = __fmaf_rn(acc[2], sc, rv[u][2]);
+            o.w = __fmaf_rn(acc[3], sc, rv[u][3]);
+            if (j + CHPF <= nprod) GDN_CHAIN_LOAD(j + CHPF, u);   // this slot's next map
+            *reinterpret_cast<float4*>(nxt + row0) = o;
+            __builtin_nontemporal_store(o.x, Snext + static_cast<size_t>(row0) * D + cw);
+            __builtin_nontemporal_store(o.y, Snext + static_cast<size_t>(row0 + 1) * D + cw);
+            __builtin_nontemporal_store(o.z, Snext + static_cast<size_t>(row0 + 2) * D + cw);
+            __builtin_nontemporal_store(o.w, Snext + static_cast<size_t>(row0 + 3) * D + cw);
+        }
     }
-    if (tid < D / 16) s_exp[tid] = ws.Sexp[(static_cast<size_t>(n) * a.Hv + h) * (D / 16) + tid];
-    __syncthreads();
-    if (nrows > 0) fix_compute(ft, nrows, sm, s_exp, ob, stride, lane);
+#undef GDN_CHAIN_LOAD
 }
 
 }  // namespace pf2
@@ -1381,6 +1460,8 @@ template <typename Tin>
 static hipError_t launch_mfma_t(const PrefillArgs& a, int in_dtype, hipStream_t stream) {
     const bool ragged = a.cu != nullptr;
     pf2::Ws ws = pf2::layout(a.ws, a.B, a.L, a.N, a.Hk, a.Hv, ragged);
+    const int cus = device_cu_count();
+    ws.nseg = std::min(ws.nseg, pf2::segments(a.B, a.L, a.N, a.Hv, ragged, cus));   // within the workspace
     void* args[] = {const_cast<PrefillArgs*>(&a), &ws};
     hipError_t e;
     const long long fblocks = static_cast<long long>(a.B) * ((a.L + pf2::TT - 1) / pf2::TT) * (2 * a.Hk + a.Hv);
@@ -1401,15 +1482,22 @@ static hipError_t launch_mfma_t(const PrefillArgs& a, int in_dtype, hipStream_t 
         // CUs, and for packed prompts when it fits two: their chains differ in length
         // and, dispatched longest first, the halves finish sooner than whole heads
         // (8 sequences of 512..8192 tokens: 567 -> 544 us, bound by the longest chain)
-        const int cus = device_cu_count();
         const bool split = 2 * heads <= cus || (a.cu != nullptr && a.N <= pf2::kSortMax && heads <= cus);
-        if (ws.seg) {   // two-segment carry: 3 kinds x 2 halves per head, then the corrections
-            e = launch_carry<1, 4, true>(args, 3 * heads, stream);
+        if (ws.nseg > 1) {
+            // segmented carry: pass 1 on whole-head workgroups (2 nseg - 3 per head), the
+            // entry states, pass 2 on half-head workgroups with a loader wave (2 (nseg - 1))
+            pf2::Ws w1 = ws, w2 = ws;
+            w1.pass = 1;
+            w2.pass = 2;
+            void* args1[] = {const_cast<PrefillArgs*>(&a), &w1};
+            void* args2[] = {const_cast<PrefillArgs*>(&a), &w2};
+            static_assert(CARRY_NTW == 1, "the first pass writes the state maps from one column tile per wave");
+            e = launch_carry<CARRY_NTW, CARRY_NW>(args1, (2 * ws.nseg - 3) * heads, stream);
             if (e != hipSuccess) return e;
-            const int nch = (a.L + pf2::C - 1) / pf2::C;
-            const int n2 = nch - nch / 2;   // a workgroup per second-segment chunk, two for the state
-            e = hipLaunchKernel(reinterpret_cast<const void*>(&pf2::seg_fix_kernel),
-                                dim3(static_cast<unsigned>(heads * (n2 + 2))), dim3(256), args, 0, stream);
+            e = hipLaunchKernel(reinterpret_cast<const void*>(&pf2::seg_chain_kernel),
+                                dim3(static_cast<unsigned>((heads + 7) / 8 * 64)), dim3(512), args1, 0, stream);
+            if (e != hipSuccess) return e;
+            e = launch_carry<1, 4, true>(args2, (ws.nseg - 1) * heads, stream);
         } else {
             e = split ? launch_carry<1, 4, true>(args, heads, stream) : launch_carry<CARRY_NTW, CARRY_NW>(args, heads, stream);
         }

@@ -101,11 +101,12 @@ def test_prefill_ragged_small():
     assert np.array_equal(got["conv_out"].float().cpu().numpy(), ref["conv_out"])
 
 
-@pytest.mark.parametrize("B,L", [(2, 150), (5, 130)], ids=["split_heads_B2", "whole_heads_B5"])
+@pytest.mark.parametrize("B,L", [(2, 150), (5, 130), (2, 800)], ids=["split_heads_B2", "whole_heads_B5", "segments_B2"])
 def test_prefill_carry_launch_paths(B, L):
     """The full 16/32-head, d = 128 shape unpacked: B = 2 (64 heads) runs the carry with two
-    workgroups per head and a loader wave; B = 5 (160 heads, more than half the CUs' worth of
-    half-head workgroups) runs whole-head workgroups of 8 waves."""
+    workgroups per head and a loader wave, and in 3 segments once it has 12 chunks (800
+    tokens); B = 5 (160 heads, more than half the CUs' worth of half-head workgroups) runs
+    whole-head workgroups of 8 waves."""
     shape, dtype = gi.QWEN, "bf16"
     _say(f"prefill carry path B={B} L={L}")
     inp = layer_inputs(shape, B, L, 14 + B, dtype, s0_std=0.1, conv_std=1.0)
@@ -323,18 +324,19 @@ def test_prefill_deterministic_and_ragged_equals_separate():
         if e - s <= 64:   # one chunk: the same carry as the packed call, bit for bit
             assert torch.equal(r["o"][0], a["o"][0, s:e])
             assert torch.equal(r["S"][0], a["S"][n])
-        else:             # a lone prompt of several chunks takes the two-segment carry
+        else:             # several chunks: the same results within tolerance
             assert rel_err(r["o"][0], a["o"][0, s:e].double().cpu().numpy()) <= TOL[dtype]
             assert rel_err(r["S"][0], a["S"][n].double().cpu().numpy()) <= TOL[dtype]
 
 
-@pytest.mark.parametrize("L", [65, 128, 129, 200, 448, 700])
-def test_prefill_two_segment_carry(L):
-    """A lone prompt (few heads, several chunks) runs the carry in two segments with
-    affine corrections; the packed path (one sequence through cu_seqlens) never does.
-    Both agree with the oracle, and with each other within tolerance."""
+@pytest.mark.parametrize("L", [65, 700, 768, 1000, 1300, 2000])
+def test_prefill_segmented_carry(L):
+    """A lone prompt of 4 heads runs the carry in segments once it has 12 chunks or more
+    (3 segments at 768 tokens, 4 at 1000 with a ragged last chunk, 5 at 1300, 8 at 2000;
+    one chain below that); the packed path (one sequence through cu_seqlens) never
+    does. Both agree with the oracle."""
     shape, dtype = SMALL128, "bf16"
-    _say(f"two-segment carry L={L}")
+    _say(f"segmented carry L={L}")
     inp = layer_inputs(shape, 1, L, 45, dtype, s0_std=0.1, conv_std=1.0)
     seg = run_prefill(shape, dtype, inp)
     packed = run_prefill(shape, dtype, inp, cu=gi.cu_seqlens([L]))
