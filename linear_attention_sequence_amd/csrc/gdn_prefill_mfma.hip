@@ -32,9 +32,9 @@
 //                  back as B operands without data movement by pairing the k
 //                  slots of the MFMA with the accumulator rows they hold. A lone
 //                  prompt with few heads runs in segments: a first pass (segment
-//                  0, and each middle segment's state map and zero-entry state),
-//                  seg_chain_kernel (the entry state of every later segment),
-//                  and a second pass over segments 1 .. nseg - 1.
+//                  0, and each middle segment's state map and zero-entry state)
+//                  and a second pass over segments 1 .. nseg - 1, whose workgroups
+//                  first form their entry states from those maps.
 #include <algorithm>
 
 #include "gdn_common.hpp"
@@ -79,9 +79,9 @@ struct Ws {
     _Float16* KT;   // [NC, Hk, D, C] keys of the chunk, transposed, tokens in k order
     float* coef;    // [NC, Hv, COEF]: exp(Gam_t), exp(Gam_last - Gam_t), exp(Gam_last), 2^uexp
     // segmented carry (see carry_kernel): the chunks of a sequence split into nseg segments
-    float* Sent;    // [nseg - 1, N, Hv, D, D] entry states of segments 1 .. nseg - 1
+    float* Sent;    // [N, Hv, D, D] entry state of segment 1
     _Float16* Mhl;  // [nseg - 2, N, Hv, 2, D, D] state maps of segments 1 .. nseg - 2 (S_end = M S_entry + R):
-                    // M = hi + lo, fp16 planes, column tile t scaled by 2^-Mexp[t]
+                    // M = hi + lo, fp16 planes, columns in k order, column tile t scaled by 2^-Mexp[t]
     int* Mexp;      // [nseg - 2, N, Hv, D / 16]
     float* Rseg;    // [nseg - 2, N, Hv, D, D] their end states from a zero entry state
     int nc_max;
@@ -150,7 +150,7 @@ static Ws layout(void* base, int B, int L, int N, int Hk, int Hv, bool ragged) {
     w.Mexp = nullptr;
     if (w.nseg > 1) {
         const size_t tiles = static_cast<size_t>(N) * Hv * D * D;
-        w.Sent = static_cast<float*>(take(static_cast<size_t>(w.nseg - 1) * tiles * 4));
+        w.Sent = static_cast<float*>(take(tiles * 4));
         w.Mhl = static_cast<_Float16*>(take(static_cast<size_t>(w.nseg - 2) * tiles * 2 * 2));
         w.Mexp = static_cast<int*>(take(static_cast<size_t>(w.nseg - 2) * N * Hv * (D / 16) * 4));
         w.Rseg = static_cast<float*>(take(static_cast<size_t>(w.nseg - 2) * tiles * 4));
@@ -913,9 +913,9 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
     // M_j S_entry + R_j. Pass 1 runs at once: FIRST, segment 0 from the entry state
     // with its outputs, ending in the entry state of segment 1; and for each middle
     // segment, LOCAL (from a zero state: R_j) and XMAP (the identity carried with
-    // U = 0: M_j), neither forming outputs. seg_chain_kernel then forms the entry
-    // state of every later segment, and pass 2 carries segments 1 .. nseg - 1 from
-    // their entry states with outputs; the last one ends in the final state.
+    // U = 0: M_j), neither forming outputs. Pass 2 carries segments 1 .. nseg - 1 with
+    // outputs, each from its entry state S_j = M_{j-1} S_{j-1} + R_{j-1}, which its
+    // workgroups form first on their own columns; the last one ends in the final state.
     const int NK = ws.nseg <= 1 ? 1 : (ws.pass == 1 ? 2 * ws.nseg - 3 : ws.nseg - 1);   // kinds per head
     // blockIdx -> (slice, slot): the NK * NS slices of a slot are dispatched together
     // and 8 blockIdx apart, i.e. on one XCD, sharing its L2 for the operands they
@@ -978,7 +978,7 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
             }
         } else {
             sj = kind + 1;
-            Sin = ws.Sent + static_cast<size_t>(sj - 1) * tiles + tile;
+            Sin = ws.Sent + tile;                        // S_1; later entry states are formed below
             if (sj != ws.nseg - 1) Send = nullptr;
         }
     }
@@ -1016,10 +1016,115 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
             else issue_stage<CPW, NW, ST_W | ST_KT | ST_CF>(a, ws, id, tok, nt, h, hk, ucol0, buf, w, lane);
         }
     };
-    if ((!LW || loader) && cb < ce) {
+    const bool prologue = LW && NTW == 1 && ws.nseg > 1 && ws.pass == 2 && sj >= 2;   // see below
+    if ((!LW || loader) && cb < ce && !prologue) {
 #pragma unroll
         for (int w = LW ? 0 : wave; w < (LW ? NW : wave + 1); ++w)
             issue_all(base + cb, row_tok + static_cast<size_t>(cb) * C, min(C, seg.len - cb * C), 0, w);
+    }
+    // Segmented mode, pass 2: segment sj >= 2 enters with S_sj = M_{sj-1} S_{sj-1} + R_{sj-1}
+    // from S_1, formed here on this workgroup's columns before its first chunk. The maps
+    // (fp16 hi + lo planes, columns in k order, scaled per 16-column tile) stream into the
+    // two stage buffers, the next one loading during the current product; the first
+    // chunk's stage is issued once they are done with. The products split both operands
+    // (hi*hi + hi*lo + lo*hi in fp32, close to an fp32 product), so these entry states
+    // are as good as a carried one.
+    const int np = (ws.nseg > 1 && ws.pass == 2) ? sj - 1 : 0;
+    if constexpr (LW && NTW == 1) {
+        if (np > 0) {
+            if (loader) {
+                for (int i = 0; i < np; ++i) {
+                    __syncthreads();                        // map i is in LDS
+                    __syncthreads();                        // every compute wave is done with it
+                }
+                if (cb < ce)
+#pragma unroll
+                    for (int w = 0; w < NW; ++w)
+                        issue_all(base + cb, row_tok + static_cast<size_t>(cb) * C, min(C, seg.len - cb * C), 0, w);
+            } else {
+                __shared__ int s_ek[kMaxSeg - 2][D / 16];
+                static_assert(2 * D * D * 2 <= SG::BYTES, "a map fits a stage buffer");
+                const size_t nhh = static_cast<size_t>(a.N) * a.Hv, head = static_cast<size_t>(n) * a.Hv + h;
+                if (tid < np * (D / 16))
+                    s_ek[tid / (D / 16)][tid % (D / 16)] =
+                        ws.Mexp[(static_cast<size_t>(tid / (D / 16)) * nhh + head) * (D / 16) + tid % (D / 16)];
+                // map i -> stage buffer (i - 1) & 1 as [hi rows, lo rows][16 granules], granule j of
+                // row r at position j ^ (r % 16): wave-wide 1 KB loads of 4 rows, this wave's
+                // instructions wave, wave + NW, ... (16 each)
+                constexpr int MI = 2 * D / 4 / NW;
+                auto issue_map = [&](int i) {
+                    const _Float16* src = ws.Mhl + (static_cast<size_t>(i - 1) * nhh + head) * 2 * D * D;
+                    unsigned char* dst = g_stage + ((i - 1) & 1) * SG::BYTES;
+#pragma unroll
+                    for (int k = 0; k < MI; ++k) {
+                        const int q = wave + NW * k, r = 4 * q + (lane >> 4), jg = (lane & 15) ^ (r & 15);
+                        __builtin_amdgcn_global_load_lds(src + r * D + 8 * jg, dst + q * 1024, 16, 0, 0);
+                    }
+                };
+                issue_map(1);
+                if (np >= 2) issue_map(2);
+                for (int i = 1; i <= np; ++i) {
+                    // map i has landed (this wave's part; map i + 1 may still be in flight)
+                    static_assert(MI == 16, "the wait below counts one map's instructions per wave");
+                    if (i + 1 <= np) __builtin_amdgcn_s_waitcnt((16 >> 4) << 14 | 0x7 << 4 | 0xF << 8);
+                    else __builtin_amdgcn_s_waitcnt(0x7 << 4 | 0xF << 8);
+                    __syncthreads();                        // ... and every wave's
+                    const unsigned char* mb = g_stage + ((i - 1) & 1) * SG::BYTES;
+                    float R[8][4];                          // R_i at this lane's accumulator positions
+                    const float* Rg = ws.Rseg + (static_cast<size_t>(i - 1) * nhh + head) * D * D;
+                    int ro = 4 * g * D + col0 + r16;
+                    asm volatile("" : "+v"(ro));            // formed here, not kept live from outside the loop
+#pragma unroll
+                    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) R[mt][e] = Rg[ro + (16 * mt + e) * D];
+                    // B operands: the state's rows scaled by their map column tile's 2^e, into fp16 range
+                    float sm = 0.f;
+#pragma unroll
+                    for (int mt = 0; mt < 8; ++mt) {
+                        const float sk = ldexpf(1.f, s_ek[i - 1][mt]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            S[mt][0][e] *= sk;
+                            sm = fmaxf(sm, fabsf(S[mt][0][e]));
+                        }
+                    }
+                    const int eP = pow2_exponent(wave_max_nonneg(sm));
+                    const float sP = ldexpf(1.f, -eP), sc = ldexpf(1.f, eP);
+                    f16x8 bh[4], bl[4];
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const float x = S[2 * ks + (e >> 2)][0][e & 3] * sP;
+                            bh[ks][e] = static_cast<_Float16>(x);
+                            bl[ks][e] = static_cast<_Float16>(x - static_cast<float>(bh[ks][e]));
+                        }
+#pragma unroll
+                    for (int mt = 0; mt < 8; ++mt) {
+                        f32x4v acc = f32x4v{0, 0, 0, 0};
+#pragma unroll
+                        for (int ks = 0; ks < 4; ++ks) {
+                            const int row = 16 * mt + r16, pos = (4 * ks + g) ^ r16;
+                            const f16x8 ah = *reinterpret_cast<const f16x8*>(mb + (row * 16 + pos) * 16);
+                            const f16x8 al = *reinterpret_cast<const f16x8*>(mb + ((row + D) * 16 + pos) * 16);
+                            acc = mfma16x16x32(ah, bh[ks], acc);
+                            acc = mfma16x16x32(ah, bl[ks], acc);
+                            acc = mfma16x16x32(al, bh[ks], acc);
+                        }
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) S[mt][0][e] = __fmaf_rn(acc[e], sc, R[mt][e]);
+                    }
+                    __syncthreads();                        // every wave is done with map i
+                    if (i + 2 <= np) issue_map(i + 2);      // into the buffer just freed
+                }
+                smax = 0.f;
+#pragma unroll
+                for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) smax = fmaxf(smax, fabsf(S[mt][0][e]));
+            }
+        }
     }
     if (loader) {   // stage c + 1 is issued after the barrier that frees its buffer
         for (int c = cb; c < ce; ++c) {
@@ -1263,7 +1368,8 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
     }
     // end state: S, or in segmented mode an entry state, R_j or M_j (or nothing). M_j
     // goes out split into fp16 high and low parts scaled per 16-column tile (a wave's
-    // columns), staged through LDS into row-major planes.
+    // columns), staged through LDS into row-major planes with the columns in k order
+    // (the order in which a state's accumulator tiles act as B operands).
     if constexpr (!LW && NTW == 1) {
         if (mapo != 0) {
             const size_t m = mapo - 1;                   // (segment, sequence, head) of the map
@@ -1279,8 +1385,8 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
                 for (int e = 0; e < 4; ++e) {
                     const float x = S[mt][0][e] * sC;
                     const _Float16 hi = static_cast<_Float16>(x);
-                    lh[(16 * mt + 4 * g + e) * MS + col0 + r16] = hi;
-                    ll[(16 * mt + 4 * g + e) * MS + col0 + r16] = static_cast<_Float16>(x - static_cast<float>(hi));
+                    lh[(16 * mt + 4 * g + e) * MS + kpos(col0 + r16)] = hi;
+                    ll[(16 * mt + 4 * g + e) * MS + kpos(col0 + r16)] = static_cast<_Float16>(x - static_cast<float>(hi));
                 }
             if (lane == 0) ws.Mexp[m * (D / 16) + col0 / 16] = eC;
             __syncthreads();
@@ -1301,117 +1407,6 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
                 for (int e = 0; e < 4; ++e)
                     __builtin_nontemporal_store(S[mt][nt][e], Send + (16 * mt + 4 * g + e) * D + col0 + 16 * nt + r16);
     }
-}
-
-// Entry states of the segmented carry: S_1 (the first pass's end state of segment 0)
-// and, for j = 1 .. nseg - 2, S_{j+1} = M_j S_j + R_j. The columns of a state evolve
-// independently, so a workgroup owns 16 columns of one (sequence, head) and chains
-// them through every segment; the 8 column blocks of a head are dispatched 8 apart,
-// i.e. on one XCD. The products run on fp16 MFMA with both operands split into a high
-// and a low fp16 part (x = hi + lo after a power-of-two scale into fp16's range: 22
-// significant bits) and hi*hi + hi*lo + lo*hi accumulated in fp32, close to an fp32
-// product, so the chain does not degrade the entry states of later segments. The maps
-// come split already (scaled per 16-column tile, which is undone on the rows of S_j
-// it multiplies). Wave w forms rows 16 w .. 16 w + 15 of every product: its rows of
-// the maps are A operands held in registers, loaded CHPF maps ahead (the products
-// are short and each depends on the last, so the load latency is paid about once),
-// and the block (in LDS, transposed) gives the B operands.
-constexpr int CBS = D + 4;   // row stride (floats) of a transposed column block
-constexpr int CHPF = 3;      // maps in flight per wave
-__global__ __launch_bounds__(512) void seg_chain_kernel(PrefillArgs a, Ws ws) {
-    __shared__ __align__(16) float blk[2][16 * CBS];
-    const int heads = a.N * a.Hv;
-    const int cbk = (blockIdx.x % 64) / 8, hd = 8 * (blockIdx.x / 64) + blockIdx.x % 8;
-    if (hd >= heads) return;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int g = lane >> 4, r16 = lane & 15;
-    const size_t tiles = static_cast<size_t>(heads) * D * D, tile = static_cast<size_t>(hd) * D * D;
-    const int cw = 16 * cbk + r16;                       // this lane's column (B operand, accumulator)
-    const int nprod = ws.nseg - 2;
-    // A operands: row 16 wave + r16, k = 32 ks + 8 g + 0..7, both planes; R at the
-    // accumulator positions (rows 16 wave + 4 g + e, column cw)
-    f16x8 mh[CHPF][4], ml[CHPF][4];
-    float rv[CHPF][4];
-#define GDN_CHAIN_LOAD(J, SL)                                                                          \
-    do {                                                                                               \
-        const size_t m_ = static_cast<size_t>((J) - 1) * heads + hd;                                   \
-        const _Float16* Mh_ = ws.Mhl + m_ * 2 * D * D + static_cast<size_t>(16 * wave + r16) * D + 8 * g; \
-        const float* R_ = ws.Rseg + m_ * D * D;                                                        \
-        _Pragma("unroll") for (int ks = 0; ks < 4; ++ks) {                                             \
-            mh[SL][ks] = *reinterpret_cast<const f16x8*>(Mh_ + 32 * ks);                               \
-            ml[SL][ks] = *reinterpret_cast<const f16x8*>(Mh_ + D * D + 32 * ks);                       \
-        }                                                                                              \
-        _Pragma("unroll") for (int e = 0; e < 4; ++e)                                                  \
-            rv[SL][e] = R_[static_cast<size_t>(16 * wave + 4 * g + e) * D + cw];                       \
-    } while (0)
-    // S_1's block first (the loads return in order), then the first maps
-    const int row1 = tid >> 2, q1 = tid & 3;   // thread -> row tid / 4, columns 4 (tid % 4) ..
-    const float4 s1 = *reinterpret_cast<const float4*>(ws.Sent + tile + static_cast<size_t>(row1) * D + 16 * cbk + 4 * q1);
-#pragma unroll
-    for (int u = 0; u < CHPF; ++u)
-        if (u < nprod) GDN_CHAIN_LOAD(1 + u, u);
-    blk[0][(4 * q1 + 0) * CBS + row1] = s1.x;   // transposed into LDS
-    blk[0][(4 * q1 + 1) * CBS + row1] = s1.y;
-    blk[0][(4 * q1 + 2) * CBS + row1] = s1.z;
-    blk[0][(4 * q1 + 3) * CBS + row1] = s1.w;
-    for (int j0 = 1; j0 <= nprod; j0 += CHPF) {
-#pragma unroll
-        for (int u = 0; u < CHPF; ++u) {
-            const int j = j0 + u;
-            if (j > nprod) break;
-            float* Snext = ws.Sent + static_cast<size_t>(j) * tiles + tile;
-            const int* ek = ws.Mexp + (static_cast<size_t>(j - 1) * heads + hd) * (D / 16);
-            __syncthreads();   // S_j's block is in blk[(j - 1) & 1]
-            const float* cur = blk[(j - 1) & 1] + r16 * CBS;
-            float* nxt = blk[j & 1] + r16 * CBS;
-            // B operands: S_j[k][cw] 2^(e of k's column tile of M_j), k = 32 ks + 8 g + 0..7
-            float bv[4][8];
-            float smax = 0.f;
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const float sk = ldexpf(1.f, (g >> 1) ? ek[2 * ks + 1] : ek[2 * ks]);
-                const float4 lo = *reinterpret_cast<const float4*>(cur + 32 * ks + 8 * g);
-                const float4 hi = *reinterpret_cast<const float4*>(cur + 32 * ks + 8 * g + 4);
-                const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    bv[ks][e] = v[e] * sk;
-                    smax = fmaxf(smax, fabsf(bv[ks][e]));
-                }
-            }
-            const int eS = pow2_exponent(wave_max_nonneg(smax));
-            const float sS = ldexpf(1.f, -eS);
-            f32x4v acc = f32x4v{0, 0, 0, 0};
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                f16x8 bh, bl;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float x = bv[ks][e] * sS;
-                    bh[e] = static_cast<_Float16>(x);
-                    bl[e] = static_cast<_Float16>(x - static_cast<float>(bh[e]));
-                }
-                acc = mfma16x16x32(mh[u][ks], bh, acc);
-                acc = mfma16x16x32(mh[u][ks], bl, acc);
-                acc = mfma16x16x32(ml[u][ks], bh, acc);
-            }
-            const float sc = ldexpf(1.f, eS);
-            const int row0 = 16 * wave + 4 * g;          // lane: rows row0 .. row0 + 3, column cw
-            float4 o;
-            o.x = __fmaf_rn(acc[0], sc, rv[u][0]);
-            o.y = __fmaf_rn(acc[1], sc, rv[u][1]);
-            o.z = __fmaf_rn(acc[2], sc, rv[u][2]);
-            o.w = __fmaf_rn(acc[3], sc, rv[u][3]);
-            if (j + CHPF <= nprod) GDN_CHAIN_LOAD(j + CHPF, u);   // this slot's next map
-            *reinterpret_cast<float4*>(nxt + row0) = o;
-            __builtin_nontemporal_store(o.x, Snext + static_cast<size_t>(row0) * D + cw);
-            __builtin_nontemporal_store(o.y, Snext + static_cast<size_t>(row0 + 1) * D + cw);
-            __builtin_nontemporal_store(o.z, Snext + static_cast<size_t>(row0 + 2) * D + cw);
-            __builtin_nontemporal_store(o.w, Snext + static_cast<size_t>(row0 + 3) * D + cw);
-        }
-    }
-#undef GDN_CHAIN_LOAD
 }
 
 }  // namespace pf2
@@ -1484,8 +1479,9 @@ static hipError_t launch_mfma_t(const PrefillArgs& a, int in_dtype, hipStream_t 
         // (8 sequences of 512..8192 tokens: 567 -> 544 us, bound by the longest chain)
         const bool split = 2 * heads <= cus || (a.cu != nullptr && a.N <= pf2::kSortMax && heads <= cus);
         if (ws.nseg > 1) {
-            // segmented carry: pass 1 on whole-head workgroups (2 nseg - 3 per head), the
-            // entry states, pass 2 on half-head workgroups with a loader wave (2 (nseg - 1))
+            // segmented carry: pass 1 on whole-head workgroups (2 nseg - 3 per head), pass 2
+            // (which forms the later entry states itself) on half-head workgroups with a
+            // loader wave (2 (nseg - 1) per head)
             pf2::Ws w1 = ws, w2 = ws;
             w1.pass = 1;
             w2.pass = 2;
@@ -1493,9 +1489,6 @@ static hipError_t launch_mfma_t(const PrefillArgs& a, int in_dtype, hipStream_t 
             void* args2[] = {const_cast<PrefillArgs*>(&a), &w2};
             static_assert(CARRY_NTW == 1, "the first pass writes the state maps from one column tile per wave");
             e = launch_carry<CARRY_NTW, CARRY_NW>(args1, (2 * ws.nseg - 3) * heads, stream);
-            if (e != hipSuccess) return e;
-            e = hipLaunchKernel(reinterpret_cast<const void*>(&pf2::seg_chain_kernel),
-                                dim3(static_cast<unsigned>((heads + 7) / 8 * 64)), dim3(512), args1, 0, stream);
             if (e != hipSuccess) return e;
             e = launch_carry<1, 4, true>(args2, (ws.nseg - 1) * heads, stream);
         } else {
