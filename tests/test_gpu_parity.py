@@ -134,10 +134,14 @@ def test_prefill_ragged_many_sequences():
     assert np.array_equal(got["conv_out"].float().cpu().numpy(), ref["conv_out"])
 
 
-def test_prefill_long_memory():
-    """Weak decay (gate scaled by 0.01) so early errors do not fade; beta near 1."""
+@pytest.mark.parametrize("L", [512, 2000], ids=["one_chain", "eight_segments"])
+def test_prefill_long_memory(L):
+    """Weak decay (gate scaled by 0.01) so early errors do not fade; beta near 1. At 2000
+    tokens the carry runs in 8 segments, whose state maps then stay far from zero and whose
+    entry states are chained through up to 6 maps."""
     shape, dtype = SMALL128, "bf16"
-    inp = layer_inputs(shape, 1, 512, 13, dtype, s0_std=0.1, conv_std=1.0)
+    _say(f"long memory L={L}")
+    inp = layer_inputs(shape, 1, L, 13, dtype, s0_std=0.1, conv_std=1.0)
     inp["gate"] = gi.round_to(0.01 * inp["gate"].astype(np.float64), dtype)
     inp["beta"] = gi.round_to(0.5 + 0.5 * inp["beta"].astype(np.float64), dtype)
     got = run_prefill(shape, dtype, inp)
