@@ -82,7 +82,7 @@ struct Ws {
     float* Sent;    // [N, Hv, D, D] entry state of segment 1
     _Float16* Mhl;  // [nseg - 2, N, Hv, 2, D, D] state maps of segments 1 .. nseg - 2 (S_end = M S_entry + R):
                     // M = hi + lo, fp16 planes, columns in k order, column tile t scaled by 2^-Mexp[t]
-    int* Mexp;      // [nseg - 2, N, Hv, D / 16]
+    int* Mexp;      // [nseg - 2, N, Hv, D / 16] (kZeroTile: the tile is exactly zero)
     float* Rseg;    // [nseg - 2, N, Hv, D, D] their end states from a zero entry state
     int nc_max;
     int nseg;       // segments per sequence (1: one chain per sequence)
@@ -875,6 +875,7 @@ __device__ __forceinline__ void issue_stage(const PrefillArgs& a, const Ws& ws, 
 }
 
 constexpr int kSortMax = 256;   // packed sequences ranked by length in every carry workgroup
+constexpr int kZeroTile = -(1 << 20);   // state-map tile exponent marking a tile that is exactly zero
 
 // Sequence of rank r when the N packed sequences are ordered by decreasing length
 // (ties by index). Every thread ranks up to N / blockDim of them against all N.
@@ -965,6 +966,7 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
     const float* Sin = a.S + tile;
     float* Send = a.S + tile;
     size_t mapo = 0;                                     // XMAP: its map's offset in Mhl, Mexp (+ 1)
+    int m0 = 0;                                          // pass 2: maps 1 .. m0 are not needed
     if (ws.nseg > 1) {
         if (ws.pass == 1) {
             if (kind == 0) {
@@ -980,6 +982,19 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
             sj = kind + 1;
             Sin = ws.Sent + tile;                        // S_1; later entry states are formed below
             if (sj != ws.nseg - 1) Send = nullptr;
+            // A segment whose state map is exactly zero (it has decayed below fp32's range)
+            // ends in R whatever its entry state: the chain restarts after the latest one,
+            // with the same result, bit for bit, as multiplying through it.
+            for (int i = sj - 1; i >= 1 && m0 == 0; --i) {
+                const int* ek = ws.Mexp + (static_cast<size_t>(i - 1) * a.N * a.Hv + n * a.Hv + h) * (D / 16);
+                bool zero = true;
+#pragma unroll
+                for (int t = 0; t < D / 16; ++t) zero = zero && ek[t] == kZeroTile;
+                if (zero) {
+                    m0 = i;
+                    Sin = ws.Rseg + static_cast<size_t>(i - 1) * tiles + tile;
+                }
+            }
         }
     }
     const int cb = ws.nseg > 1 ? seg_begin(nch, ws.nseg, sj) : 0;
@@ -1016,20 +1031,21 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
             else issue_stage<CPW, NW, ST_W | ST_KT | ST_CF>(a, ws, id, tok, nt, h, hk, ucol0, buf, w, lane);
         }
     };
-    const bool prologue = LW && NTW == 1 && ws.nseg > 1 && ws.pass == 2 && sj >= 2;   // see below
+    const int np = (ws.nseg > 1 && ws.pass == 2) ? sj - 1 - m0 : 0;   // maps m0 + 1 .. sj - 1 (see below)
+    const bool prologue = LW && NTW == 1 && np > 0;
     if ((!LW || loader) && cb < ce && !prologue) {
 #pragma unroll
         for (int w = LW ? 0 : wave; w < (LW ? NW : wave + 1); ++w)
             issue_all(base + cb, row_tok + static_cast<size_t>(cb) * C, min(C, seg.len - cb * C), 0, w);
     }
     // Segmented mode, pass 2: segment sj >= 2 enters with S_sj = M_{sj-1} S_{sj-1} + R_{sj-1}
-    // from S_1, formed here on this workgroup's columns before its first chunk. The maps
+    // from S_{m0+1} (S_1, or R_m0 after a zero map), formed here on this workgroup's columns
+    // before its first chunk. The maps
     // (fp16 hi + lo planes, columns in k order, scaled per 16-column tile) stream into the
     // two stage buffers, the next one loading during the current product; the first
     // chunk's stage is issued once they are done with. The products split both operands
     // (hi*hi + hi*lo + lo*hi in fp32, close to an fp32 product), so these entry states
     // are as good as a carried one.
-    const int np = (ws.nseg > 1 && ws.pass == 2) ? sj - 1 : 0;
     if constexpr (LW && NTW == 1) {
         if (np > 0) {
             if (loader) {
@@ -1047,13 +1063,13 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
                 const size_t nhh = static_cast<size_t>(a.N) * a.Hv, head = static_cast<size_t>(n) * a.Hv + h;
                 if (tid < np * (D / 16))
                     s_ek[tid / (D / 16)][tid % (D / 16)] =
-                        ws.Mexp[(static_cast<size_t>(tid / (D / 16)) * nhh + head) * (D / 16) + tid % (D / 16)];
-                // map i -> stage buffer (i - 1) & 1 as [hi rows, lo rows][16 granules], granule j of
+                        ws.Mexp[(static_cast<size_t>(m0 + tid / (D / 16)) * nhh + head) * (D / 16) + tid % (D / 16)];
+                // map m0 + i -> stage buffer (i - 1) & 1 as [hi rows, lo rows][16 granules], granule j of
                 // row r at position j ^ (r % 16): wave-wide 1 KB loads of 4 rows, this wave's
                 // instructions wave, wave + NW, ... (16 each)
                 constexpr int MI = 2 * D / 4 / NW;
                 auto issue_map = [&](int i) {
-                    const _Float16* src = ws.Mhl + (static_cast<size_t>(i - 1) * nhh + head) * 2 * D * D;
+                    const _Float16* src = ws.Mhl + (static_cast<size_t>(m0 + i - 1) * nhh + head) * 2 * D * D;
                     unsigned char* dst = g_stage + ((i - 1) & 1) * SG::BYTES;
 #pragma unroll
                     for (int k = 0; k < MI; ++k) {
@@ -1070,8 +1086,8 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
                     else __builtin_amdgcn_s_waitcnt(0x7 << 4 | 0xF << 8);
                     __syncthreads();                        // ... and every wave's
                     const unsigned char* mb = g_stage + ((i - 1) & 1) * SG::BYTES;
-                    float R[8][4];                          // R_i at this lane's accumulator positions
-                    const float* Rg = ws.Rseg + (static_cast<size_t>(i - 1) * nhh + head) * D * D;
+                    float R[8][4];                          // R_{m0+i} at this lane's accumulator positions
+                    const float* Rg = ws.Rseg + (static_cast<size_t>(m0 + i - 1) * nhh + head) * D * D;
                     int ro = 4 * g * D + col0 + r16;
                     asm volatile("" : "+v"(ro));            // formed here, not kept live from outside the loop
 #pragma unroll
@@ -1388,7 +1404,7 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
                     lh[(16 * mt + 4 * g + e) * MS + kpos(col0 + r16)] = hi;
                     ll[(16 * mt + 4 * g + e) * MS + kpos(col0 + r16)] = static_cast<_Float16>(x - static_cast<float>(hi));
                 }
-            if (lane == 0) ws.Mexp[m * (D / 16) + col0 / 16] = eC;
+            if (lane == 0) ws.Mexp[m * (D / 16) + col0 / 16] = smax > 0.f ? eC : kZeroTile;
             __syncthreads();
             _Float16* dst = ws.Mhl + m * 2 * D * D;
             for (int q = tid; q < 2 * D * (D / 8); q += NW * 64) {   // 16-byte granules of both planes
