@@ -81,15 +81,20 @@ __device__ __forceinline__ float sigmoid_hw(float x) {
 // gate and beta of V head h at flat index idx, with the optional prologue
 // gate = -exp(A_log[h]) softplus(a + dt_bias[h]), beta = sigmoid(b) when A_log is set
 // (then `gate`/`beta` hold the raw a/b).
+// The same map from values already loaded: raw a, b and the head's A_log, dt_bias.
+__device__ __forceinline__ void gate_beta_of(float a, float b, float A_log, float dt_bias, float* g, float* bt) {
+    *g = -exp_hw(A_log) * softplus_hw(a + dt_bias);
+    *bt = sigmoid_hw(b);
+}
+
 template <typename Tin>
 __device__ __forceinline__ void gate_beta_at(const void* gate, const void* beta, const void* A_log,
                                              const void* dt_bias, size_t idx, int h, float* g, float* b) {
     float gv = to_f32(static_cast<const Tin*>(gate)[idx]);
     float bv = to_f32(static_cast<const Tin*>(beta)[idx]);
     if (A_log != nullptr) {
-        gv = -exp_hw(to_f32(static_cast<const Tin*>(A_log)[h])) *
-             softplus_hw(gv + to_f32(static_cast<const Tin*>(dt_bias)[h]));
-        bv = sigmoid_hw(bv);
+        gate_beta_of(gv, bv, to_f32(static_cast<const Tin*>(A_log)[h]), to_f32(static_cast<const Tin*>(dt_bias)[h]),
+                     &gv, &bv);
     }
     *g = gv;
     *b = bv;

@@ -141,8 +141,6 @@ __device__ __forceinline__ void recur_tail(const RecArgs& a, const Unit& u, cons
     const int cg = tid % CG, rg = tid / CG;
     const int lane = tid % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform
-    const Tin* gate = static_cast<const Tin*>(a.gate);
-    const Tin* beta = static_cast<const Tin*>(a.beta);
     const float qscale = 1.0f / sqrtf(static_cast<float>(DK));
     for (int t = wave; t < T; t += NW) {
         float qq = 0.f, kk = 0.f, kq = 0.f;
@@ -162,19 +160,7 @@ __device__ __forceinline__ void recur_tail(const RecArgs& a, const Unit& u, cons
             L.sq[t * DK + i] *= qs;
             L.sk[t * DK + i] *= rk;
         }
-        if (lane == 0) {
-            const size_t gi = (static_cast<size_t>(u.b) * T + t) * a.Hv + u.h;
-            float gv, bv;
-            if constexpr (PRO) {
-                gate_beta_at<Tin>(gate, beta, a.fu.A_log, a.fu.dt_bias, gi, u.h, &gv, &bv);
-            } else {
-                gv = to_f32(gate[gi]);
-                bv = to_f32(beta[gi]);
-            }
-            L.s_alpha[t] = expf(gv);
-            L.s_beta[t] = bv;
-            L.s_kq[t] = kq * rk * qs;
-        }
+        if (lane == 0) L.s_kq[t] = kq * rk * qs;
     }
     __syncthreads();
 
@@ -274,6 +260,21 @@ __global__ __launch_bounds__(NT) void recurrent_kernel(RecArgs a) {
     float4 s[G::RPT];
     load_tile<DK, DV, NT, CW, NT_LOAD>(a, u, s);
 
+    // gate and beta of token t = threadIdx.x, issued right behind the tile: their round trip
+    // then overlaps the tile's instead of following the conv barrier, where it held up the
+    // whole workgroup (the prologue's per-head A_log and dt_bias likewise)
+    const int tg = threadIdx.x;
+    float g_in = 0.f, b_in = 0.f, alog_in = 0.f, dtb_in = 0.f;
+    if (tg < T) {
+        const size_t gi = (static_cast<size_t>(u.b) * T + tg) * a.Hv + u.h;
+        g_in = to_f32(static_cast<const Tin*>(a.gate)[gi]);
+        b_in = to_f32(static_cast<const Tin*>(a.beta)[gi]);
+        if constexpr (PRO) {
+            alog_in = to_f32(static_cast<const Tin*>(a.fu.A_log)[u.h]);
+            dtb_in = to_f32(static_cast<const Tin*>(a.fu.dt_bias)[u.h]);
+        }
+    }
+
     // 2. conv + SiLU of this unit's channels for every token of the block
     const Tin* x = static_cast<const Tin*>(a.qkv);
     const Tin* w = static_cast<const Tin*>(a.w);
@@ -317,6 +318,12 @@ __global__ __launch_bounds__(NT) void recurrent_kernel(RecArgs a) {
             const float zv = to_f32(z[((static_cast<size_t>(u.b) * T + t) * a.Hv + u.h) * DV + u.j0 + j]);
             L.s_gz[i] = to_f32(nw[u.j0 + j]) * (zv * sigmoid_hw(zv));
         }
+    }
+    if (tg < T) {
+        float gv = g_in, bv = b_in;
+        if constexpr (PRO) gate_beta_of(g_in, b_in, alog_in, dtb_in, &gv, &bv);
+        L.s_alpha[tg] = expf(gv);
+        L.s_beta[tg] = bv;
     }
     __syncthreads();
     recur_tail<Tin, DK, DV, NT, CW, NT_STORE, PRO, EPI>(a, u, L, T, s);
