@@ -221,6 +221,50 @@ __global__ __launch_bounds__(256) void front_kernel(PrefillArgs a, Ws ws) {
     const int ch0 = u * D;   // [Q | K | V] blocks of D channels
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const Tin* x = static_cast<const Tin*>(a.qkv) + (static_cast<size_t>(row) * a.D + ch0) * a.L;
+    const bool is_q = u < a.Hk, is_k = !is_q && u < 2 * a.Hk;
+
+    // Interior tiles of unpacked bf16 rows whose length is a multiple of 8 (so that every
+    // 8-token group is 16-byte aligned): each lane loads 8 tokens of a channel and the 4
+    // tokens before them in two vector loads and runs the conv in registers. Every window
+    // lies inside the row and no sequence ends in the tile, so there is no masking and no
+    // conv-state update.
+    const bool vec = sizeof(Tin) == 2 && a.cu == nullptr && a.L % 8 == 0 && p0 > 0 && p0 + TT < a.L &&
+                     (reinterpret_cast<uintptr_t>(a.qkv) & 15) == 0 && (reinterpret_cast<uintptr_t>(a.w) & 7) == 0;
+    if (vec) {
+        static_assert(TT == 32 && D == 128, "4 lanes of 8 tokens per channel, 16 channels per instruction");
+        const int lq = lane >> 2, g = lane & 3;
+        const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
+        const uint16_t* wb = reinterpret_cast<const uint16_t*>(a.w);
+        uint4 xr[2];
+        uint2 hr[2], wr[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int cc = (wave * 2 + i) * 16 + lq;
+            const uint16_t* xp = xb + static_cast<size_t>(cc) * a.L + p0 + 8 * g;
+            xr[i] = *reinterpret_cast<const uint4*>(xp);
+            hr[i] = *reinterpret_cast<const uint2*>(xp - 4);
+            wr[i] = *reinterpret_cast<const uint2*>(wb + static_cast<size_t>(ch0 + cc) * kConvK);
+        }
+        const auto lo = [](unsigned v) { return __uint_as_float(v << 16); };
+        const auto hi = [](unsigned v) { return __uint_as_float(v & 0xffff0000u); };
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int cc = (wave * 2 + i) * 16 + lq;
+            const float xv[11] = {hi(hr[i].x), lo(hr[i].y), hi(hr[i].y),
+                                  lo(xr[i].x), hi(xr[i].x), lo(xr[i].y), hi(xr[i].y),
+                                  lo(xr[i].z), hi(xr[i].z), lo(xr[i].w), hi(xr[i].w)};
+            const float w0 = lo(wr[i].x), w1 = hi(wr[i].x), w2 = lo(wr[i].y), w3 = hi(wr[i].y);
+            const int cpos = is_q || is_k ? kpos(cc) : cc;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                float acc = w0 * xv[j];
+                acc = __fmaf_rn(w1, xv[j + 1], acc);
+                acc = __fmaf_rn(w2, xv[j + 2], acc);
+                acc = __fmaf_rn(w3, xv[j + 3], acc);
+                buf[(8 * g + j) * (D + 1) + cpos] = fast_silu(acc);
+            }
+        }
+    } else {
 
     // a wave loads TT consecutive tokens of 64 / TT channels per instruction
     // (coalesced); the 3 tokens before the tile (3 x 128 values) come from two
@@ -372,11 +416,11 @@ __global__ __launch_bounds__(256) void front_kernel(PrefillArgs a, Ws ws) {
         }
     }
     __syncthreads();
-    const bool is_q = u < a.Hk, is_k = !is_q && u < 2 * a.Hk;
     // q and k channels are placed in k order here (the norms below do not depend on the order)
     const int cpos = is_q || is_k ? kpos(c) : c;
 #pragma unroll
     for (int j = 0; j < TT / 2; ++j) buf[(th * (TT / 2) + j) * (D + 1) + cpos] = y[j];
+    }
     __syncthreads();
     // per-token sum of squares: thread (token tid % TT, channel part tid / TT)
     // reads its part column-wise (lanes run along tokens: conflict-free)
@@ -420,7 +464,7 @@ __global__ __launch_bounds__(256) void front_kernel(PrefillArgs a, Ws ws) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] = static_cast<_Float16>(buf[t * (D + 1) + 8 * j + e] * r);
             const size_t tok = static_cast<size_t>(row) * a.L + p0 + t;
-            if (s_n[t] >= 0) *reinterpret_cast<f16x8*>(base + tok * hs * D + 8 * j) = v;
+            if (vec || s_n[t] >= 0) *reinterpret_cast<f16x8*>(base + tok * hs * D + 8 * j) = v;
         }
     }
 }
