@@ -58,7 +58,9 @@ def layer_inputs(shape: gi.Shape, B: int, L: int, seed: int, dtype: str, N=None,
     )
 
 
-def run_prefill(shape, dtype, inp, cu=None):
+def run_prefill(shape, dtype, inp, cu=None, qkv_offset=0):
+    """qkv_offset > 0 places qkv that many elements into a larger buffer (so its address
+    is only element-aligned)."""
     p = params(shape, dtype)
     B, D, L = inp["qkv"].shape
     N = inp["S0"].shape[0]
@@ -66,7 +68,12 @@ def run_prefill(shape, dtype, inp, cu=None):
     o = torch.zeros((B, L, shape.Hv, shape.dv), dtype=torch.float32, device="cuda")
     cout = torch.zeros_like(dev(inp["conv0"], dtype))
     ws = gdn.prefill_workspace(p, B, L, N)
-    gdn.gdn_prefill(p, dev(inp["qkv"], dtype), dev(inp["gate"], dtype), dev(inp["beta"], dtype),
+    x = dev(inp["qkv"], dtype)
+    if qkv_offset:
+        buf = torch.zeros(x.numel() + qkv_offset, dtype=x.dtype, device="cuda")
+        buf[qkv_offset:].copy_(x.reshape(-1))
+        x = buf[qkv_offset:].view(x.shape)
+    gdn.gdn_prefill(p, x, dev(inp["gate"], dtype), dev(inp["beta"], dtype),
                     dev(inp["w"], dtype), dev(inp["conv0"], dtype), cout, S, o, ws,
                     cu_seqlens=None if cu is None else dev(np.asarray(cu, np.int32)))
     torch.cuda.synchronize()

@@ -352,6 +352,25 @@ def test_prefill_segmented_carry(L):
         assert np.array_equal(got["conv_out"].float().cpu().numpy(), ref["conv_out"])
 
 
+@pytest.mark.parametrize("B,L", [(1, 768), (2, 800), (1, 2000)])
+def test_prefill_front_paths_bitexact(B, L):
+    """The front kernel's interior tiles take a 16-byte vector path when the rows are bf16,
+    unpacked, a multiple of 8 tokens long and qkv is 16-byte aligned; with qkv one element
+    off that alignment every tile takes the general path. Both do the same arithmetic in the
+    same order, so the whole layer agrees bit for bit (and with the oracle)."""
+    shape, dtype = SMALL128, "bf16"
+    _say(f"front paths B={B} L={L}")
+    inp = layer_inputs(shape, B, L, 46, dtype, s0_std=0.1, conv_std=1.0)
+    vec = run_prefill(shape, dtype, inp)
+    gen = run_prefill(shape, dtype, inp, qkv_offset=1)
+    for k in ("o", "S", "conv_out"):
+        assert torch.equal(vec[k], gen[k]), k
+    ref = oracle.gdn_forward(oparams(shape), inp["qkv"], inp["gate"], inp["beta"], inp["w"],
+                             inp["conv0"], inp["S0"])
+    assert rel_err(vec["o"], ref["o"]) <= TOL[dtype]
+    assert rel_err(vec["S"], ref["S"]) <= TOL[dtype]
+
+
 def test_prefill_split_carry():
     """prefill(L) == prefill(L1) then prefill(L - L1) with both states carried."""
     shape, dtype = SMALL128, "bf16"
