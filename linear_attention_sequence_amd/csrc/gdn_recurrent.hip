@@ -55,8 +55,8 @@ __device__ __forceinline__ RecLds rec_lds(float* lds, int T) {
     L.sv = L.sk + T * DK;                // [T][CW] v (this workgroup's columns)
     L.s_alpha = L.sv + T * CW;           // [T] exp(gate)
     L.s_beta = L.s_alpha + T;            // [T]
-    L.s_kq = L.s_beta + T;               // [T] k_hat . q_hat
-    L.red = L.s_kq + T;                  // [NW][CG][8] partial dot products
+    L.s_kq = L.s_beta + T;               // [T][3] per token: 1/|k|, the q scale, k_hat . q_hat
+    L.red = L.s_kq + 3 * T;              // [NW][CG][8] partial dot products
     L.s_delta = L.red + NW * (CW / 4) * 8;  // [CW]
     L.s_rms = L.s_delta + CW;               // [4] per-wave sums of o^2 (gated RMSNorm)
     L.s_o = L.s_rms + 4;                    // [CW] raw output of the token (gated RMSNorm)
@@ -68,7 +68,7 @@ template <int DK, int CW, int NT, bool EPI>
 size_t recurrent_lds_bytes(int T) {
     constexpr int CG = CW / 4;
     constexpr int NW = NT / kWave;
-    return sizeof(float) * (static_cast<size_t>(T) * (2 * DK + CW) + 3 * T + NW * CG * 8 + CW + 4 +
+    return sizeof(float) * (static_cast<size_t>(T) * (2 * DK + CW) + 5 * T + NW * CG * 8 + CW + 4 +
                             (EPI ? static_cast<size_t>(T + 1) * CW : 0));
 }
 
@@ -142,6 +142,11 @@ __device__ __forceinline__ void recur_tail(const RecArgs& a, const Unit& u, cons
     const int lane = tid % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform
     const float qscale = 1.0f / sqrtf(static_cast<float>(DK));
+    // Norms of every token (wave t % NW takes token t). q and k stay raw in LDS: the scales
+    // are applied to the reduced dot products (S^T k_hat = rk S^T k, S^T q_hat = qs S^T q)
+    // and to delta (k_hat delta^T = k (rk delta)^T), so this pass needs no barrier of its
+    // own and overlaps the other waves' dot products; its results are read after the first
+    // token's reduction barrier.
     for (int t = wave; t < T; t += NW) {
         float qq = 0.f, kk = 0.f, kq = 0.f;
         for (int i = lane; i < DK; i += kWave) {
@@ -156,13 +161,12 @@ __device__ __forceinline__ void recur_tail(const RecArgs& a, const Unit& u, cons
         const float rq = a.use_l2 ? 1.0f / sqrtf(qq + a.eps) : 1.0f;
         const float rk = a.use_l2 ? 1.0f / sqrtf(kk + a.eps) : 1.0f;
         const float qs = rq * qscale;
-        for (int i = lane; i < DK; i += kWave) {
-            L.sq[t * DK + i] *= qs;
-            L.sk[t * DK + i] *= rk;
+        if (lane == 0) {
+            L.s_kq[3 * t] = rk;
+            L.s_kq[3 * t + 1] = qs;
+            L.s_kq[3 * t + 2] = kq * rk * qs;
         }
-        if (lane == 0) L.s_kq[t] = kq * rk * qs;
     }
-    __syncthreads();
 
     for (int t = 0; t < T; ++t) {
         float pk[4] = {0.f, 0.f, 0.f, 0.f}, pq[4] = {0.f, 0.f, 0.f, 0.f};
@@ -201,10 +205,11 @@ __device__ __forceinline__ void recur_tail(const RecArgs& a, const Unit& u, cons
                 PK += L.red[(wv * CG + jg) * 8 + jc];
                 PQ += L.red[(wv * CG + jg) * 8 + 4 + jc];
             }
-            const float p = al * PK;
+            const float rk = L.s_kq[3 * t], qs = L.s_kq[3 * t + 1];
+            const float p = al * (PK * rk);
             const float d = be * (L.sv[t * CW + j] - p);
-            L.s_delta[j] = d;
-            ov = __fmaf_rn(d, L.s_kq[t], al * PQ);
+            L.s_delta[j] = d * rk;
+            ov = __fmaf_rn(d, L.s_kq[3 * t + 2], al * (PQ * qs));
             if constexpr (EPI) L.s_o[j] = ov;
         }
         constexpr int OW = (CW + kWave - 1) / kWave;   // waves holding output columns
