@@ -50,13 +50,14 @@ struct RecLds {
 template <int DK, int CW, int NW>
 __device__ __forceinline__ RecLds rec_lds(float* lds, int T) {
     RecLds L;
-    L.sq = lds;                          // [T][DK] q_hat
-    L.sk = L.sq + T * DK;                // [T][DK] k_hat
+    L.sq = lds;                          // [T][DK] q (raw: the norms scale the reduced products)
+    L.sk = L.sq + T * DK;                // [T][DK] k (raw)
     L.sv = L.sk + T * DK;                // [T][CW] v (this workgroup's columns)
     L.s_alpha = L.sv + T * CW;           // [T] exp(gate)
     L.s_beta = L.s_alpha + T;            // [T]
     L.s_kq = L.s_beta + T;               // [T][3] per token: 1/|k|, the q scale, k_hat . q_hat
-    L.red = L.s_kq + 3 * T;              // [NW][CG][8] partial dot products
+    // the regions from here on are read as float4: start on a 16-byte boundary
+    L.red = lds + ((static_cast<int>(L.s_kq - lds) + 3 * T + 3) & ~3);   // [NW][CG][8] partial dot products
     L.s_delta = L.red + NW * (CW / 4) * 8;  // [CW]
     L.s_rms = L.s_delta + CW;               // [4] per-wave sums of o^2 (gated RMSNorm)
     L.s_o = L.s_rms + 4;                    // [CW] raw output of the token (gated RMSNorm)
@@ -68,7 +69,7 @@ template <int DK, int CW, int NT, bool EPI>
 size_t recurrent_lds_bytes(int T) {
     constexpr int CG = CW / 4;
     constexpr int NW = NT / kWave;
-    return sizeof(float) * (static_cast<size_t>(T) * (2 * DK + CW) + 5 * T + NW * CG * 8 + CW + 4 +
+    return sizeof(float) * (static_cast<size_t>(T) * (2 * DK + CW) + 5 * T + 3 + NW * CG * 8 + CW + 4 +
                             (EPI ? static_cast<size_t>(T + 1) * CW : 0));
 }
 
