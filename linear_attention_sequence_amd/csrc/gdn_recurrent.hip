@@ -56,9 +56,9 @@ __device__ __forceinline__ RecLds rec_lds(float* lds, int T) {
     L.s_alpha = L.sv + T * CW;           // [T] exp(gate)
     L.s_beta = L.s_alpha + T;            // [T]
     L.s_kq = L.s_beta + T;               // [T][3] per token: 1/|k|, the q scale, k_hat . q_hat
-    // the regions from here on are read as float4: start on a 16-byte boundary
-    L.red = lds + ((static_cast<int>(L.s_kq - lds) + 3 * T + 3) & ~3);   // [NW][CG][8] partial dot products
-    L.s_delta = L.red + NW * (CW / 4) * 8;  // [CW]
+    L.red = L.s_kq + 3 * T;              // [NW][CG][8] partial dot products
+    // delta is read as float4: it starts on a 16-byte boundary
+    L.s_delta = lds + ((static_cast<int>(L.red - lds) + NW * (CW / 4) * 8 + 3) & ~3);   // [CW]
     L.s_rms = L.s_delta + CW;               // [4] per-wave sums of o^2 (gated RMSNorm)
     L.s_o = L.s_rms + 4;                    // [CW] raw output of the token (gated RMSNorm)
     L.s_gz = L.s_o + CW;                    // [T][CW] norm_weight * silu(z) (gated RMSNorm)
