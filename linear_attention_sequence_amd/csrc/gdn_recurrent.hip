@@ -44,7 +44,7 @@ struct RecGeom {
 };
 
 struct RecLds {
-    float *sq, *sk, *sv, *s_alpha, *s_beta, *s_kq, *red, *s_delta, *s_rms, *s_o, *s_gz;
+    float *sq, *sk, *sv, *s_alpha, *s_beta, *s_kq, *red, *s_gz;
 };
 
 template <int DK, int CW, int NW>
@@ -56,12 +56,9 @@ __device__ __forceinline__ RecLds rec_lds(float* lds, int T) {
     L.s_alpha = L.sv + T * CW;           // [T] exp(gate)
     L.s_beta = L.s_alpha + T;            // [T]
     L.s_kq = L.s_beta + T;               // [T][3] per token: 1/|k|, the q scale, k_hat . q_hat
-    // partial sums and delta are read as float4: 16-byte boundaries
-    L.red = lds + ((static_cast<int>(L.s_kq - lds) + 3 * T + 3) & ~3);   // [2][NW][CG][8] partial dot products
-    L.s_delta = L.red + 2 * NW * (CW / 4) * 8;                           // [CW]
-    L.s_rms = L.s_delta + CW;               // [4] per-wave sums of o^2 (gated RMSNorm)
-    L.s_o = L.s_rms + 4;                    // [CW] raw output of the token (gated RMSNorm)
-    L.s_gz = L.s_o + CW;                    // [T][CW] norm_weight * silu(z) (gated RMSNorm)
+    // the partial sums and the gated RMSNorm factors are read as float4: 16-byte boundaries
+    L.red = lds + ((static_cast<int>(L.s_kq - lds) + 3 * T + 3) & ~3);   // [2][NW][CG][8] partial S^T k, S^T q
+    L.s_gz = L.red + 2 * NW * (CW / 4) * 8;                              // [T][CW] norm_weight * silu(z)
     return L;
 }
 
@@ -69,8 +66,8 @@ template <int DK, int CW, int NT, bool EPI>
 size_t recurrent_lds_bytes(int T) {
     constexpr int CG = CW / 4;
     constexpr int NW = NT / kWave;
-    return sizeof(float) * (static_cast<size_t>(T) * (2 * DK + CW) + 5 * T + 3 + 2 * NW * CG * 8 + CW + 4 +
-                            (EPI ? static_cast<size_t>(T + 1) * CW : 0));
+    return sizeof(float) * (static_cast<size_t>(T) * (2 * DK + CW) + 5 * T + 3 + 2 * NW * CG * 8 +
+                            (EPI ? static_cast<size_t>(T) * CW : 0));
 }
 
 // Which (sequence, V head, column slice) a unit index names.
@@ -189,11 +186,11 @@ __device__ __forceinline__ void recur_tail(const RecArgs& a, const Unit& u, cons
                 pq[c] += __shfl_xor(pq[c], m, kWave);
             }
         }
-        // without the epilogue each thread forms delta for its own columns, so there is no
-        // second barrier per token: a wave may then write token t + 1's partials while
-        // others still read token t's, hence two buffers (token t + 2 reuses the first
-        // only after token t + 1's barrier)
-        float* red = L.red + (EPI ? 0 : (t & 1)) * (NW * CG * 8);
+        // One barrier per token: after it every thread forms delta for its own four columns
+        // from the reduced partials. A wave may then write token t + 1's partials while others
+        // still read token t's, hence two buffers (token t + 2 reuses the first only after
+        // token t + 1's barrier).
+        float* red = L.red + (t & 1) * (NW * CG * 8);
         if (lane < CG) {
             float* rp = red + (wave * CG + lane) * 8;
 #pragma unroll
@@ -201,76 +198,18 @@ __device__ __forceinline__ void recur_tail(const RecArgs& a, const Unit& u, cons
         }
         __syncthreads();
         const float al = L.s_alpha[t], be = L.s_beta[t];
-        const size_t orow = ((static_cast<size_t>(u.b) * T + t) * a.Hv + u.h) * DV + u.j0;
+        const float rk = L.s_kq[3 * t], qs = L.s_kq[3 * t + 1], kqh = L.s_kq[3 * t + 2];
+        float4 PK = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int wv = 0; wv < NW; ++wv) {
+            const float4 v = *reinterpret_cast<const float4*>(red + (wv * CG + cg) * 8);
+            PK.x += v.x; PK.y += v.y; PK.z += v.z; PK.w += v.w;
+        }
+        const float4 vv = *reinterpret_cast<const float4*>(L.sv + t * CW + 4 * cg);
+        const float4 d = make_float4(be * (vv.x - al * (PK.x * rk)), be * (vv.y - al * (PK.y * rk)),
+                                     be * (vv.z - al * (PK.z * rk)), be * (vv.w - al * (PK.w * rk)));
+        const float4 dl = make_float4(d.x * rk, d.y * rk, d.z * rk, d.w * rk);
         float* Sout = a.S_out + ((static_cast<size_t>(u.b) * T + t) * a.Hv + u.h) * DK * DV + u.j0;
-        if constexpr (!EPI) {
-            const float rk = L.s_kq[3 * t], qs = L.s_kq[3 * t + 1], kqh = L.s_kq[3 * t + 2];
-            float4 PK = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-            for (int wv = 0; wv < NW; ++wv) {
-                const float4 v = *reinterpret_cast<const float4*>(red + (wv * CG + cg) * 8);
-                PK.x += v.x; PK.y += v.y; PK.z += v.z; PK.w += v.w;
-            }
-            const float4 vv = *reinterpret_cast<const float4*>(L.sv + t * CW + 4 * cg);
-            const float4 d = make_float4(be * (vv.x - al * (PK.x * rk)), be * (vv.y - al * (PK.y * rk)),
-                                         be * (vv.z - al * (PK.z * rk)), be * (vv.w - al * (PK.w * rk)));
-            const float4 dl = make_float4(d.x * rk, d.y * rk, d.z * rk, d.w * rk);
-#pragma unroll
-            for (int r = 0; r < RPT; ++r) {
-                const float kv = L.sk[t * DK + rg + r * RG];
-                s[r].x = __fmaf_rn(kv, dl.x, al * s[r].x);
-                s[r].y = __fmaf_rn(kv, dl.y, al * s[r].y);
-                s[r].z = __fmaf_rn(kv, dl.z, al * s[r].z);
-                s[r].w = __fmaf_rn(kv, dl.w, al * s[r].w);
-                float* dst = Sout + static_cast<size_t>(rg + r * RG) * DV + 4 * cg;
-                if constexpr (NT_STORE) {
-                    const f32x4 v = {s[r].x, s[r].y, s[r].z, s[r].w};
-                    __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst));
-                } else {
-                    *reinterpret_cast<float4*>(dst) = s[r];
-                }
-            }
-            // the output after the state tile's stores are issued (this order measured
-            // 1 us faster per decode step): row group 0, CG lanes of 4 columns each
-            if (rg == 0) {
-                float4 PQ = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-                for (int wv = 0; wv < NW; ++wv) {
-                    const float4 v = *reinterpret_cast<const float4*>(red + (wv * CG + cg) * 8 + 4);
-                    PQ.x += v.x; PQ.y += v.y; PQ.z += v.z; PQ.w += v.w;
-                }
-                const float4 ov = make_float4(__fmaf_rn(d.x, kqh, al * (PQ.x * qs)), __fmaf_rn(d.y, kqh, al * (PQ.y * qs)),
-                                              __fmaf_rn(d.z, kqh, al * (PQ.z * qs)), __fmaf_rn(d.w, kqh, al * (PQ.w * qs)));
-                *reinterpret_cast<float4*>(a.o + orow + 4 * cg) = ov;
-            }
-            continue;
-        }
-        float ov = 0.f;
-        if (tid < CW) {
-            const int j = tid, jg = j / 4, jc = j % 4;
-            float PK = 0.f, PQ = 0.f;
-#pragma unroll
-            for (int wv = 0; wv < NW; ++wv) {
-                PK += red[(wv * CG + jg) * 8 + jc];
-                PQ += red[(wv * CG + jg) * 8 + 4 + jc];
-            }
-            const float rk = L.s_kq[3 * t], qs = L.s_kq[3 * t + 1];
-            const float p = al * (PK * rk);
-            const float d = be * (L.sv[t * CW + j] - p);
-            L.s_delta[j] = d * rk;
-            ov = __fmaf_rn(d, L.s_kq[3 * t + 2], al * (PQ * qs));
-            if constexpr (EPI) L.s_o[j] = ov;
-        }
-        constexpr int OW = (CW + kWave - 1) / kWave;   // waves holding output columns
-        static_assert(OW <= 4, "s_rms holds four partial sums");
-        if constexpr (EPI) {                            // gated RMSNorm: per-wave sums of o^2
-            if (wave < OW) {
-                const float ss = wave_sum_uniform(ov * ov);
-                if (lane == 0) L.s_rms[wave] = ss;
-            }
-        }
-        __syncthreads();
-        const float4 dl = *reinterpret_cast<const float4*>(L.s_delta + 4 * cg);
 #pragma unroll
         for (int r = 0; r < RPT; ++r) {
             const float kv = L.sk[t * DK + rg + r * RG];
@@ -286,16 +225,31 @@ __device__ __forceinline__ void recur_tail(const RecArgs& a, const Unit& u, cons
                 *reinterpret_cast<float4*>(dst) = s[r];
             }
         }
-        // the token's output is stored after the state tile's stores are issued
-        // (this order measured 1 us faster per decode step); with the epilogue it
-        // is normalised first
-        if (!EPI && tid < CW) a.o[orow + tid] = ov;
-        if (EPI && tid < CW) {
-            float ss = 0.f;
+        // The output row, after the state tile's stores are issued (this order measured
+        // 1 us faster per decode step): row group 0, CG lanes of wave 0 with four columns
+        // each, so the gated RMSNorm reduces its row within the wave.
+        if (wave == 0) {
+            float4 ov = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (rg == 0) {
+                float4 PQ = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-            for (int wv = 0; wv < OW; ++wv) ss += L.s_rms[wv];
-            const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / DV) + a.fu.norm_eps);
-            a.o[orow + tid] = (L.s_o[tid] * inv) * L.s_gz[t * CW + tid];
+                for (int wv = 0; wv < NW; ++wv) {
+                    const float4 v = *reinterpret_cast<const float4*>(red + (wv * CG + cg) * 8 + 4);
+                    PQ.x += v.x; PQ.y += v.y; PQ.z += v.z; PQ.w += v.w;
+                }
+                ov = make_float4(__fmaf_rn(d.x, kqh, al * (PQ.x * qs)), __fmaf_rn(d.y, kqh, al * (PQ.y * qs)),
+                                 __fmaf_rn(d.z, kqh, al * (PQ.z * qs)), __fmaf_rn(d.w, kqh, al * (PQ.w * qs)));
+            }
+            if constexpr (EPI) {   // the other lanes of the wave add zeros
+                const float ss = wave_sum_uniform(ov.x * ov.x + ov.y * ov.y + ov.z * ov.z + ov.w * ov.w);
+                const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / DV) + a.fu.norm_eps);
+                if (rg == 0) {
+                    const float4 gz = *reinterpret_cast<const float4*>(L.s_gz + t * CW + 4 * cg);
+                    ov = make_float4((ov.x * inv) * gz.x, (ov.y * inv) * gz.y, (ov.z * inv) * gz.z, (ov.w * inv) * gz.w);
+                }
+            }
+            const size_t orow = ((static_cast<size_t>(u.b) * T + t) * a.Hv + u.h) * DV + u.j0;
+            if (rg == 0) *reinterpret_cast<float4*>(a.o + orow + 4 * cg) = ov;
         }
     }
 }
