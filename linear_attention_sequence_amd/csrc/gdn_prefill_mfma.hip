@@ -1433,7 +1433,10 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
     if constexpr (!LW && NTW == 1) {
         if (mapo != 0) {
             const size_t m = mapo - 1;                   // (segment, sequence, head) of the map
-            const int eC = pow2_exponent(wave_max_nonneg(smax));
+            // the tile's largest magnitude over the whole wave (smax is per lane: a lane
+            // holds 32 of the tile's 2048 entries, which can all be zero in a nonzero tile)
+            const float tmax = wave_max_nonneg(smax);
+            const int eC = pow2_exponent(tmax);
             const float sC = ldexpf(1.f, -eC);
             constexpr int MS = D + 8;                    // LDS row stride (halfs)
             _Float16* lh = reinterpret_cast<_Float16*>(g_stage);
@@ -1448,7 +1451,7 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
                     lh[(16 * mt + 4 * g + e) * MS + kpos(col0 + r16)] = hi;
                     ll[(16 * mt + 4 * g + e) * MS + kpos(col0 + r16)] = static_cast<_Float16>(x - static_cast<float>(hi));
                 }
-            if (lane == 0) ws.Mexp[m * (D / 16) + col0 / 16] = smax > 0.f ? eC : kZeroTile;
+            if (lane == 0) ws.Mexp[m * (D / 16) + col0 / 16] = tmax > 0.f ? eC : kZeroTile;
             __syncthreads();
             _Float16* dst = ws.Mhl + m * 2 * D * D;
             for (int q = tid; q < 2 * D * (D / 8); q += NW * 64) {   // 16-byte granules of both planes
@@ -1480,10 +1483,7 @@ size_t prefill_mfma_workspace_bytes(int B, int L, int N, int Hk, int Hv) {
 // Whole-head carry workgroups: 8 waves of one 16-column tile each (two waves per
 // SIMD hide each other's LDS and MFMA latencies; on the 8-sequence ragged prefill
 // this beat 4 waves of two tiles by 10%).
-#ifndef CARRY_NTW
-#define CARRY_NTW 1
-#define CARRY_NW 8
-#endif
+constexpr int kWholeNTW = 1, kWholeNW = 8;
 
 // Compute units of the current device (queried once per device).
 static int device_cu_count() {
@@ -1547,12 +1547,12 @@ static hipError_t launch_mfma_t(const PrefillArgs& a, int in_dtype, hipStream_t 
             w2.pass = 2;
             void* args1[] = {const_cast<PrefillArgs*>(&a), &w1};
             void* args2[] = {const_cast<PrefillArgs*>(&a), &w2};
-            static_assert(CARRY_NTW == 1, "the first pass writes the state maps from one column tile per wave");
-            e = launch_carry<CARRY_NTW, CARRY_NW>(args1, (2 * ws.nseg - 3) * heads, stream);
+            static_assert(kWholeNTW == 1, "the first pass writes the state maps from one column tile per wave");
+            e = launch_carry<kWholeNTW, kWholeNW>(args1, (2 * ws.nseg - 3) * heads, stream);
             if (e != hipSuccess) return e;
             e = launch_carry<1, 4, true>(args2, (ws.nseg - 1) * heads, stream);
         } else {
-            e = split ? launch_carry<1, 4, true>(args, heads, stream) : launch_carry<CARRY_NTW, CARRY_NW>(args, heads, stream);
+            e = split ? launch_carry<1, 4, true>(args, heads, stream) : launch_carry<kWholeNTW, kWholeNW>(args, heads, stream);
         }
         if (e != hipSuccess) return e;
     }

@@ -1,7 +1,9 @@
 """GPU parity at the full workload sizes, in the launch configuration bench.py
-times. The HIP path runs the whole workload; the fp64 oracle computes a sample
-of (sequence, V head) units (both V heads of a GQA pair, first/last heads and
-sequences) and every raw conv-state value, which are compared exactly."""
+times. The HIP path runs the whole workload and the fp64 oracle computes every
+(sequence, V head) unit of it (about 10 GFLOP/s on 16 host threads: decode's 69
+GFLOP, the ragged prompt's 119 GFLOP and the 4096-token prompt's 17 GFLOP each
+take seconds), so every output, every final state or snapshot, and every raw
+conv-state value (compared exactly) is checked, whichever workgroup produced it."""
 from __future__ import annotations
 
 import numpy as np
@@ -23,13 +25,6 @@ def _gpu():
         pytest.skip("no GPU")
     gdn.load()
     oracle.build_oracle(force=False)
-
-
-def _mask(N, Hv, units):
-    m = np.zeros((N, Hv), bool)
-    for n, h in units:
-        m[n, h] = True
-    return m
 
 
 def test_decode_B64_256_steps():
@@ -55,12 +50,11 @@ def test_decode_B64_256_steps():
         o[:, t:t + 1] = ot
         cs = cn
     torch.cuda.synchronize()
-    units = [(0, 0), (0, 1), (17, 14), (17, 15), (63, 30), (63, 31), (40, 7)]
-    ref = oracle.gdn_forward(oparams(SH), x, g, b, w, c0, S0, unit_mask=_mask(B, SH.Hv, units))
-    bi = [u[0] for u in units]
-    hi = [u[1] for u in units]
-    assert rel_err(o[bi, :, hi], ref["o"][bi, :, hi]) <= TOL["bf16"]
-    assert rel_err(S[bi, hi], ref["S"][bi, hi]) <= TOL["bf16"]
+    ref = oracle.gdn_forward(oparams(SH), x, g, b, w, c0, S0)
+    assert rel_err(o, ref["o"]) <= TOL["bf16"]
+    assert rel_err(S, ref["S"]) <= TOL["bf16"]
+    for bb in (0, B - 1):   # per-sequence errors stay within the bound too (not only the global max)
+        assert rel_err(o[bb], ref["o"][bb]) <= TOL["bf16"], bb
     assert np.array_equal(cs.float().cpu().numpy(), ref["conv_out"])
 
 
@@ -86,12 +80,13 @@ def test_prefill_L4096():
     b = gi.beta(SH, 1, L, seed, "bf16")
     w = gi.conv_weight(SH, seed, "bf16")
     o, S, cout = _prefill(x, g, b, w, 1)
-    heads = [0, 1, 16, 17, 31]
-    ref = oracle.gdn_forward(oparams(SH), x, g, b, w, np.zeros((1, SH.D, 3)), np.zeros((1, SH.Hv, 128, 128)),
-                             unit_mask=_mask(1, SH.Hv, [(0, h) for h in heads]))
+    ref = oracle.gdn_forward(oparams(SH), x, g, b, w, np.zeros((1, SH.D, 3)), np.zeros((1, SH.Hv, 128, 128)))
     assert not torch.isnan(o).any()
-    assert rel_err(o[0][:, heads], ref["o"][0][:, heads]) <= TOL["bf16"]
-    assert rel_err(S[0, heads], ref["S"][0, heads]) <= TOL["bf16"]
+    assert rel_err(o, ref["o"]) <= TOL["bf16"]
+    assert rel_err(S, ref["S"]) <= TOL["bf16"]
+    for h in range(SH.Hv):   # every head, i.e. every (slice, slot) of both carry passes
+        assert rel_err(o[0, :, h], ref["o"][0, :, h]) <= TOL["bf16"], h
+        assert rel_err(S[0, h], ref["S"][0, h]) <= TOL["bf16"], h
     assert np.array_equal(cout.float().cpu().numpy(), ref["conv_out"])
 
 
@@ -106,14 +101,14 @@ def test_ragged_prefill_8_sequences():
     b = gi.beta(SH, 1, L, seed, "bf16")
     w = gi.conv_weight(SH, seed, "bf16")
     o, S, cout = _prefill(x, g, b, w, N, cu=cu)
-    units = [(0, 0), (0, 31), (3, 8), (3, 9), (7, 0), (int(np.argmax(lens)), 20)]
     ref = oracle.gdn_forward(oparams(SH), x, g, b, w, np.zeros((N, SH.D, 3)), np.zeros((N, SH.Hv, 128, 128)),
-                             cu_seqlens=cu, unit_mask=_mask(N, SH.Hv, units))
+                             cu_seqlens=cu)
     assert not torch.isnan(o).any()
-    for n, h in units:
+    for n in range(N):
         s, e = int(cu[n]), int(cu[n + 1])
-        assert rel_err(o[0, s:e, h], ref["o"][0, s:e, h]) <= TOL["bf16"], (n, h)
-        assert rel_err(S[n, h], ref["S"][n, h]) <= TOL["bf16"], (n, h)
+        for h in range(SH.Hv):
+            assert rel_err(o[0, s:e, h], ref["o"][0, s:e, h]) <= TOL["bf16"], (n, h)
+            assert rel_err(S[n, h], ref["S"][n, h]) <= TOL["bf16"], (n, h)
     assert np.array_equal(cout.float().cpu().numpy(), ref["conv_out"])
 
 
@@ -139,15 +134,11 @@ def test_verify_B128_T4_and_commit():
     gdn.gdn_verify_commit(p, dev(acc), xd, cin, snap, c_out, S_out)
     torch.cuda.synchronize()
     assert torch.equal(S_in, dev(S0))   # S_in is read only
-    units = [(0, 0), (0, 1), (64, 16), (64, 17), (127, 31), (99, 5)]
-    ref = oracle.gdn_forward(oparams(SH), x, g, b, w, c0, S0, snapshots=True,
-                             unit_mask=_mask(B, SH.Hv, units))
-    bi = [u[0] for u in units]
-    hi = [u[1] for u in units]
-    assert rel_err(o[bi, :, hi], ref["o"][bi, :, hi]) <= TOL["bf16"]
-    assert rel_err(snap[bi, :, hi], ref["snap"][bi, :, hi]) <= TOL["bf16"]
+    ref = oracle.gdn_forward(oparams(SH), x, g, b, w, c0, S0, snapshots=True)
+    assert rel_err(o, ref["o"]) <= TOL["bf16"]
+    assert rel_err(snap, ref["snap"]) <= TOL["bf16"]
     S_ref, c_ref = oracle.verify_commit(oparams(SH), acc, x, c0, ref["snap"])
-    assert rel_err(S_out[bi, hi], S_ref[bi, hi]) <= TOL["bf16"]
+    assert rel_err(S_out, S_ref) <= TOL["bf16"]
     assert np.array_equal(c_out.float().cpu().numpy(), c_ref)
     # every row's committed state is exactly its selected snapshot
     sel = snap[torch.arange(B, device="cuda"), torch.from_numpy(acc).long().cuda()]

@@ -319,18 +319,17 @@ def test_prefill_deterministic_and_ragged_equals_separate():
     b = run_prefill(shape, dtype, inp, cu=cu)
     for k in ("o", "S", "conv_out"):
         assert torch.equal(a[k], b[k]), k
+    # Each sequence alone, through cu_seqlens = [0, len] and unpacked: every (chunk, head)
+    # and every carry workgroup does the same arithmetic whatever else is packed beside it
+    # (chains this short never run in segments), so the results agree bit for bit.
     for n in range(len(lens)):
         s, e = int(cu[n]), int(cu[n + 1])
         one = {"qkv": inp["qkv"][:, :, s:e], "gate": inp["gate"][:, s:e], "beta": inp["beta"][:, s:e],
                "w": inp["w"], "conv0": inp["conv0"][n:n + 1], "S0": inp["S0"][n:n + 1]}
-        r = run_prefill(shape, dtype, one)
-        assert torch.equal(r["conv_out"][0], a["conv_out"][n])
-        if e - s <= 64:   # one chunk: the same carry as the packed call, bit for bit
-            assert torch.equal(r["o"][0], a["o"][0, s:e])
-            assert torch.equal(r["S"][0], a["S"][n])
-        else:             # several chunks: the same results within tolerance
-            assert rel_err(r["o"][0], a["o"][0, s:e].double().cpu().numpy()) <= TOL[dtype]
-            assert rel_err(r["S"][0], a["S"][n].double().cpu().numpy()) <= TOL[dtype]
+        for r in (run_prefill(shape, dtype, one, cu=gi.cu_seqlens([e - s])), run_prefill(shape, dtype, one)):
+            assert torch.equal(r["conv_out"][0], a["conv_out"][n]), n
+            assert torch.equal(r["o"][0], a["o"][0, s:e]), n
+            assert torch.equal(r["S"][0], a["S"][n]), n
 
 
 @pytest.mark.parametrize("L", [65, 700, 768, 1000, 1300, 2000])
@@ -350,6 +349,37 @@ def test_prefill_segmented_carry(L):
         assert rel_err(got["o"], ref["o"]) <= TOL[dtype]
         assert rel_err(got["S"], ref["S"]) <= TOL[dtype]
         assert np.array_equal(got["conv_out"].float().cpu().numpy(), ref["conv_out"])
+
+
+@pytest.mark.parametrize("L", [1300, 2000])
+def test_prefill_segmented_zero_column_map(L):
+    """Segment state maps whose first column is exactly zero while the rest of its 16-column
+    tile is not. Every key is the unit vector e_0 (K channel 0 of each head constant, every
+    other K channel zero, identity conv taps), beta = 1 and gate = 0, so each token replaces
+    row 0 of S by its value and leaves the other rows alone: a segment's map is I - e_0 e_0^T.
+    The tile of map columns 0..15 must keep its scale (a zero-tile flag taken from one lane
+    would drop rows 1..15 of every later entry state). 5 and 8 segments."""
+    shape, dtype = SMALL128, "bf16"
+    _say(f"segmented carry, zero map column L={L}")
+    rng = np.random.default_rng([1301, L])
+    D, HKD = shape.D, shape.Hk * shape.dk
+    x = np.zeros((1, D, L))
+    x[:, :HKD] = rng.standard_normal((1, HKD, L))                 # queries
+    x[:, 2 * HKD:] = rng.standard_normal((1, D - 2 * HKD, L))      # values
+    for hk in range(shape.Hk):
+        x[:, HKD + hk * shape.dk] = 4.0                            # key channel 0 of head hk
+    w = np.zeros((D, 1, shape.K))
+    w[:, 0, shape.K - 1] = 1.0                                     # conv = current token
+    inp = {"qkv": gi.round_to(x, dtype), "gate": np.zeros((1, L, shape.Hv), np.float32),
+           "beta": np.ones((1, L, shape.Hv), np.float32), "w": gi.round_to(w, dtype),
+           "conv0": np.zeros((1, D, shape.K - 1), np.float32), "S0": gi.state0(shape, 1, 47, 0.1)}
+    seg = run_prefill(shape, dtype, inp)
+    packed = run_prefill(shape, dtype, inp, cu=gi.cu_seqlens([L]))
+    ref = oracle.gdn_forward(oparams(shape), inp["qkv"], inp["gate"], inp["beta"], inp["w"],
+                             inp["conv0"], inp["S0"])
+    for got in (seg, packed):
+        assert rel_err(got["o"], ref["o"]) <= TOL[dtype]
+        assert rel_err(got["S"], ref["S"]) <= TOL[dtype]
 
 
 @pytest.mark.parametrize("B,L", [(1, 768), (2, 800), (1, 2000)])
