@@ -1,9 +1,10 @@
 """Python binding of libgdn.so, the MI355X Gated DeltaNet layer (include/gdn.h).
 
 Argument marshalling only: each function checks that the torch tensors it is
-given are contiguous device tensors of the expected dtype, reads the sizes off
-their shapes and passes raw pointers plus the current HIP stream to the C entry
-point of the same name. All arithmetic runs in the HIP kernels of libgdn.so;
+given have the dtype and the exact shape the call derives from the params and
+the leading tensor (ValueError otherwise, before anything is launched), that
+they are contiguous device tensors, reads the sizes off their shapes and passes
+raw pointers plus the current HIP stream to the C entry point of the same name. All arithmetic runs in the HIP kernels of libgdn.so;
 there is no fallback. If the library is missing the import still succeeds
 (so that `build()` can run) but every call raises.
 """
@@ -148,6 +149,28 @@ def _expect(t, dtype, name):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+def _shape(t, expected, name):
+    """Raise ValueError unless tensor t (if given) has exactly the shape the call derives
+    for it, so that no undersized buffer reaches a kernel."""
+    if t is not None and tuple(t.shape) != tuple(expected):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}; this call needs {tuple(expected)}")
+
+
+def _fusion_shapes(p: "GdnParams", fusion, z_shape):
+    if fusion is None:
+        return
+    _shape(fusion.A_log, (p.num_v_heads,), "A_log")
+    _shape(fusion.dt_bias, (p.num_v_heads,), "dt_bias")
+    _shape(fusion.z, z_shape, "z")
+    _shape(fusion.norm_weight, (p.head_v_dim,), "norm_weight")
+
+
+def _dims(t, n, name):
+    if t.dim() != n:
+        raise ValueError(f"{name} must have {n} dimensions, got shape {tuple(t.shape)}")
+    return tuple(t.shape)
+
+
 def _stream(stream=None):
     s = stream if stream is not None else torch.cuda.current_stream()
     return ctypes.c_void_p(s.cuda_stream)
@@ -158,6 +181,32 @@ def _call(fn, *args):
     st = getattr(lib, fn)(*args)
     if st != 0:
         raise GdnError(fn, st, lib.gdn_status_string(st).decode())
+
+
+def _recurrent_shapes(p, B, T, qkv, gate, beta, conv_weight, conv_state_in, S, o):
+    """Shapes shared by the decode and verify calls (T tokens per sequence)."""
+    Hv = p.num_v_heads
+    _shape(qkv, (B, p.D, T), "qkv")
+    _shape(gate, (B, T, Hv), "gate")
+    _shape(beta, (B, T, Hv), "beta")
+    _shape(conv_weight, (p.D, 1, p.conv_kernel), "conv_weight")
+    _shape(conv_state_in, (B, p.D, p.conv_kernel - 1), "conv_state_in")
+    _shape(S, (B, Hv, p.head_k_dim, p.head_v_dim), "S")
+    _shape(o, (B, T, Hv, p.head_v_dim), "o")
+
+
+def _prefill_shapes(p, B, L, N, qkv, gate, beta, conv_weight, conv_state_in, conv_state_out, S, o,
+                    cu_seqlens):
+    Hv, win = p.num_v_heads, (N, p.D, p.conv_kernel - 1)
+    _shape(qkv, (B, p.D, L), "qkv")
+    _shape(gate, (B, L, Hv), "gate")
+    _shape(beta, (B, L, Hv), "beta")
+    _shape(conv_weight, (p.D, 1, p.conv_kernel), "conv_weight")
+    _shape(conv_state_in, win, "conv_state_in")
+    _shape(conv_state_out, win, "conv_state_out")
+    _shape(S, (N, Hv, p.head_k_dim, p.head_v_dim), "S")
+    _shape(o, (B, L, Hv, p.head_v_dim), "o")
+    _shape(cu_seqlens, (N + 1,), "cu_seqlens")
 
 
 def gdn_version() -> int:
@@ -172,8 +221,15 @@ def gdn_conv1d_silu(p: GdnParams, qkv, conv_weight, conv_state_in, conv_state_ou
         _expect(t, p.torch_dtype, n)
     _expect(y, torch.float32, "y")
     _expect(cu_seqlens, torch.int32, "cu_seqlens")
-    B, _, L = qkv.shape
-    N = conv_state_in.shape[0]
+    B, _, L = _dims(qkv, 3, "qkv")
+    N = _dims(conv_state_in, 3, "conv_state_in")[0]
+    D, K = p.D, p.conv_kernel
+    _shape(qkv, (B, D, L), "qkv")
+    _shape(conv_weight, (D, 1, K), "conv_weight")
+    _shape(conv_state_in, (N, D, K - 1), "conv_state_in")
+    _shape(conv_state_out, (N, D, K - 1), "conv_state_out")
+    _shape(y, (B, D, L), "y")
+    _shape(cu_seqlens, (N + 1,), "cu_seqlens")
     _call("gdn_conv1d_silu", ctypes.byref(p.c()), B, L, _ptr(qkv), _ptr(conv_weight),
           _ptr(conv_state_in), _ptr(conv_state_out), _ptr(y), _ptr(cu_seqlens), N, _stream(stream))
 
@@ -186,7 +242,9 @@ def gdn_decode_step(p: GdnParams, qkv, gate, beta, conv_weight, conv_state_in, c
         _expect(t, p.torch_dtype, n)
     _expect(S, torch.float32, "S")
     _expect(o, torch.float32, "o")
-    B = qkv.shape[0]
+    B = _dims(qkv, 3, "qkv")[0]
+    _recurrent_shapes(p, B, 1, qkv, gate, beta, conv_weight, conv_state_in, S, o)
+    _shape(conv_state_out, (B, p.D, p.conv_kernel - 1), "conv_state_out")
     _call("gdn_decode_step", ctypes.byref(p.c()), B, _ptr(qkv), _ptr(gate), _ptr(beta),
           _ptr(conv_weight), _ptr(conv_state_in), _ptr(conv_state_out), _ptr(S), _ptr(o),
           _stream(stream))
@@ -200,7 +258,10 @@ def gdn_decode_step_ex(p: GdnParams, fusion: GdnFusion | None, qkv, gate, beta, 
         _expect(t, p.torch_dtype, n)
     _expect(S, torch.float32, "S")
     _expect(o, torch.float32, "o")
-    B = qkv.shape[0]
+    B = _dims(qkv, 3, "qkv")[0]
+    _recurrent_shapes(p, B, 1, qkv, gate, beta, conv_weight, conv_state_in, S, o)
+    _shape(conv_state_out, (B, p.D, p.conv_kernel - 1), "conv_state_out")
+    _fusion_shapes(p, fusion, (B, 1, p.num_v_heads, p.head_v_dim))
     _call("gdn_decode_step_ex", ctypes.byref(p.c()), _fusion_ref(p, fusion), B, _ptr(qkv),
           _ptr(gate), _ptr(beta), _ptr(conv_weight), _ptr(conv_state_in), _ptr(conv_state_out),
           _ptr(S), _ptr(o), _stream(stream))
@@ -214,7 +275,10 @@ def gdn_verify_block(p: GdnParams, qkv, gate, beta, conv_weight, conv_state_in, 
         _expect(t, p.torch_dtype, n)
     for t, n in ((S_in, "S_in"), (S_snap, "S_snap"), (o, "o")):
         _expect(t, torch.float32, n)
-    B, _, T = qkv.shape
+    B, _, T = _dims(qkv, 3, "qkv")
+    _recurrent_shapes(p, B, T, qkv, gate, beta, conv_weight, conv_state_in, None, o)
+    _shape(S_snap, (B, T, p.num_v_heads, p.head_k_dim, p.head_v_dim), "S_snap")
+    _shape(S_in, (B, p.num_v_heads, p.head_k_dim, p.head_v_dim), "S_in")
     _call("gdn_verify_block", ctypes.byref(p.c()), B, T, _ptr(qkv), _ptr(gate), _ptr(beta),
           _ptr(conv_weight), _ptr(conv_state_in), _ptr(S_in), _ptr(S_snap), _ptr(o),
           _stream(stream))
@@ -228,7 +292,11 @@ def gdn_verify_block_ex(p: GdnParams, fusion: GdnFusion | None, qkv, gate, beta,
         _expect(t, p.torch_dtype, n)
     for t, n in ((S_in, "S_in"), (S_snap, "S_snap"), (o, "o")):
         _expect(t, torch.float32, n)
-    B, _, T = qkv.shape
+    B, _, T = _dims(qkv, 3, "qkv")
+    _recurrent_shapes(p, B, T, qkv, gate, beta, conv_weight, conv_state_in, None, o)
+    _shape(S_snap, (B, T, p.num_v_heads, p.head_k_dim, p.head_v_dim), "S_snap")
+    _shape(S_in, (B, p.num_v_heads, p.head_k_dim, p.head_v_dim), "S_in")
+    _fusion_shapes(p, fusion, (B, T, p.num_v_heads, p.head_v_dim))
     _call("gdn_verify_block_ex", ctypes.byref(p.c()), _fusion_ref(p, fusion), B, T, _ptr(qkv),
           _ptr(gate), _ptr(beta), _ptr(conv_weight), _ptr(conv_state_in), _ptr(S_in),
           _ptr(S_snap), _ptr(o), _stream(stream))
@@ -243,7 +311,13 @@ def gdn_verify_block_slots(p: GdnParams, fusion: GdnFusion | None, qkv, gate, be
     for t, n in ((S_prev, "S_prev"), (S_snap, "S_snap"), (o, "o")):
         _expect(t, torch.float32, n)
     _expect(slot, torch.int32, "slot")
-    B, _, T = qkv.shape
+    B, _, T = _dims(qkv, 3, "qkv")
+    _recurrent_shapes(p, B, T, qkv, gate, beta, conv_weight, conv_state_in, None, o)
+    _shape(S_snap, (B, T, p.num_v_heads, p.head_k_dim, p.head_v_dim), "S_snap")
+    T_prev = _dims(S_prev, 5, "S_prev")[1]
+    _shape(S_prev, (B, T_prev, p.num_v_heads, p.head_k_dim, p.head_v_dim), "S_prev")
+    _shape(slot, (B,), "slot")
+    _fusion_shapes(p, fusion, (B, T, p.num_v_heads, p.head_v_dim))
     _call("gdn_verify_block_slots", ctypes.byref(p.c()), _fusion_ref(p, fusion), B, T, _ptr(qkv),
           _ptr(gate), _ptr(beta), _ptr(conv_weight), _ptr(conv_state_in), _ptr(S_prev),
           S_prev.shape[1], _ptr(slot), _ptr(S_snap), _ptr(o), _stream(stream))
@@ -258,7 +332,14 @@ def gdn_verify_commit(p: GdnParams, accept_len, qkv, conv_state_in, S_snap, conv
         _expect(t, p.torch_dtype, n)
     _expect(S_snap, torch.float32, "S_snap")
     _expect(S_out, torch.float32, "S_out")
-    B, _, T = qkv.shape
+    B, _, T = _dims(qkv, 3, "qkv")
+    win = (B, p.D, p.conv_kernel - 1)
+    _shape(accept_len, (B,), "accept_len")
+    _shape(qkv, (B, p.D, T), "qkv")
+    _shape(conv_state_in, win, "conv_state_in")
+    _shape(conv_state_out, win, "conv_state_out")
+    _shape(S_snap, (B, T, p.num_v_heads, p.head_k_dim, p.head_v_dim), "S_snap")
+    _shape(S_out, (B, p.num_v_heads, p.head_k_dim, p.head_v_dim), "S_out")
     _call("gdn_verify_commit", ctypes.byref(p.c()), B, T, _ptr(accept_len), _ptr(qkv),
           _ptr(conv_state_in), _ptr(S_snap), _ptr(conv_state_out), _ptr(S_out), _stream(stream))
 
@@ -276,8 +357,9 @@ def gdn_prefill(p: GdnParams, qkv, gate, beta, conv_weight, conv_state_in, conv_
     _expect(S, torch.float32, "S")
     _expect(o, torch.float32, "o")
     _expect(cu_seqlens, torch.int32, "cu_seqlens")
-    B, _, L = qkv.shape
-    N = S.shape[0]
+    B, _, L = _dims(qkv, 3, "qkv")
+    N = _dims(S, 4, "S")[0]
+    _prefill_shapes(p, B, L, N, qkv, gate, beta, conv_weight, conv_state_in, conv_state_out, S, o, cu_seqlens)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _call("gdn_prefill", ctypes.byref(p.c()), B, L, _ptr(qkv), _ptr(gate), _ptr(beta),
           _ptr(conv_weight), _ptr(conv_state_in), _ptr(conv_state_out), _ptr(S), _ptr(o),
@@ -294,8 +376,10 @@ def gdn_prefill_ex(p: GdnParams, fusion: GdnFusion | None, qkv, gate, beta, conv
     _expect(S, torch.float32, "S")
     _expect(o, torch.float32, "o")
     _expect(cu_seqlens, torch.int32, "cu_seqlens")
-    B, _, L = qkv.shape
-    N = S.shape[0]
+    B, _, L = _dims(qkv, 3, "qkv")
+    N = _dims(S, 4, "S")[0]
+    _prefill_shapes(p, B, L, N, qkv, gate, beta, conv_weight, conv_state_in, conv_state_out, S, o, cu_seqlens)
+    _fusion_shapes(p, fusion, (B, L, p.num_v_heads, p.head_v_dim))
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _call("gdn_prefill_ex", ctypes.byref(p.c()), _fusion_ref(p, fusion), B, L, _ptr(qkv),
           _ptr(gate), _ptr(beta), _ptr(conv_weight), _ptr(conv_state_in), _ptr(conv_state_out),
