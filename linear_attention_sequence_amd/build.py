@@ -1,10 +1,14 @@
-"""Build libgdn.so (the HIP kernels and the C ABI of include/gdn.h) for gfx950.
+"""Build libgdn.so (the HIP kernels and the C ABI of include/gdn.h) and
+libgdn_ceiling.so (the measurement kernels of include/gdn_ceiling.h) for gfx950.
 
 Run as `python -m linear_attention_sequence_amd.build` or call build(). The
-library is written next to this file; nothing is installed elsewhere.
+libraries are written next to this file, with build_info.json (the commit and
+source digest they were built from); nothing is installed elsewhere.
 """
 from __future__ import annotations
 
+import hashlib
+import json
 import os
 import shutil
 import subprocess
@@ -16,6 +20,9 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libgdn.so")
 SOURCES = ["gdn_api.cpp", "gdn_recurrent.hip", "gdn_conv.hip", "gdn_prefill.hip", "gdn_prefill_mfma.hip"]
+CEILING_LIB = os.path.join(HERE, "libgdn_ceiling.so")
+CEILING_SOURCES = ["gdn_ceiling.hip"]
+BUILD_INFO = os.path.join(HERE, "build_info.json")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -33,15 +40,45 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP library cannot be built")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into libgdn.so (always recompiles)."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
+def source_digest() -> str:
+    """SHA-256 (16 hex digits) over every source and header the libraries are built from."""
+    h = hashlib.sha256()
+    files = sorted(os.listdir(CSRC)) + sorted(os.listdir(INCLUDE))
+    for name in files:
+        path = os.path.join(CSRC if os.path.exists(os.path.join(CSRC, name)) else INCLUDE, name)
+        if os.path.isfile(path) and name.endswith((".hip", ".cpp", ".hpp", ".h")):
+            h.update(name.encode())
+            with open(path, "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _git_commit() -> str | None:
+    try:
+        out = subprocess.run(["git", "-C", ROOT, "describe", "--always", "--dirty", "--abbrev=12"],
+                             capture_output=True, text=True, timeout=10)
+        return out.stdout.strip() or None
+    except (OSError, subprocess.SubprocessError):
+        return None
+
+
+def _compile(sources, out, verbose):
+    srcs = [os.path.join(CSRC, s) for s in sources]
+    tmp = out + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile libgdn.so and libgdn_ceiling.so (always recompiles)."""
+    _compile(SOURCES, LIB, verbose)
+    _compile(CEILING_SOURCES, CEILING_LIB, verbose)
+    with open(BUILD_INFO, "w") as f:
+        json.dump({"commit": _git_commit(), "source_digest": source_digest(),
+                   "hipcc_flags": " ".join(HIPCC_FLAGS)}, f)
     return LIB
 
 

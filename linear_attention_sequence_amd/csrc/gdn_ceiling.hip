@@ -1,0 +1,151 @@
+// Measurement kernels: achievable HBM read / write / copy rates and the MFMA
+// throughput of the device (see include/gdn_ceiling.h). Each is the simplest form that
+// keeps the unit under test saturated: 16-byte accesses with several in flight per
+// thread for memory, eight independent accumulator chains per wave for MFMA.
+#include "gdn_ceiling.h"
+
+#include <hip/hip_runtime.h>
+
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
+
+__global__ __launch_bounds__(kThreads) void read_kernel(const f32x4* __restrict__ src, size_t n, float* sink) {
+    const size_t stride = static_cast<size_t>(gridDim.x) * kThreads;
+    size_t i = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x;
+    unsigned acc = 0;
+    for (; i + (kUnroll - 1) * stride < n; i += kUnroll * stride) {
+        f32x4 v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) v[u] = src[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            acc ^= __float_as_uint(v[u].x) ^ __float_as_uint(v[u].y) ^ __float_as_uint(v[u].z) ^ __float_as_uint(v[u].w);
+    }
+    for (; i < n; i += stride) {
+        const f32x4 v = src[i];
+        acc ^= __float_as_uint(v.x) ^ __float_as_uint(v.y) ^ __float_as_uint(v.z) ^ __float_as_uint(v.w);
+    }
+    if (acc == 0x7fc00001u) sink[blockIdx.x] = __uint_as_float(acc);   // a NaN payload finite data never makes
+}
+
+template <bool NT>
+__global__ __launch_bounds__(kThreads) void write_kernel(f32x4* __restrict__ dst, size_t n) {
+    const size_t stride = static_cast<size_t>(gridDim.x) * kThreads;
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    for (size_t i = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x; i < n; i += stride) {
+        if constexpr (NT) __builtin_nontemporal_store(z, dst + i);
+        else dst[i] = z;
+    }
+}
+
+template <bool NT>
+__global__ __launch_bounds__(kThreads) void copy_kernel(const f32x4* __restrict__ src, f32x4* __restrict__ dst, size_t n) {
+    const size_t stride = static_cast<size_t>(gridDim.x) * kThreads;
+    size_t i = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x;
+    for (; i + (kUnroll - 1) * stride < n; i += kUnroll * stride) {
+        f32x4 v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) v[u] = src[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            if constexpr (NT) __builtin_nontemporal_store(v[u], dst + i + u * stride);
+            else dst[i + u * stride] = v[u];
+        }
+    }
+    for (; i < n; i += stride) {
+        if constexpr (NT) __builtin_nontemporal_store(src[i], dst + i);
+        else dst[i] = src[i];
+    }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void mfma_kernel(float* sink, int iters) {
+    const int lane = threadIdx.x & 63;
+    f32x4 acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (DT == 0) {
+        f16x8 a, b;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            a[e] = static_cast<_Float16>((lane + e) * 0.001f);
+            b[e] = static_cast<_Float16>((lane - e) * 0.001f);
+        }
+        for (int it = 0; it < iters; ++it)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[j], 0, 0, 0);
+    } else {
+        bf16x8 a, b;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            a[e] = static_cast<__bf16>((lane + e) * 0.001f);
+            b[e] = static_cast<__bf16>((lane - e) * 0.001f);
+        }
+        for (int it = 0; it < iters; ++it)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s += acc[j].x + acc[j].y + acc[j].z + acc[j].w;
+    if (s == -1.2345e30f) sink[blockIdx.x] = s;   // never true for these operands
+}
+
+bool grid_ok(int grid) { return grid >= 1 && grid <= (1 << 20); }
+bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+int launched() { return hipGetLastError() == hipSuccess ? 0 : 2; }
+
+}  // namespace
+
+extern "C" {
+
+int gdn_ceiling_read(const void* src, size_t bytes, float* sink, int grid, void* stream) {
+    if (!src || !sink || !grid_ok(grid) || bytes == 0 || bytes % 64 != 0 || !al16(src)) return 1;
+    read_kernel<<<grid, kThreads, 0, static_cast<hipStream_t>(stream)>>>(static_cast<const f32x4*>(src), bytes / 16, sink);
+    return launched();
+}
+
+int gdn_ceiling_write(void* dst, size_t bytes, int nontemporal, int grid, void* stream) {
+    if (!dst || !grid_ok(grid) || bytes == 0 || bytes % 64 != 0 || !al16(dst)) return 1;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (nontemporal) write_kernel<true><<<grid, kThreads, 0, s>>>(static_cast<f32x4*>(dst), bytes / 16);
+    else write_kernel<false><<<grid, kThreads, 0, s>>>(static_cast<f32x4*>(dst), bytes / 16);
+    return launched();
+}
+
+int gdn_ceiling_copy(const void* src, void* dst, size_t bytes, int nontemporal, int grid, void* stream) {
+    if (!src || !dst || !grid_ok(grid) || bytes == 0 || bytes % 64 != 0 || !al16(src) || !al16(dst)) return 1;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+    if (a < b + bytes && b < a + bytes) return 1;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const f32x4* sp = static_cast<const f32x4*>(src);
+    f32x4* dp = static_cast<f32x4*>(dst);
+    if (nontemporal) copy_kernel<true><<<grid, kThreads, 0, s>>>(sp, dp, bytes / 16);
+    else copy_kernel<false><<<grid, kThreads, 0, s>>>(sp, dp, bytes / 16);
+    return launched();
+}
+
+int gdn_ceiling_mfma(float* sink, int grid, int iters, int dtype, void* stream) {
+    if (!sink || !grid_ok(grid) || iters < 1 || (dtype != 0 && dtype != 1)) return 1;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (dtype == 0) mfma_kernel<0><<<grid, kThreads, 0, s>>>(sink, iters);
+    else mfma_kernel<1><<<grid, kThreads, 0, s>>>(sink, iters);
+    return launched();
+}
+
+int gdn_ceiling_device_info(int device, int* cus, int* clock_khz, int* mem_clock_khz, int* mem_bus_bits) {
+    if (!cus || !clock_khz || !mem_clock_khz || !mem_bus_bits) return 1;
+    if (hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) return 2;
+    if (hipDeviceGetAttribute(clock_khz, hipDeviceAttributeClockRate, device) != hipSuccess) return 2;
+    if (hipDeviceGetAttribute(mem_clock_khz, hipDeviceAttributeMemoryClockRate, device) != hipSuccess) return 2;
+    if (hipDeviceGetAttribute(mem_bus_bits, hipDeviceAttributeMemoryBusWidth, device) != hipSuccess) return 2;
+    return 0;
+}
+
+}  // extern "C"

@@ -15,8 +15,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 OK, NULL, SHAPE, DTYPE, UNSUP, ALIAS, WS, LAUNCH, ALIGN = range(9)
 
 
-def header_symbols():
-    with open(os.path.join(ROOT, "include", "gdn.h")) as f:
+def header_symbols(header="gdn.h"):
+    with open(os.path.join(ROOT, "include", header)) as f:
         text = f.read()
     return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(gdn_\w+)\s*\(", text, re.M)))
 
@@ -36,6 +36,27 @@ def test_header_lists_the_binding_exports():
 def test_library_exports_every_header_symbol(lib):
     for name in header_symbols():
         assert hasattr(lib, name), name
+
+
+def test_ceiling_library_exports_and_validation(lib):
+    """The measurement library of include/gdn_ceiling.h loads, exports its calls, and rejects
+    bad arguments (status 1) before any launch."""
+    path = os.path.join(os.path.dirname(gdn.LIB_PATH), "libgdn_ceiling.so")
+    assert os.path.exists(path)
+    cl = ctypes.CDLL(path)
+    names = header_symbols("gdn_ceiling.h")
+    assert names == ["gdn_ceiling_copy", "gdn_ceiling_device_info", "gdn_ceiling_mfma",
+                     "gdn_ceiling_read", "gdn_ceiling_write"]
+    for name in names:
+        assert hasattr(cl, name), name
+    V, I, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    cl.gdn_ceiling_copy.argtypes = [V, V, SZ, I, I, V]
+    cl.gdn_ceiling_mfma.argtypes = [V, I, I, I, V]
+    cl.gdn_ceiling_read.argtypes = [V, SZ, V, I, V]
+    assert cl.gdn_ceiling_copy(A(1), A(1), 1 << 20, 1, 1024, None) == 1           # overlap
+    assert cl.gdn_ceiling_copy(A(1), A(2), 100, 1, 1024, None) == 1               # not a multiple of 64
+    assert cl.gdn_ceiling_read(A(1), 1 << 20, A(2), 0, None) == 1                 # empty grid
+    assert cl.gdn_ceiling_mfma(A(1), 256, 10, 2, None) == 1                       # unknown dtype
 
 
 def test_status_strings_and_version(lib):
