@@ -124,7 +124,8 @@ def summary(per_ms):
     med = statistics.median(per_ms)
     spread = (max(per_ms) - min(per_ms)) / med if med > 0 else 0.0
     return {"reps": len(per_ms), "median_us": med * 1e3, "min_us": min(per_ms) * 1e3,
-            "max_us": max(per_ms) * 1e3, "spread": spread, "trustworthy": spread <= SPREAD_GUARD}
+            "max_us": max(per_ms) * 1e3, "spread": spread, "trustworthy": spread <= SPREAD_GUARD,
+            "per_rep_us": [round(x * 1e3, 2) for x in per_ms]}
 
 
 # ---------------------------------------------------------------------------
@@ -154,17 +155,21 @@ def measure_ceilings(torch, lib, cus):
     s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     P = lambda t: ctypes.c_void_p(t.data_ptr())
 
-    def rate(fn, units):
+    def rate(fn, units, per_rep=10):
+        """units per second: median over REPS of per_rep launches back to back (pipelined,
+        as the layer's kernels are timed)"""
+        fn()
         fn()
         torch.cuda.synchronize()
         ms = []
         for _ in range(REPS):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            fn()
+            for _ in range(per_rep):
+                fn()
             e1.record()
             torch.cuda.synchronize()
-            ms.append(e0.elapsed_time(e1))
+            ms.append(e0.elapsed_time(e1) / per_rep)
         return units / (statistics.median(ms) * 1e-3)
 
     def check(st):
@@ -181,13 +186,16 @@ def measure_ceilings(torch, lib, cus):
     for nt, key in ((1, "hbm_copy_nt_GBs"), (0, "hbm_copy_GBs")):
         out[key] = max(rate(lambda g=g: check(lib.gdn_ceiling_copy(P(src), P(dst), nbytes, nt, g, s)), 2 * nbytes)
                        for g in grids) / 1e9
-    iters = 4000
-    for dt, key in ((0, "mfma_f16_TFLOPs"), (1, "mfma_bf16_TFLOPs")):
-        out[key] = max(rate(lambda g=g: check(lib.gdn_ceiling_mfma(P(sink), g, iters, dt, s)), g * 4 * iters * 8 * 16384)
-                       for g in (cus * 2, cus * 4)) / 1e12
+    iters = 2000
+    for dt, key, fl in ((0, "mfma_f16_16x16x32_TFLOPs", 16384), (1, "mfma_bf16_16x16x32_TFLOPs", 16384),
+                        (2, "mfma_f16_32x32x16_TFLOPs", 32768), (3, "mfma_bf16_32x32x16_TFLOPs", 32768)):
+        out[key] = max(rate(lambda g=g, dt=dt: check(lib.gdn_ceiling_mfma(P(sink), g, iters, dt, s)),
+                            g * 4 * iters * 8 * fl, per_rep=3) for g in (cus * 2, cus * 4)) / 1e12
+    out["mfma_f16_TFLOPs"] = max(out["mfma_f16_16x16x32_TFLOPs"], out["mfma_f16_32x32x16_TFLOPs"])
     out["copy_best_GBs"] = max(out["hbm_copy_GBs"], out["hbm_copy_nt_GBs"])
     out["note"] = ("1 GiB per memory kernel (4x the Infinity Cache), grid sizes 4-32 workgroups per CU, "
-                   "median of 5 launches each, best grid; copy counts read + write bytes")
+                   "median of 5 repetitions of 10 launches back to back, best grid; copy counts read + write "
+                   "bytes; MFMA: 8 independent chains per wave, 2 or 4 workgroups of 4 waves per CU")
     del src, dst, sink
     torch.cuda.empty_cache()
     return out
@@ -499,7 +507,7 @@ def bench_prefill(args, torch, gdn, gi, ragged=False, fused=False):
 
 
 DEFAULT_STEPS = {"decode": (256, 32), "decode_fused": (256, 32), "verify": (50, 5), "commit": (50, 5),
-                 "prefill": (20, 3), "ragged": (10, 2), "prefill_fused": (20, 3), "ragged_fused": (10, 2),
+                 "prefill": (60, 4), "ragged": (20, 2), "prefill_fused": (60, 4), "ragged_fused": (20, 2),
                  "spec_round_copy": (50, 5), "spec_round_slots": (50, 5)}
 EXTRAS = ("prefill", "ragged", "verify", "commit")
 

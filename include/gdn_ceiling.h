@@ -21,9 +21,9 @@
 extern "C" {
 #endif
 
-/* Reads `bytes` from src with 16-byte loads (grid-stride, four loads in flight per
- * thread); sink [grid] receives one value per workgroup only in a case that never
- * happens with finite data, so it stays unwritten in practice but keeps the loads. */
+/* Reads `bytes` from src with 16-byte loads (grid-stride); sink [grid] receives one
+ * value per workgroup only in a case that never happens with finite data, so it stays
+ * unwritten in practice but keeps the loads. */
 int gdn_ceiling_read(const void* src, size_t bytes, float* sink, int grid, void* stream);
 
 /* Writes `bytes` of zeros to dst with 16-byte stores; nontemporal != 0 uses streaming
@@ -34,8 +34,9 @@ int gdn_ceiling_write(void* dst, size_t bytes, int nontemporal, int grid, void* 
 int gdn_ceiling_copy(const void* src, void* dst, size_t bytes, int nontemporal, int grid,
                      void* stream);
 
-/* `iters` rounds of 8 independent v_mfma_f32_16x16x32 products per wave (dtype 0: fp16
- * operands, 1: bf16 operands), 4 waves per workgroup: grid * 4 * iters * 8 * 16384 flops.
+/* `iters` rounds of 8 independent MFMA products per wave, 4 waves per workgroup. dtype
+ * 0: v_mfma_f32_16x16x32_f16, 1: ..._16x16x32_bf16 (16384 flops each: grid * 4 * iters *
+ * 8 * 16384 in all); 2: v_mfma_f32_32x32x16_f16, 3: ..._32x32x16_bf16 (32768 flops each).
  * sink [grid] as for gdn_ceiling_read. */
 int gdn_ceiling_mfma(float* sink, int grid, int iters, int dtype, void* stream);
 

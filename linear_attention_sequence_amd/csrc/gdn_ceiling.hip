@@ -13,25 +13,15 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
 
+// Plain grid-stride loops: consecutive lanes read consecutive 16-byte granules, each
+// wave streams contiguous memory (an unrolled form that kept four strided granules in
+// flight per thread measured slower).
 __global__ __launch_bounds__(kThreads) void read_kernel(const f32x4* __restrict__ src, size_t n, float* sink) {
     const size_t stride = static_cast<size_t>(gridDim.x) * kThreads;
-    size_t i = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x;
-    unsigned acc = 0;
-    for (; i + (kUnroll - 1) * stride < n; i += kUnroll * stride) {
-        f32x4 v[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) v[u] = src[i + u * stride];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-            acc ^= __float_as_uint(v[u].x) ^ __float_as_uint(v[u].y) ^ __float_as_uint(v[u].z) ^ __float_as_uint(v[u].w);
-    }
-    for (; i < n; i += stride) {
-        const f32x4 v = src[i];
-        acc ^= __float_as_uint(v.x) ^ __float_as_uint(v.y) ^ __float_as_uint(v.z) ^ __float_as_uint(v.w);
-    }
-    if (acc == 0x7fc00001u) sink[blockIdx.x] = __uint_as_float(acc);   // a NaN payload finite data never makes
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (size_t i = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x; i < n; i += stride) acc += src[i];
+    if (acc.x == -1.2345e30f) sink[blockIdx.x] = acc.y + acc.z + acc.w;   // never true for the data read
 }
 
 template <bool NT>
@@ -47,30 +37,25 @@ __global__ __launch_bounds__(kThreads) void write_kernel(f32x4* __restrict__ dst
 template <bool NT>
 __global__ __launch_bounds__(kThreads) void copy_kernel(const f32x4* __restrict__ src, f32x4* __restrict__ dst, size_t n) {
     const size_t stride = static_cast<size_t>(gridDim.x) * kThreads;
-    size_t i = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x;
-    for (; i + (kUnroll - 1) * stride < n; i += kUnroll * stride) {
-        f32x4 v[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) v[u] = src[i + u * stride];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            if constexpr (NT) __builtin_nontemporal_store(v[u], dst + i + u * stride);
-            else dst[i + u * stride] = v[u];
-        }
-    }
-    for (; i < n; i += stride) {
+    for (size_t i = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x; i < n; i += stride) {
         if constexpr (NT) __builtin_nontemporal_store(src[i], dst + i);
         else dst[i] = src[i];
     }
 }
 
+// DT: 0 fp16 16x16x32, 1 bf16 16x16x32, 2 fp16 32x32x16, 3 bf16 32x32x16 (all 8 or 16
+// accumulator registers per lane per chain, eight independent chains per wave)
 template <int DT>
 __global__ __launch_bounds__(kThreads) void mfma_kernel(float* sink, int iters) {
     const int lane = threadIdx.x & 63;
-    f32x4 acc[8];
+    constexpr bool BIG = DT >= 2;
+    typedef float acc_t __attribute__((ext_vector_type(BIG ? 16 : 4)));
+    acc_t acc[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (DT == 0) {
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int e = 0; e < (BIG ? 16 : 4); ++e) acc[j][e] = 0.f;
+    if constexpr (DT == 0 || DT == 2) {
         f16x8 a, b;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -79,7 +64,10 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(float* sink, int iters) 
         }
         for (int it = 0; it < iters; ++it)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[j], 0, 0, 0);
+            for (int j = 0; j < 8; ++j) {
+                if constexpr (BIG) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc[j], 0, 0, 0);
+                else acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[j], 0, 0, 0);
+            }
     } else {
         bf16x8 a, b;
 #pragma unroll
@@ -89,11 +77,16 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(float* sink, int iters) 
         }
         for (int it = 0; it < iters; ++it)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+            for (int j = 0; j < 8; ++j) {
+                if constexpr (BIG) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
+                else acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+            }
     }
     float s = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) s += acc[j].x + acc[j].y + acc[j].z + acc[j].w;
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int e = 0; e < (BIG ? 16 : 4); ++e) s += acc[j][e];
     if (s == -1.2345e30f) sink[blockIdx.x] = s;   // never true for these operands
 }
 
@@ -132,10 +125,12 @@ int gdn_ceiling_copy(const void* src, void* dst, size_t bytes, int nontemporal, 
 }
 
 int gdn_ceiling_mfma(float* sink, int grid, int iters, int dtype, void* stream) {
-    if (!sink || !grid_ok(grid) || iters < 1 || (dtype != 0 && dtype != 1)) return 1;
+    if (!sink || !grid_ok(grid) || iters < 1 || dtype < 0 || dtype > 3) return 1;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (dtype == 0) mfma_kernel<0><<<grid, kThreads, 0, s>>>(sink, iters);
-    else mfma_kernel<1><<<grid, kThreads, 0, s>>>(sink, iters);
+    else if (dtype == 1) mfma_kernel<1><<<grid, kThreads, 0, s>>>(sink, iters);
+    else if (dtype == 2) mfma_kernel<2><<<grid, kThreads, 0, s>>>(sink, iters);
+    else mfma_kernel<3><<<grid, kThreads, 0, s>>>(sink, iters);
     return launched();
 }
 

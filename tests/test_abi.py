@@ -56,7 +56,7 @@ def test_ceiling_library_exports_and_validation(lib):
     assert cl.gdn_ceiling_copy(A(1), A(1), 1 << 20, 1, 1024, None) == 1           # overlap
     assert cl.gdn_ceiling_copy(A(1), A(2), 100, 1, 1024, None) == 1               # not a multiple of 64
     assert cl.gdn_ceiling_read(A(1), 1 << 20, A(2), 0, None) == 1                 # empty grid
-    assert cl.gdn_ceiling_mfma(A(1), 256, 10, 2, None) == 1                       # unknown dtype
+    assert cl.gdn_ceiling_mfma(A(1), 256, 10, 4, None) == 1                       # unknown dtype
 
 
 def test_status_strings_and_version(lib):
@@ -230,3 +230,4 @@ def test_verify_slots_and_window_only_commit_validation(lib):
     assert commit(S_snap=None) == NULL                   # one of the two only
     assert commit(S_out=None) == NULL
     assert commit(S_snap=None, S_out=None, cout=A(5)) == ALIAS
+
