@@ -69,7 +69,8 @@ typedef enum {
     GDN_ERR_ALIAS = 5,        /* two buffers that must not overlap do */
     GDN_ERR_WORKSPACE = 6,    /* workspace NULL or smaller than gdn_prefill_workspace_size() */
     GDN_ERR_LAUNCH = 7,       /* the HIP runtime refused a kernel launch */
-    GDN_ERR_ALIGN = 8         /* a tensor pointer is not 16-byte aligned (workspace: 256) */
+    GDN_ERR_ALIGN = 8,        /* a tensor pointer is not 16-byte aligned (workspace: 256) */
+    GDN_ERR_TOO_LARGE = 9     /* gdn_prefill_ex_noalloc: the call needs more than its static scratch */
 } gdn_status;
 
 typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
@@ -264,6 +265,32 @@ gdn_status gdn_prefill_ex(const gdn_params* p, const gdn_fusion* fusion, int32_t
                           void* conv_state_out, float* S, float* o, const int32_t* cu_seqlens,
                           int32_t N, int32_t chunk, void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/*
+ * gdn_prefill_ex_noalloc — gdn_prefill_ex for callers that cannot allocate device memory
+ * (code under HIP graph capture, serving loops that must not call hipMalloc, harnesses
+ * that forbid it). Identical to gdn_prefill_ex, bit for bit, except that the workspace is
+ * a static array of 128 MiB (134217728 bytes) inside the library instead of a caller
+ * buffer; the caller still passes every input and output. The call allocates nothing
+ * (no hipMalloc, hipFree or allocating library routine); the array's address is looked
+ * up once per device (hipGetSymbolAddress, on the first call made with that device
+ * current) and the device holds the array until the process ends.
+ *   Limit: a call whose gdn_prefill_workspace_size() exceeds 134217728 bytes returns
+ *   GDN_ERR_TOO_LARGE and enqueues nothing (about 1,800 tokens at 16 K / 32 V heads of
+ *   dimension 128; gdn_prefill_workspace_size gives the exact need).
+ *   Sharing: every call on one device uses that device's one array. Calls that can run
+ *   at the same time on one device (different streams, or different host threads) race
+ *   on it and must be serialised by the caller; calls on one stream run in order and
+ *   are safe. The array's contents on entry do not matter (nothing in it is read before
+ *   the call writes it).
+ * Other arguments, layouts and errors as gdn_prefill_ex.
+ */
+gdn_status gdn_prefill_ex_noalloc(const gdn_params* p, const gdn_fusion* fusion, int32_t B,
+                                  int32_t L, const void* qkv, const void* gate, const void* beta,
+                                  const void* conv_weight, const void* conv_state_in,
+                                  void* conv_state_out, float* S, float* o,
+                                  const int32_t* cu_seqlens, int32_t N, int32_t chunk,
+                                  void* stream);
 
 #ifdef __cplusplus
 }

@@ -22,12 +22,13 @@ LIB_PATH = os.path.join(HERE, "libgdn.so")
 GDN_F32, GDN_BF16 = 0, 1
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_SHAPE", 3: "GDN_ERR_DTYPE",
           4: "GDN_ERR_UNSUPPORTED", 5: "GDN_ERR_ALIAS", 6: "GDN_ERR_WORKSPACE",
-          7: "GDN_ERR_LAUNCH", 8: "GDN_ERR_ALIGN"}
+          7: "GDN_ERR_LAUNCH", 8: "GDN_ERR_ALIGN", 9: "GDN_ERR_TOO_LARGE"}
 
 # every symbol include/gdn.h declares
 EXPORTS = ("gdn_status_string", "gdn_version", "gdn_conv1d_silu", "gdn_decode_step",
            "gdn_verify_block", "gdn_verify_commit", "gdn_prefill_workspace_size", "gdn_prefill",
-           "gdn_decode_step_ex", "gdn_verify_block_ex", "gdn_prefill_ex", "gdn_verify_block_slots")
+           "gdn_decode_step_ex", "gdn_verify_block_ex", "gdn_prefill_ex", "gdn_verify_block_slots",
+           "gdn_prefill_ex_noalloc")
 
 
 class GdnError(RuntimeError):
@@ -125,9 +126,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.gdn_verify_block_ex.argtypes = [PP, PF, I32, I32, V, V, V, V, V, V, V, V, V]
     lib.gdn_prefill_ex.argtypes = [PP, PF, I32, I32, V, V, V, V, V, V, V, V, V, I32, I32, V, SZ, V]
     lib.gdn_verify_block_slots.argtypes = [PP, PF, I32, I32, V, V, V, V, V, V, I32, V, V, V, V]
+    lib.gdn_prefill_ex_noalloc.argtypes = [PP, PF, I32, I32, V, V, V, V, V, V, V, V, V, I32, I32, V]
     for fn in ("gdn_conv1d_silu", "gdn_decode_step", "gdn_verify_block", "gdn_verify_commit",
                "gdn_prefill", "gdn_decode_step_ex", "gdn_verify_block_ex", "gdn_prefill_ex",
-               "gdn_verify_block_slots"):
+               "gdn_verify_block_slots", "gdn_prefill_ex_noalloc"):
         getattr(lib, fn).restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -384,6 +386,27 @@ def gdn_prefill_ex(p: GdnParams, fusion: GdnFusion | None, qkv, gate, beta, conv
     _call("gdn_prefill_ex", ctypes.byref(p.c()), _fusion_ref(p, fusion), B, L, _ptr(qkv),
           _ptr(gate), _ptr(beta), _ptr(conv_weight), _ptr(conv_state_in), _ptr(conv_state_out),
           _ptr(S), _ptr(o), _ptr(cu_seqlens), N, chunk, _ptr(workspace), ws_bytes, _stream(stream))
+
+
+def gdn_prefill_ex_noalloc(p: GdnParams, fusion: GdnFusion | None, qkv, gate, beta, conv_weight,
+                           conv_state_in, conv_state_out, S, o, cu_seqlens=None, chunk: int = 64,
+                           stream=None):
+    """gdn_prefill_ex with the library's static device scratch as its workspace (no
+    allocation: for callers that cannot allocate). Raises GdnError(GDN_ERR_TOO_LARGE) when
+    the prompt needs more than the 128 MiB scratch."""
+    for t, n in ((qkv, "qkv"), (gate, "gate"), (beta, "beta"), (conv_weight, "conv_weight"),
+                 (conv_state_in, "conv_state_in"), (conv_state_out, "conv_state_out")):
+        _expect(t, p.torch_dtype, n)
+    _expect(S, torch.float32, "S")
+    _expect(o, torch.float32, "o")
+    _expect(cu_seqlens, torch.int32, "cu_seqlens")
+    B, _, L = _dims(qkv, 3, "qkv")
+    N = _dims(S, 4, "S")[0]
+    _prefill_shapes(p, B, L, N, qkv, gate, beta, conv_weight, conv_state_in, conv_state_out, S, o, cu_seqlens)
+    _fusion_shapes(p, fusion, (B, L, p.num_v_heads, p.head_v_dim))
+    _call("gdn_prefill_ex_noalloc", ctypes.byref(p.c()), _fusion_ref(p, fusion), B, L, _ptr(qkv),
+          _ptr(gate), _ptr(beta), _ptr(conv_weight), _ptr(conv_state_in), _ptr(conv_state_out),
+          _ptr(S), _ptr(o), _ptr(cu_seqlens), N, chunk, _stream(stream))
 
 
 def prefill_workspace(p: GdnParams, B: int, L: int, N: int, chunk: int = 64, device="cuda"):

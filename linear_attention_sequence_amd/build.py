@@ -19,7 +19,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libgdn.so")
-SOURCES = ["gdn_api.cpp", "gdn_recurrent.hip", "gdn_conv.hip", "gdn_prefill.hip", "gdn_prefill_mfma.hip"]
+SOURCES = ["gdn_api.cpp", "gdn_recurrent.hip", "gdn_conv.hip", "gdn_prefill.hip", "gdn_prefill_mfma.hip",
+           "gdn_noalloc.hip"]
 CEILING_LIB = os.path.join(HERE, "libgdn_ceiling.so")
 CEILING_SOURCES = ["gdn_ceiling.hip"]
 BUILD_INFO = os.path.join(HERE, "build_info.json")

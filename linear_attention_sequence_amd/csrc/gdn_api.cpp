@@ -98,6 +98,7 @@ const char* gdn_status_string(gdn_status s) {
         case GDN_ERR_WORKSPACE: return "workspace missing or too small";
         case GDN_ERR_LAUNCH: return "kernel launch failed";
         case GDN_ERR_ALIGN: return "tensor pointer misaligned";
+        case GDN_ERR_TOO_LARGE: return "the call needs more than the library's static scratch (128 MiB)";
     }
     return "unknown status";
 }

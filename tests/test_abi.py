@@ -12,7 +12,7 @@ import linear_attention_sequence_amd as gdn
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-OK, NULL, SHAPE, DTYPE, UNSUP, ALIAS, WS, LAUNCH, ALIGN = range(9)
+OK, NULL, SHAPE, DTYPE, UNSUP, ALIAS, WS, LAUNCH, ALIGN, TOO_LARGE = range(10)
 
 
 def header_symbols(header="gdn.h"):
@@ -60,7 +60,7 @@ def test_ceiling_library_exports_and_validation(lib):
 
 
 def test_status_strings_and_version(lib):
-    for code in range(9):
+    for code in range(10):
         assert lib.gdn_status_string(code)
     assert lib.gdn_version() >= 10000
 
@@ -231,3 +231,17 @@ def test_verify_slots_and_window_only_commit_validation(lib):
     assert commit(S_out=None) == NULL
     assert commit(S_snap=None, S_out=None, cout=A(5)) == ALIAS
 
+
+def test_noalloc_prefill_rejects_prompts_beyond_its_scratch(lib):
+    """gdn_prefill_ex_noalloc checks the need against its 128 MiB static scratch before it
+    touches the GPU: a 4096-token prompt at 16/32 heads needs more and is refused."""
+    p = P()
+    need = lib.gdn_prefill_workspace_size(p, 1, 4096, 1, 64)
+    assert need > (128 << 20)
+    st = lib.gdn_prefill_ex_noalloc(p, None, 1, 4096, A(1), A(2), A(3), A(4), A(5), A(6), A(7), A(8),
+                                    None, 1, 64, None)
+    assert st == TOO_LARGE
+    assert b"static scratch" in lib.gdn_status_string(TOO_LARGE)
+    # invalid arguments are reported as gdn_prefill_ex reports them (need is 0 for them)
+    assert lib.gdn_prefill_ex_noalloc(p, None, 1, 64, A(1), A(2), A(3), A(4), A(5), A(6), A(7), A(8),
+                                      None, 1, 32, None) == UNSUP
