@@ -507,7 +507,7 @@ def bench_prefill(args, torch, gdn, gi, ragged=False, fused=False):
 
 
 DEFAULT_STEPS = {"decode": (256, 32), "decode_fused": (256, 32), "verify": (50, 5), "commit": (50, 5),
-                 "prefill": (60, 4), "ragged": (20, 2), "prefill_fused": (60, 4), "ragged_fused": (20, 2),
+                 "prefill": (60, 20), "ragged": (20, 10), "prefill_fused": (60, 20), "ragged_fused": (20, 10),
                  "spec_round_copy": (50, 5), "spec_round_slots": (50, 5)}
 EXTRAS = ("prefill", "ragged", "verify", "commit")
 

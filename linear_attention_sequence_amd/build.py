@@ -66,7 +66,9 @@ def _git_commit() -> str | None:
 def _compile(sources, out, verbose):
     srcs = [os.path.join(CSRC, s) for s in sources]
     tmp = out + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
+    # only the C ABI is exported (csrc/exports.map)
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, *srcs,
+           "-Wl,--version-script=" + os.path.join(CSRC, "exports.map"), "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)

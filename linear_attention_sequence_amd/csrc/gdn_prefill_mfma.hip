@@ -40,35 +40,23 @@
 #include "gdn_common.hpp"
 #include "gdn_launch.hpp"
 #include "gdn_mfma.hpp"
+#include "gdn_prefill_plan.hpp"
 
 namespace gdn {
 namespace pf2 {
 
-constexpr int C = 64;      // chunk length
-constexpr int D = 128;     // head dim (dk == dv)
+using plan::C;
+using plan::COEF;
+using plan::D;
+using plan::kidx;
+using plan::kMaxSeg;
+using plan::kpos;
+using plan::seg_begin;
+using plan::Stage;
 constexpr int TT = 32;     // front-end tile (tokens): 19 KB of LDS, eight workgroups per CU
 constexpr int RAW = TT + 5;  // raw tile row stride (floats): TT + 3 used, odd stride against bank conflicts
-// per (chunk, V head) coefficients: [0, C) exp(Gam_t); [C, 2C) exp(Gam_last - Gam_t);
-// 2C: exp(Gam_last); 2C + 1: 2^uexp, the scale of the stored U; padded to 40 granules
-constexpr int COEF = 160;
 
-// Contraction order of the carry's A operands. Its B operands are accumulator tiles
-// (a lane holds rows 4 g .. 4 g + 3 of every 16-row tile), so the eight k slots of
-// lane group g in step ks are the logical indices 32 ks + 4 g + (0..3) and
-// 32 ks + 16 + 4 g + (0..3). W and q_hat (contracted over the state's rows, i.e.
-// the key features), and K^T and P (contracted over tokens) are stored in that
-// order, so that a lane's eight halfs are one 16-byte read: logical index
-// k = 32 b + 16 h + 4 g + e sits at position kpos(k) = 32 b + 8 g + 4 h + e, and
-// position p holds kidx(p). k_hat is stored the same way (the Gram products only
-// need q_hat and k_hat to agree).
-__host__ __device__ __forceinline__ constexpr int kpos(int k) {
-    return (k & ~31) | (((k >> 2) & 3) << 3) | (((k >> 4) & 1) << 2) | (k & 3);
-}
-__host__ __device__ __forceinline__ constexpr int kidx(int p) {
-    return (p & ~31) | (((p >> 2) & 1) << 4) | (((p >> 3) & 3) << 2) | (p & 3);
-}
-static_assert(kidx(kpos(45)) == 45 && kpos(kidx(45)) == 45 && kpos(16) == 4 && kpos(4) == 8, "k order");
-
+// Device view of the workspace (regions and sizes from plan::layout).
 struct Ws {
     _Float16* qh;   // [Ttot, Hk, D] q_hat (normalised, scaled), features in k order
     _Float16* kh;   // [Ttot, Hk, D] k_hat, features in k order
@@ -90,73 +78,27 @@ struct Ws {
     size_t bytes;
 };
 
-static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
-
-static int max_chunks(int B, int L, int N, bool ragged) {
-    const int per = (L + C - 1) / C;
-    return ragged ? per + N : B * per;
-}
-
-// Unpacked prompts whose heads leave the CUs idle run the carry in segments (see
-// carry_kernel). Its second pass runs 2 (nseg - 1) half-head workgroups per head and
-// its first 2 nseg - 3 whole-head ones, each pass in one round of the CUs; a segment
-// averages at least kMinSegChunks chunks, and nseg >= 3 (with two segments the two
-// passes are one chain cut in two).
-constexpr int kMaxSeg = 8;
-constexpr int kMinSegChunks = 4;
-constexpr int kLayoutCUs = 256;   // the workspace is sized for this many CUs at most
-static int segments(int B, int L, int N, int Hv, bool ragged, int cus) {
-    if (ragged || B != N || N <= 0 || Hv <= 0) return 1;
-    const long long heads = static_cast<long long>(N) * Hv;
-    long long ks = cus / (2 * heads) + 1;
-    ks = std::min<long long>(ks, kMaxSeg);
-    ks = std::min<long long>(ks, ((L + C - 1) / C) / kMinSegChunks);
-    return ks >= 3 ? static_cast<int>(ks) : 1;
-}
-
-// First chunk of segment j (0 <= j <= nseg) of a sequence of nch chunks. Segment 0
-// alone also forms its outputs in the first pass, at whole-head speed, so it gets
-// kSeg0 / 8 of the share of each other segment.
-constexpr int kSeg0 = 5;
-__host__ __device__ __forceinline__ int seg_begin(int nch, int nseg, int j) {
-    if (j <= 0) return 0;
-    if (j >= nseg) return nch;
-    const int den = kSeg0 + 8 * (nseg - 1);
-    return (nch * (kSeg0 + 8 * (j - 1)) + den / 2) / den;
-}
-
 static Ws layout(void* base, int B, int L, int N, int Hk, int Hv, bool ragged) {
+    const plan::Layout l = plan::layout(B, L, N, Hk, Hv, ragged);
+    char* b = static_cast<char*>(base);
+    auto at = [&](size_t off, size_t n) -> void* { return (b != nullptr && n > 0) ? b + off : nullptr; };
     Ws w;
-    const size_t T = static_cast<size_t>(B) * L;
-    const size_t nc = static_cast<size_t>(max_chunks(B, L, N, ragged));
-    size_t off = 0;
-    auto take = [&](size_t bytes) {
-        void* r = base ? static_cast<char*>(base) + off : nullptr;
-        off = align256(off + bytes);
-        return r;
-    };
-    w.qh = static_cast<_Float16*>(take(T * Hk * D * 2));
-    w.kh = static_cast<_Float16*>(take(T * Hk * D * 2));
-    w.vh = static_cast<_Float16*>(take(T * Hv * D * 2));
-    w.W = static_cast<_Float16*>(take(nc * Hv * C * D * 2));
-    w.U = static_cast<_Float16*>(take(nc * Hv * C * D * 2));
-    w.P = static_cast<_Float16*>(take(nc * Hv * C * C * 2));
-    w.KT = static_cast<_Float16*>(take(nc * Hk * D * C * 2));
-    w.coef = static_cast<float*>(take(nc * Hv * COEF * 4));
-    w.nseg = segments(B, L, N, Hv, ragged, kLayoutCUs);
+    w.qh = static_cast<_Float16*>(at(l.qh, l.n_qh));
+    w.kh = static_cast<_Float16*>(at(l.kh, l.n_kh));
+    w.vh = static_cast<_Float16*>(at(l.vh, l.n_vh));
+    w.W = static_cast<_Float16*>(at(l.W, l.n_W));
+    w.U = static_cast<_Float16*>(at(l.U, l.n_U));
+    w.P = static_cast<_Float16*>(at(l.P, l.n_P));
+    w.KT = static_cast<_Float16*>(at(l.KT, l.n_KT));
+    w.coef = static_cast<float*>(at(l.coef, l.n_coef));
+    w.Sent = static_cast<float*>(at(l.Sent, l.n_Sent));
+    w.Mhl = static_cast<_Float16*>(at(l.Mhl, l.n_Mhl));
+    w.Mexp = static_cast<int*>(at(l.Mexp, l.n_Mexp));
+    w.Rseg = static_cast<float*>(at(l.Rseg, l.n_Rseg));
+    w.nc_max = l.nc_max;
+    w.nseg = l.nseg;
     w.pass = 0;
-    w.Sent = w.Rseg = nullptr;
-    w.Mhl = nullptr;
-    w.Mexp = nullptr;
-    if (w.nseg > 1) {
-        const size_t tiles = static_cast<size_t>(N) * Hv * D * D;
-        w.Sent = static_cast<float*>(take(tiles * 4));
-        w.Mhl = static_cast<_Float16*>(take(static_cast<size_t>(w.nseg - 2) * tiles * 2 * 2));
-        w.Mexp = static_cast<int*>(take(static_cast<size_t>(w.nseg - 2) * N * Hv * (D / 16) * 4));
-        w.Rseg = static_cast<float*>(take(static_cast<size_t>(w.nseg - 2) * tiles * 4));
-    }
-    w.nc_max = static_cast<int>(nc);
-    w.bytes = off;
+    w.bytes = l.bytes;
     return w;
 }
 
@@ -516,25 +458,10 @@ __global__ __launch_bounds__(256, 4) void chunk_kernel(PrefillArgs a, Ws ws) {
     _Float16* KbT = reinterpret_cast<_Float16*>(region);
     _Float16* VbT = reinterpret_cast<_Float16*>(region + D * TS * 2);
 
-    // blockIdx -> (chunk, V head). The f V heads of a K head read the same keys and
-    // queries: they are dispatched 8 blockIdx apart, i.e. to one XCD, whose L2 then
-    // serves the second read; the tail that does not fill a group of 8 (chunk, K head)
-    // units is laid out unit-major.
+    // blockIdx -> (chunk, V head), the GQA pair of V heads on one XCD (plan::chunk_unit)
     const int f = a.Hv / a.Hk;
-    int u, hl;
-    {
-        const int units = ws.nc_max * a.Hk, grp = units / 8, full = 8 * f * grp;
-        const int b = blockIdx.x;
-        if (b < full) {
-            u = (b / (8 * f)) * 8 + b % 8;
-            hl = (b / 8) % f;
-        } else {
-            const int rem = b - full, tail = units - 8 * grp;
-            u = 8 * grp + rem % tail;
-            hl = rem / tail;
-        }
-    }
-    const int hk = u % a.Hk, id = u / a.Hk, h = hk * f + hl;
+    const plan::ChunkUnit cu = plan::chunk_unit(blockIdx.x, ws.nc_max, a.Hk, a.Hv);
+    const int hk = cu.hk, id = cu.id, h = cu.h;
     int n, c;
     Seg seg;
     if (id >= ws.nc_max || !find_chunk(id, a, &n, &c, &seg)) return;
@@ -823,22 +750,9 @@ __global__ __launch_bounds__(256, 4) void chunk_kernel(PrefillArgs a, Ws ws) {
 // ---- state carry ----------------------------------------------------------------------
 // A workgroup of NW waves owns CPW = NW * NTW * 16 columns of one head's state:
 // wave w owns the 16-column tiles [col0, col0 + 16 * NTW). A head is split over
-// 128 / CPW workgroups (more CUs when there are few sequences).
-//
-// One LDS stage holds, for one chunk and head, in 16-byte granules:
-//   W [64][16 granules]  Q [64][16]  KT [128][8]  P [64][8]  U^T [CPW][8] (this
-//   workgroup's columns, tokens along the row)  coefficients [40]
-// Granule j of row r sits at position j ^ (r mod rowgranules) of its row, which
-// spreads the 16 rows one MFMA operand read touches over the banks.
-template <int CPW>
-struct Stage {
-    static constexpr int W = 0, Q = 1024, KT = 2048, P = 3072, U = 3584;
-    static constexpr int UG = CPW / 8;                 // U^T rows per 8 (the region is 64 x UG granules)
-    static constexpr int CF = U + 64 * UG;
-    static constexpr int END = CF + COEF / 4;
-    static constexpr int INSTR = (END + 63) / 64;      // wave-wide 1 KB loads
-    static constexpr int BYTES = INSTR * 1024;
-};
+// 128 / CPW workgroups (more CUs when there are few sequences). The LDS stage of one
+// chunk (W, Q, K^T, P, this workgroup's columns of U^T, the coefficients) and the
+// row and granule each lane loads into it are plan::Stage, plan::load16, plan::load8.
 
 // Eight halfs of an A operand whose k slots (g, e) hold logical columns
 // 32ks + 4g + e (e < 4) and 32ks + 16 + 4g + (e - 4) (e >= 4): with the row stored in
@@ -878,47 +792,49 @@ __device__ __forceinline__ void issue_stage(const PrefillArgs& a, const Ws& ws, 
     const size_t pbase = (static_cast<size_t>(id) * a.Hv + h) * C * C;
     const size_t cfbase = (static_cast<size_t>(id) * a.Hv + h) * COEF;
     unsigned char* stage = g_stage + buf * SG::BYTES;
-    auto ld = [&](const void* src, int q) { __builtin_amdgcn_global_load_lds(src, stage + q * 1024, 16, 0, 0); };
-    // W and Q: 16 granules per row, an instruction covers rows 4q'..4q'+3
-    const int r16l = 4 * wave + (lane >> 4);                 // row of instruction i = 0
-    const int j16 = (lane & 15) ^ (r16l & 15);               // (4 * NW * i) is a multiple of 16
+    auto ld = [&](const void* src, int slot) { __builtin_amdgcn_global_load_lds(src, stage + slot * 1024, 16, 0, 0); };
+    static_assert(NW % 4 == 0, "plan::step16 / step8 keep the granule swizzle for nw a multiple of 4");
+    // W and Q: 16 granules per row, a load covers 4 rows (load i = load 0 + 4 NW i rows)
+    const plan::LaneLoad w0 = plan::load16(SG::W / 64, wave, lane), q0 = plan::load16(SG::Q / 64, wave, lane);
     if constexpr ((PARTS & ST_W) != 0) {
-        const _Float16* src = ws.W + wbase + r16l * D + 8 * j16;
+        const _Float16* src = ws.W + wbase + w0.row * D + 8 * w0.gran;
 #pragma unroll
-        for (int i = 0; i < 16 / NW; ++i) ld(src + i * 4 * NW * D, SG::W / 64 + wave + NW * i);
+        for (int i = 0; i < 16 / NW; ++i) ld(src + i * 4 * NW * D, plan::step16(w0, NW, i).slot);
     }
 #pragma unroll
     for (int i = 0; i < ((PARTS & ST_Q) ? 16 / NW : 0); ++i) {   // rows past the end: a finite row
-        const int r = r16l + 4 * NW * i;
-        const int rr = r < nt ? r : nt - 1;
-        ld(ws.qh + ((tok0 + rr) * a.Hk + hk) * D + 8 * j16, SG::Q / 64 + wave + NW * i);
+        const plan::LaneLoad l = plan::step16(q0, NW, i);
+        const int rr = l.row < nt ? l.row : nt - 1;
+        ld(ws.qh + ((tok0 + rr) * a.Hk + hk) * D + 8 * l.gran, l.slot);
     }
-    // KT and P: 8 granules per row, an instruction covers rows 8q'..8q'+7
-    const int r8l = 8 * wave + (lane >> 3);
-    const int j8 = (lane & 7) ^ (lane >> 3);                  // row & 7 == lane >> 3
+    // KT and P: 8 granules per row, a load covers 8 rows (load i = load 0 + 8 NW i rows)
     if constexpr ((PARTS & ST_KT) != 0) {
-        const _Float16* src = ws.KT + ktbase + r8l * C + 8 * j8;
+        const plan::LaneLoad k0 = plan::load8(SG::KT / 64, wave, lane);
+        const _Float16* src = ws.KT + ktbase + k0.row * C + 8 * k0.gran;
 #pragma unroll
-        for (int i = 0; i < 16 / NW; ++i) ld(src + i * 8 * NW * C, SG::KT / 64 + wave + NW * i);
+        for (int i = 0; i < 16 / NW; ++i) ld(src + i * 8 * NW * C, plan::step8(k0, NW, i).slot);
     }
     if constexpr ((PARTS & ST_P) != 0) {
-        const _Float16* src = ws.P + pbase + r8l * C + 8 * j8;
+        const plan::LaneLoad p0 = plan::load8(SG::P / 64, wave, lane);
+        const _Float16* src = ws.P + pbase + p0.row * C + 8 * p0.gran;
 #pragma unroll
-        for (int i = 0; i < 8 / NW; ++i) ld(src + i * 8 * NW * C, SG::P / 64 + wave + NW * i);
+        for (int i = 0; i < 8 / NW; ++i) ld(src + i * 8 * NW * C, plan::step8(p0, NW, i).slot);
     }
     // this workgroup's rows of U^T (its columns): 8 granules per row, like KT
     if constexpr ((PARTS & ST_U) != 0) {
-        const _Float16* src = ws.U + wbase + static_cast<size_t>(ucol0 + r8l) * C + 8 * j8;
+        const plan::LaneLoad u0 = plan::load8(SG::U / 64, wave, lane);
+        const _Float16* src = ws.U + wbase + static_cast<size_t>(ucol0 + u0.row) * C + 8 * u0.gran;
 #pragma unroll
-        for (int i = 0; i < CPW / 8 / NW; ++i) ld(src + i * 8 * NW * C, SG::U / 64 + wave + NW * i);
+        for (int i = 0; i < CPW / 8 / NW; ++i) ld(src + i * 8 * NW * C, plan::step8(u0, NW, i).slot);
     }
     // coefficients (40 granules; lanes past the end land in padding)
     if constexpr ((PARTS & ST_CF) != 0) {
-        if (wave == NW - 1) ld(ws.coef + cfbase + 4 * (lane < COEF / 4 ? lane : 0), SG::CF / 64);
+        if (wave == NW - 1)
+            ld(ws.coef + cfbase + 4 * (lane < COEF / 4 ? lane : 0), SG::CF / 64);
     }
 }
 
-constexpr int kSortMax = 256;   // packed sequences ranked by length in every carry workgroup
+using plan::kSortMax;
 constexpr int kZeroTile = -(1 << 20);   // state-map tile exponent marking a tile that is exactly zero
 
 // Sequence of rank r when the N packed sequences are ordered by decreasing length
@@ -961,23 +877,9 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
     // U = 0: M_j), neither forming outputs. Pass 2 carries segments 1 .. nseg - 1 with
     // outputs, each from its entry state S_j = M_{j-1} S_{j-1} + R_{j-1}, which its
     // workgroups form first on their own columns; the last one ends in the final state.
-    const int NK = ws.nseg <= 1 ? 1 : (ws.pass == 1 ? 2 * ws.nseg - 3 : ws.nseg - 1);   // kinds per head
-    // blockIdx -> (slice, slot): the NK * NS slices of a slot are dispatched together
-    // and 8 blockIdx apart, i.e. on one XCD, sharing its L2 for the operands they
-    // read; the tail that does not fill a group of 8 slots is laid out slice-major.
-    int slice = 0, slot = blockIdx.x;
-    if (NK * NS > 1) {
-        const int nsl = NK * NS, grp = nh / 8, full = 8 * nsl * grp;
-        if (static_cast<int>(blockIdx.x) < full) {
-            const int w = blockIdx.x % (8 * nsl);
-            slice = w / 8;
-            slot = (blockIdx.x / (8 * nsl)) * 8 + w % 8;
-        } else {
-            const int rem = blockIdx.x - full, tail = nh - 8 * grp;
-            slice = rem / tail;
-            slot = 8 * grp + rem % tail;
-        }
-    }
+    const int NK = plan::carry_kinds(ws.nseg, ws.pass);   // kinds per head
+    const plan::Slice sl = plan::carry_slice(blockIdx.x, NK * NS, nh);
+    const int slice = sl.slice, slot = sl.slot;
     const int cs = slice % NS;
     const int kind = slice / NS;
     const int h = slot % a.Hv;
@@ -1000,44 +902,34 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
     int nch = chunks_of(seg);
     if (base + nch > ws.nc_max) nch = ws.nc_max - base;   // only malformed cu_seqlens get here
     if (nch <= 0) return;
-    // this workgroup's job: segment sj (chunks [cb, ce)), its entry state, whether it
-    // forms outputs and loads U, and where its end state goes (nowhere if null)
+    // this workgroup's job (plan::carry_job): segment sj (chunks [cb, ce)), its entry
+    // state, whether it forms outputs and loads U, and where its end state goes
     const size_t tile = (static_cast<size_t>(n) * a.Hv + h) * D * D;
     const size_t tiles = static_cast<size_t>(a.N) * a.Hv * D * D;
-    enum { FROM, ZERO, IDENT };
-    int sj = 0, entry = FROM;
-    bool outs = true, useU = true;
+    const plan::Job job = plan::carry_job(ws.nseg, ws.pass, kind);
+    const int sj = job.sj, entry = job.entry;
+    const bool outs = job.outs, useU = job.useU;
     const float* Sin = a.S + tile;
     float* Send = a.S + tile;
-    size_t mapo = 0;                                     // XMAP: its map's offset in Mhl, Mexp (+ 1)
+    size_t mapo = 0;                                     // XMAP: its map's index in Mhl, Mexp (+ 1)
+    if (job.from_sent) Sin = ws.Sent + tile;             // pass 2: S_1; later entry states are formed below
+    if (job.end == plan::kEndSent) Send = ws.Sent + tile;
+    else if (job.end == plan::kEndRseg) Send = ws.Rseg + static_cast<size_t>(sj - 1) * tiles + tile;
+    else if (job.end == plan::kEndNone) Send = nullptr;
+    if (job.map >= 0) mapo = (static_cast<size_t>(job.map) * tiles + tile) / (D * D) + 1;
     int m0 = 0;                                          // pass 2: maps 1 .. m0 are not needed
-    if (ws.nseg > 1) {
-        if (ws.pass == 1) {
-            if (kind == 0) {
-                Send = ws.Sent + tile;
-            } else {
-                sj = (kind + 1) / 2;
-                outs = false;
-                const size_t off = static_cast<size_t>(sj - 1) * tiles + tile;
-                if (kind & 1) { entry = ZERO; Send = ws.Rseg + off; }
-                else { entry = IDENT; useU = false; Send = nullptr; mapo = off / (D * D) + 1; }
-            }
-        } else {
-            sj = kind + 1;
-            Sin = ws.Sent + tile;                        // S_1; later entry states are formed below
-            if (sj != ws.nseg - 1) Send = nullptr;
-            // A segment whose state map is exactly zero (it has decayed below fp32's range)
-            // ends in R whatever its entry state: the chain restarts after the latest one,
-            // with the same result, bit for bit, as multiplying through it.
-            for (int i = sj - 1; i >= 1 && m0 == 0; --i) {
-                const int* ek = ws.Mexp + (static_cast<size_t>(i - 1) * a.N * a.Hv + n * a.Hv + h) * (D / 16);
-                bool zero = true;
+    if (job.from_sent) {
+        // A segment whose state map is exactly zero (it has decayed below fp32's range)
+        // ends in R whatever its entry state: the chain restarts after the latest one,
+        // with the same result, bit for bit, as multiplying through it.
+        for (int i = sj - 1; i >= 1 && m0 == 0; --i) {
+            const int* ek = ws.Mexp + (static_cast<size_t>(i - 1) * a.N * a.Hv + n * a.Hv + h) * (D / 16);
+            bool zero = true;
 #pragma unroll
-                for (int t = 0; t < D / 16; ++t) zero = zero && ek[t] == kZeroTile;
-                if (zero) {
-                    m0 = i;
-                    Sin = ws.Rseg + static_cast<size_t>(i - 1) * tiles + tile;
-                }
+            for (int t = 0; t < D / 16; ++t) zero = zero && ek[t] == kZeroTile;
+            if (zero) {
+                m0 = i;
+                Sin = ws.Rseg + static_cast<size_t>(i - 1) * tiles + tile;
             }
         }
     }
@@ -1053,7 +945,7 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 16 * mt + 4 * g + e, j = col0 + 16 * nt + r16;
-                S[mt][nt][e] = entry == FROM ? Sin[i * D + j] : (entry == IDENT && i == j ? 1.f : 0.f);
+                S[mt][nt][e] = entry == plan::kFromState ? Sin[i * D + j] : (entry == plan::kFromIdentity && i == j ? 1.f : 0.f);
                 smax = fmaxf(smax, fabsf(S[mt][nt][e]));
             }
 
@@ -1115,11 +1007,11 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
                 auto issue_map = [&](int i) {
                     const _Float16* src = ws.Mhl + (static_cast<size_t>(m0 + i - 1) * nhh + head) * 2 * D * D;
                     unsigned char* dst = g_stage + ((i - 1) & 1) * SG::BYTES;
+                    const plan::LaneLoad l0 = plan::load16(0, wave, lane);
+                    const _Float16* s0 = src + l0.row * D + 8 * l0.gran;
 #pragma unroll
-                    for (int k = 0; k < MI; ++k) {
-                        const int q = wave + NW * k, r = 4 * q + (lane >> 4), jg = (lane & 15) ^ (r & 15);
-                        __builtin_amdgcn_global_load_lds(src + r * D + 8 * jg, dst + q * 1024, 16, 0, 0);
-                    }
+                    for (int k = 0; k < MI; ++k)
+                        __builtin_amdgcn_global_load_lds(s0 + k * 4 * NW * D, dst + plan::step16(l0, NW, k).slot * 1024, 16, 0, 0);
                 };
                 issue_map(1);
                 if (np >= 2) issue_map(2);
@@ -1516,7 +1408,7 @@ static hipError_t launch_mfma_t(const PrefillArgs& a, int in_dtype, hipStream_t 
     const bool ragged = a.cu != nullptr;
     pf2::Ws ws = pf2::layout(a.ws, a.B, a.L, a.N, a.Hk, a.Hv, ragged);
     const int cus = device_cu_count();
-    ws.nseg = std::min(ws.nseg, pf2::segments(a.B, a.L, a.N, a.Hv, ragged, cus));   // within the workspace
+    ws.nseg = plan::carry_plan(a.B, a.L, a.N, a.Hv, ragged, cus).nseg;   // within the workspace's
     void* args[] = {const_cast<PrefillArgs*>(&a), &ws};
     hipError_t e;
     const long long fblocks = static_cast<long long>(a.B) * ((a.L + pf2::TT - 1) / pf2::TT) * (2 * a.Hk + a.Hv);
@@ -1531,29 +1423,16 @@ static hipError_t launch_mfma_t(const PrefillArgs& a, int in_dtype, hipStream_t 
                             dim3(256), args, 0, stream);
         if (e != hipSuccess) return e;
     }
-    const long long heads = static_cast<long long>(a.N) * a.Hv;
-    if (heads > 0) {
-        // Split each head over two workgroups when that still fits one round of the
-        // CUs, and for packed prompts when it fits two: their chains differ in length
-        // and, dispatched longest first, the halves finish sooner than whole heads
-        // (8 sequences of 512..8192 tokens: 567 -> 544 us, bound by the longest chain)
-        const bool split = 2 * heads <= cus || (a.cu != nullptr && a.N <= pf2::kSortMax && heads <= cus);
-        if (ws.nseg > 1) {
-            // segmented carry: pass 1 on whole-head workgroups (2 nseg - 3 per head), pass 2
-            // (which forms the later entry states itself) on half-head workgroups with a
-            // loader wave (2 (nseg - 1) per head)
-            pf2::Ws w1 = ws, w2 = ws;
-            w1.pass = 1;
-            w2.pass = 2;
-            void* args1[] = {const_cast<PrefillArgs*>(&a), &w1};
-            void* args2[] = {const_cast<PrefillArgs*>(&a), &w2};
-            static_assert(kWholeNTW == 1, "the first pass writes the state maps from one column tile per wave");
-            e = launch_carry<kWholeNTW, kWholeNW>(args1, (2 * ws.nseg - 3) * heads, stream);
-            if (e != hipSuccess) return e;
-            e = launch_carry<1, 4, true>(args2, (ws.nseg - 1) * heads, stream);
-        } else {
-            e = split ? launch_carry<1, 4, true>(args, heads, stream) : launch_carry<kWholeNTW, kWholeNW>(args, heads, stream);
-        }
+    // carry launches (plan::carry_plan: whole-head or half-head workgroups, one pass or
+    // the two of the segmented carry)
+    const plan::CarryPlan cp = plan::carry_plan(a.B, a.L, a.N, a.Hv, ragged, cus);
+    for (int i = 0; i < cp.count; ++i) {
+        pf2::Ws wp = ws;
+        wp.pass = cp.l[i].pass;
+        void* argp[] = {const_cast<PrefillArgs*>(&a), &wp};
+        static_assert(kWholeNTW == 1, "the first pass writes the state maps from one column tile per wave");
+        e = cp.l[i].half ? launch_carry<1, 4, true>(argp, cp.l[i].units, stream)
+                         : launch_carry<kWholeNTW, kWholeNW>(argp, cp.l[i].units, stream);
         if (e != hipSuccess) return e;
     }
     if (fblocks > 0) return hipSuccess;   // the front kernel wrote the conv state
