@@ -217,8 +217,10 @@ gdn_status gdn_verify_block_slots(const gdn_params* p, const gdn_fusion* fusion,
 
 /*
  * gdn_prefill_workspace_size — bytes of device workspace gdn_prefill needs for
- * these sizes (an upper bound that holds whatever cu_seqlens contains).
- * Returns 0 when the arguments are invalid or unsupported.
+ * these sizes and p->in_dtype (bf16 inputs at head dim 128 take the MFMA path,
+ * whose workspace is smaller than the fp32 path's); an upper bound that holds
+ * whatever cu_seqlens contains. Returns 0 when the arguments are invalid or
+ * unsupported.
  */
 size_t gdn_prefill_workspace_size(const gdn_params* p, int32_t B, int32_t L, int32_t N,
                                   int32_t chunk);
@@ -276,8 +278,9 @@ gdn_status gdn_prefill_ex(const gdn_params* p, const gdn_fusion* fusion, int32_t
  * up once per device (hipGetSymbolAddress, on the first call made with that device
  * current) and the device holds the array until the process ends.
  *   Limit: a call whose gdn_prefill_workspace_size() exceeds 134217728 bytes returns
- *   GDN_ERR_TOO_LARGE and enqueues nothing (about 1,800 tokens at 16 K / 32 V heads of
- *   dimension 128; gdn_prefill_workspace_size gives the exact need).
+ *   GDN_ERR_TOO_LARGE and enqueues nothing (with bf16 inputs about 2,800 tokens at
+ *   16 K / 32 V heads of dimension 128; gdn_prefill_workspace_size gives the exact
+ *   need).
  *   Sharing: every call on one device uses that device's one array. Calls that can run
  *   at the same time on one device (different streams, or different host threads) race
  *   on it and must be serialised by the caller; calls on one stream run in order and

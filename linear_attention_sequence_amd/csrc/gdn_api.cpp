@@ -289,7 +289,8 @@ size_t gdn_prefill_workspace_size(const gdn_params* p, int32_t B, int32_t L, int
     if (prefill_check_sizes(p, B, L, N, chunk, B == 1) != GDN_OK &&
         prefill_check_sizes(p, B, L, N, chunk, false) != GDN_OK)
         return 0;
-    return gdn::prefill_workspace_bytes(B, L, N, p->num_k_heads, p->num_v_heads, p->head_k_dim, chunk);
+    return gdn::prefill_workspace_bytes(B, L, N, p->num_k_heads, p->num_v_heads, p->head_k_dim, chunk,
+                                        p->in_dtype);
 }
 
 gdn_status gdn_prefill(const gdn_params* p, int32_t B, int32_t L, const void* qkv,
@@ -322,7 +323,7 @@ gdn_status gdn_prefill_ex(const gdn_params* p, const gdn_fusion* fusion, int32_t
         return GDN_ERR_NULL;
     if (!aligned(S, 16) || (o && !aligned(o, 16))) return GDN_ERR_ALIGN;
     const size_t need = gdn::prefill_workspace_bytes(B, L, N, p->num_k_heads, p->num_v_heads,
-                                                     p->head_k_dim, chunk);
+                                                     p->head_k_dim, chunk, p->in_dtype);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return GDN_ERR_WORKSPACE;
     if (need > 0 && !aligned(workspace, 256)) return GDN_ERR_ALIGN;
     const long long D = dimD(p);

@@ -79,7 +79,7 @@ hipError_t launch_recurrent(const RecArgs& a, int in_dtype, int d, hipStream_t s
 hipError_t launch_commit(const CommitArgs& a, int in_dtype, int d, hipStream_t stream);
 hipError_t launch_conv1d_silu(const ConvArgs& a, int in_dtype, hipStream_t stream);
 hipError_t launch_conv_state(const ConvArgs& a, int in_dtype, hipStream_t stream);
-size_t prefill_workspace_bytes(int B, int L, int N, int Hk, int Hv, int d, int chunk);
+size_t prefill_workspace_bytes(int B, int L, int N, int Hk, int Hv, int d, int chunk, int in_dtype);
 hipError_t launch_prefill(const PrefillArgs& a, int in_dtype, int d, hipStream_t stream);
 size_t prefill_mfma_workspace_bytes(int B, int L, int N, int Hk, int Hv);
 hipError_t launch_prefill_mfma(const PrefillArgs& a, int in_dtype, hipStream_t stream);

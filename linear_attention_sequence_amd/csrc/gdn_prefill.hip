@@ -77,17 +77,13 @@ static PrefillWs ws_layout(void* base, int B, int L, int N, int Hk, int Hv, int 
     return w;
 }
 
-size_t prefill_workspace_bytes(int B, int L, int N, int Hk, int Hv, int d, int chunk) {
-    // sized for the ragged layout and the plain one, and at d = 128 for both the
-    // MFMA path (bf16 inputs) and the fp32 path (fp32 inputs)
+size_t prefill_workspace_bytes(int B, int L, int N, int Hk, int Hv, int d, int chunk, int in_dtype) {
+    // the layout of the path the call takes (MFMA for bf16 inputs at d = 128, else the
+    // fp32 path), sized for the ragged layout and the plain one
+    if (d == 128 && in_dtype == 1) return prefill_mfma_workspace_bytes(B, L, N, Hk, Hv);
     const size_t a = ws_layout(nullptr, B, L, N, Hk, Hv, d, chunk, true).bytes;
     const size_t b = ws_layout(nullptr, B, L, N, Hk, Hv, d, chunk, false).bytes;
-    size_t m = a > b ? a : b;
-    if (d == 128) {
-        const size_t c = prefill_mfma_workspace_bytes(B, L, N, Hk, Hv);
-        m = c > m ? c : m;
-    }
-    return m;
+    return a > b ? a : b;
 }
 
 // Number of chunks of sequence n.

@@ -165,9 +165,10 @@ def test_prefill_validation(lib):
     assert prefill(o=A(7)) == ALIAS
     assert prefill(ws=A(8)) == ALIAS
     assert prefill(B=2, N=2, cu=A(11)) == SHAPE
-    # ragged: B == 1 with N sequences; the workspace bound covers both packings
-    need_r = lib.gdn_prefill_workspace_size(p, 1, 4096, 8, 64)
-    assert need_r >= need
+    # the bound for (B = 1, L, N = 1) serves the call either unpacked or through
+    # cu_seqlens: one byte less is refused both ways
+    assert prefill(N=1, cu=A(11), ws_bytes=need - 1) == WS
+    assert lib.gdn_prefill_workspace_size(p, 1, 4096, 8, 64) > 0
     assert prefill(N=0, cu=A(11)) == OK
 
 
@@ -234,11 +235,11 @@ def test_verify_slots_and_window_only_commit_validation(lib):
 
 def test_noalloc_prefill_rejects_prompts_beyond_its_scratch(lib):
     """gdn_prefill_ex_noalloc checks the need against its 128 MiB static scratch before it
-    touches the GPU: a 4096-token prompt at 16/32 heads needs more and is refused."""
+    touches the GPU: an 8192-token prompt at 16/32 heads needs more and is refused."""
     p = P()
-    need = lib.gdn_prefill_workspace_size(p, 1, 4096, 1, 64)
+    need = lib.gdn_prefill_workspace_size(p, 1, 8192, 1, 64)
     assert need > (128 << 20)
-    st = lib.gdn_prefill_ex_noalloc(p, None, 1, 4096, A(1), A(2), A(3), A(4), A(5), A(6), A(7), A(8),
+    st = lib.gdn_prefill_ex_noalloc(p, None, 1, 8192, A(1), A(2), A(3), A(4), A(5), A(6), A(7), A(8),
                                     None, 1, 64, None)
     assert st == TOO_LARGE
     assert b"static scratch" in lib.gdn_status_string(TOO_LARGE)

@@ -70,9 +70,11 @@ def test_noalloc_prefill_two_calls_match_the_workspace_call():
 
 def test_noalloc_prefill_refuses_prompts_beyond_its_scratch():
     p = params(SH, "bf16")
-    inp = layer_inputs(SH, 1, 4096, 63, "bf16")
+    L = 8192
+    assert gdn.gdn_prefill_workspace_size(p, 1, L, 1) > (128 << 20)
+    inp = layer_inputs(SH, 1, L, 63, "bf16")
     args = [dev(inp[k], "bf16") for k in ("qkv", "gate", "beta", "w", "conv0")]
     S = dev(inp["S0"])
-    o = torch.empty((1, 4096, SH.Hv, SH.dv), device="cuda")
+    o = torch.empty((1, L, SH.Hv, SH.dv), device="cuda")
     with pytest.raises(gdn.GdnError, match="GDN_ERR_TOO_LARGE"):
         gdn.gdn_prefill_ex_noalloc(p, None, *args, torch.empty_like(args[4]), S, o)
