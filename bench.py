@@ -216,7 +216,8 @@ def run_metadata(torch, lib):
     except OSError:
         meta["rocm"] = None
     pr = torch.cuda.get_device_properties(0)
-    meta.update({"gpu": pr.name, "arch": pr.gcnArchName, "cus": pr.multi_processor_count,
+    meta.update({"gpu": pr.name or f"AMD Instinct, {pr.gcnArchName.split(':')[0]}",   # the box reports no name
+                 "arch": pr.gcnArchName, "cus": pr.multi_processor_count,
                  "hbm_bytes": pr.total_memory, "torch": torch.__version__, "python": platform.python_version()})
     if lib is not None:
         v = [ctypes.c_int() for _ in range(4)]
@@ -429,7 +430,8 @@ def bench_verify(args, torch, gdn, gi, commit=False, rnd=None):
 # prefill (L = 4096) and ragged prefill (8 sequences)
 # ---------------------------------------------------------------------------
 PREFILL_FLOP_PER_TOKEN_HEAD = 163840   # bf16-MFMA-shaped work of the chunked form, C = 64, d = 128
-PREFILL_SOURCES = ["gdn_prefill_mfma.hip", "gdn_prefill.hip", "gdn_common.hpp", "gdn_mfma.hpp", "gdn_api.cpp"]
+PREFILL_SOURCES = ["gdn_prefill_mfma.hip", "gdn_prefill_plan.hpp", "gdn_prefill.hip", "gdn_common.hpp", "gdn_mfma.hpp",
+                   "gdn_api.cpp"]
 
 
 def prefill_bytes(sh, L, N, fused):
