@@ -23,6 +23,9 @@ SOURCES = ["gdn_api.cpp", "gdn_recurrent.hip", "gdn_conv.hip", "gdn_prefill.hip"
            "gdn_noalloc.hip"]
 CEILING_LIB = os.path.join(HERE, "libgdn_ceiling.so")
 CEILING_SOURCES = ["gdn_ceiling.hip"]
+# the MFMA throughput loops keep their accumulators in VGPRs: with AGPR accumulators the
+# register allocator moved the 16x16x32 chains between registers every iteration
+CEILING_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 BUILD_INFO = os.path.join(HERE, "build_info.json")
 
 HIPCC_FLAGS = [
@@ -63,11 +66,11 @@ def _git_commit() -> str | None:
         return None
 
 
-def _compile(sources, out, verbose):
+def _compile(sources, out, verbose, extra=()):
     srcs = [os.path.join(CSRC, s) for s in sources]
     tmp = out + ".tmp"
     # only the C ABI is exported (csrc/exports.map)
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, *srcs,
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, *srcs,
            "-Wl,--version-script=" + os.path.join(CSRC, "exports.map"), "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -78,7 +81,7 @@ def _compile(sources, out, verbose):
 def build(verbose: bool = False) -> str:
     """Compile libgdn.so and libgdn_ceiling.so (always recompiles)."""
     _compile(SOURCES, LIB, verbose)
-    _compile(CEILING_SOURCES, CEILING_LIB, verbose)
+    _compile(CEILING_SOURCES, CEILING_LIB, verbose, CEILING_FLAGS)
     with open(BUILD_INFO, "w") as f:
         json.dump({"commit": _git_commit(), "source_digest": source_digest(),
                    "hipcc_flags": " ".join(HIPCC_FLAGS)}, f)
