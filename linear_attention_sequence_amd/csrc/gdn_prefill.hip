@@ -498,7 +498,9 @@ static hipError_t launch_prefill_core(const PrefillArgs& a, int in_dtype, int d,
 hipError_t launch_prefill(const PrefillArgs& a, int in_dtype, int d, hipStream_t stream) {
     if (a.chunk != 64) return hipErrorInvalidValue;
     hipError_t e = launch_prefill_core(a, in_dtype, d, stream);
-    if (e == hipSuccess && a.fu.z != nullptr) e = launch_prefill_epilogue(a, in_dtype, d, stream);
+    // the MFMA path (bf16, d = 128) applies the gated RMSNorm in its carry's output store
+    const bool norm_fused = d == 128 && in_dtype == 1;
+    if (e == hipSuccess && a.fu.z != nullptr && !norm_fused) e = launch_prefill_epilogue(a, in_dtype, d, stream);
     return e;
 }
 

@@ -855,9 +855,12 @@ __device__ int sequence_of_rank(const PrefillArgs& a, int r) {
     return s_pick;
 }
 
-template <int NTW, int NW, bool LW>
+template <int NTW, int NW, bool LW, bool NORM>
 __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws ws) {
     constexpr int CPW = NW * NTW * 16;
+    // NORM: the gated RMSNorm of each token's head row is applied before its store,
+    // which needs the whole row (all 128 columns) in this workgroup
+    static_assert(!NORM || (NTW == 1 && NW * 16 == D && !LW), "a fused norm needs a whole-head workgroup");
     // One wave per SIMD (NW <= 4) leaves registers to hold a whole phase's operands:
     // their LDS reads are then issued ahead of the phase's MFMAs under one wait (a
     // scheduling barrier keeps them there). With two waves per SIMD the waves hide
@@ -968,7 +971,7 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
         }
     };
     const int np = (ws.nseg > 1 && ws.pass == 2) ? sj - 1 - m0 : 0;   // maps m0 + 1 .. sj - 1 (see below)
-    const bool prologue = LW && NTW == 1 && np > 0;
+    const bool prologue = NTW == 1 && np > 0;
     if ((!LW || loader) && cb < ce && !prologue) {
 #pragma unroll
         for (int w = LW ? 0 : wave; w < (LW ? NW : wave + 1); ++w)
@@ -982,9 +985,9 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
     // chunk's stage is issued once they are done with. The products split both operands
     // (hi*hi + hi*lo + lo*hi in fp32, close to an fp32 product), so these entry states
     // are as good as a carried one.
-    if constexpr (LW && NTW == 1) {
+    if constexpr (NTW == 1) {
         if (np > 0) {
-            if (loader) {
+            if (LW && loader) {
                 for (int i = 0; i < np; ++i) {
                     __syncthreads();                        // map i is in LDS
                     __syncthreads();                        // every compute wave is done with it
@@ -1003,7 +1006,7 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
                 // map m0 + i -> stage buffer (i - 1) & 1 as [hi rows, lo rows][16 granules], granule j of
                 // row r at position j ^ (r % 16): wave-wide 1 KB loads of 4 rows, this wave's
                 // instructions wave, wave + NW, ... (16 each)
-                constexpr int MI = 2 * D / 4 / NW;
+                constexpr int MI = 2 * D / 4 / NW;   // 16 with 4 compute waves, 8 with 8
                 auto issue_map = [&](int i) {
                     const _Float16* src = ws.Mhl + (static_cast<size_t>(m0 + i - 1) * nhh + head) * 2 * D * D;
                     unsigned char* dst = g_stage + ((i - 1) & 1) * SG::BYTES;
@@ -1016,9 +1019,10 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
                 issue_map(1);
                 if (np >= 2) issue_map(2);
                 for (int i = 1; i <= np; ++i) {
-                    // map i has landed (this wave's part; map i + 1 may still be in flight)
-                    static_assert(MI == 16, "the wait below counts one map's instructions per wave");
-                    if (i + 1 <= np) __builtin_amdgcn_s_waitcnt((16 >> 4) << 14 | 0x7 << 4 | 0xF << 8);
+                    // map i has landed (this wave's part; map i + 1's MI loads may still be in
+                    // flight): vmcnt(MI), its bits [3:0] and [15:14], expcnt and lgkmcnt at their maxima
+                    static_assert(MI < 64, "vmcnt holds 6 bits");
+                    if (i + 1 <= np) __builtin_amdgcn_s_waitcnt((MI >> 4) << 14 | (MI & 15) | 0x7 << 4 | 0xF << 8);
                     else __builtin_amdgcn_s_waitcnt(0x7 << 4 | 0xF << 8);
                     __syncthreads();                        // ... and every wave's
                     const unsigned char* mb = g_stage + ((i - 1) & 1) * SG::BYTES;
@@ -1075,6 +1079,10 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
                 for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) smax = fmaxf(smax, fabsf(S[mt][0][e]));
+                // without a loader wave each wave issues its share of the first chunk's
+                // stage itself, into buffer 0, which the last barrier above freed
+                if (!LW && cb < ce)
+                    issue_all(base + cb, row_tok + static_cast<size_t>(cb) * C, min(C, seg.len - cb * C), 0, wave);
             }
         }
     }
@@ -1092,6 +1100,39 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
         }
         return;
     }
+    // Fused gated RMSNorm (NORM): y = w * o / rms(o) * z * sigmoid(z) over each token's
+    // 128 columns. A lane holds 4 columns of 4 tokens of a chunk's output; it keeps
+    // them (and their gates, loaded while the chunk computes) until every wave's
+    // share of the tokens' sums of squares is in LDS, i.e. past the next chunk's
+    // first barrier (or one more barrier after the last chunk), and then stores y.
+    __shared__ float s_ss[NORM ? 2 : 1][NORM ? C : 1][NORM ? NW : 1];   // [chunk parity][token][wave]
+    f32x4v ov[4], wn{};
+    uint2 zr[4];
+    float* pob = nullptr;                                // pending chunk's first output row
+    int pnt = 0;                                         // ... and its token count
+    const bf16_t* zg = static_cast<const bf16_t*>(a.fu.z);
+    if constexpr (NORM) {
+        const bf16_t* wg = static_cast<const bf16_t*>(a.fu.norm_w) + col0 + 4 * g;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wn[e] = to_f32(wg[e]);
+    }
+    auto bf_lo = [](unsigned u) { return __uint_as_float(u << 16); };
+    auto bf_hi = [](unsigned u) { return __uint_as_float(u & 0xffff0000u); };
+    auto finish = [&](int buf) {   // the pending chunk's y (sums of squares in s_ss[buf])
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const int t = 16 * mt + r16;
+            const f32x4v p0 = *reinterpret_cast<const f32x4v*>(&s_ss[buf][t][0]);
+            const f32x4v p1 = *reinterpret_cast<const f32x4v*>(&s_ss[buf][t][4]);
+            const float ss = ((p0[0] + p0[1]) + (p0[2] + p0[3])) + ((p1[0] + p1[1]) + (p1[2] + p1[3]));
+            const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / D) + a.fu.norm_eps);
+            const float z[4] = {bf_lo(zr[mt].x), bf_hi(zr[mt].x), bf_lo(zr[mt].y), bf_hi(zr[mt].y)};
+            f32x4v y;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = wn[e] * (ov[mt][e] * inv) * (z[e] * sigmoid_hw(z[e]));
+            if (t < pnt) __builtin_nontemporal_store(y, reinterpret_cast<f32x4v*>(pob + t * ts + col0 + 4 * g));
+        }
+    };
     // The next chunk's stage is issued in three parts spread over this chunk's
     // phases (each part before the phase that would otherwise wait on the memory
     // pipeline), so that the vector-memory issue queue never backs up the MFMA work.
@@ -1109,6 +1150,9 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
                 issue_stage<CPW, NW, ST_W | ST_U | ST_CF>(a, ws, id + 1, tok0 + C, ntn, h, hk, ucol0, sb_, wave, lane);
             else
                 issue_stage<CPW, NW, ST_W | ST_CF>(a, ws, id + 1, tok0 + C, ntn, h, hk, ucol0, sb_, wave, lane);
+        }
+        if constexpr (NORM) {
+            if (outs && c > cb) finish((c - 1 - cb) & 1);
         }
         const unsigned char* st = g_stage + ((c - cb) & 1) * SG::BYTES;
         const _Float16* Wl = reinterpret_cast<const _Float16*>(st + SG::W * 16);
@@ -1229,6 +1273,16 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
         // with a loader wave: 256 registers, and each tile's reads then overlap the
         // previous tile's MFMAs: 237 -> 225 us at L = 4096), else inside the loop
         constexpr int OB = LW ? 1 : 4;
+        if constexpr (NORM) {
+            if (outs) {   // this chunk's gates (rows past the end: a row inside)
+                const bf16_t* zb = zg + (tok0 * a.Hv + h) * D + col0 + 4 * g;
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    const int t = min(16 * mt + r16, ntc - 1);
+                    zr[mt] = *reinterpret_cast<const uint2*>(zb + t * ts);
+                }
+            }
+        }
         if (outs) {
 #pragma unroll
         for (int m0 = 0; m0 < 4; m0 += OB) {
@@ -1268,8 +1322,15 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
                 const float eg = cf[t] * iS;
                 const float4 v = make_float4(__fmaf_rn(eg, a1[0][0], iD * a2[0][0]), __fmaf_rn(eg, a1[0][1], iD * a2[0][1]),
                                              __fmaf_rn(eg, a1[0][2], iD * a2[0][2]), __fmaf_rn(eg, a1[0][3], iD * a2[0][3]));
-                if (full || t < ntc)
+                if constexpr (NORM) {   // held for the norm; this wave's 16 columns of the token's sum of squares
+                    ov[mt] = f32x4v{v.x, v.y, v.z, v.w};
+                    float ss = __fmaf_rn(v.w, v.w, __fmaf_rn(v.z, v.z, __fmaf_rn(v.y, v.y, v.x * v.x)));
+                    ss += __shfl_xor(ss, 16);
+                    ss += __shfl_xor(ss, 32);
+                    if (g == 0) s_ss[(c - cb) & 1][t][wave] = ss;
+                } else if (full || t < ntc) {
                     __builtin_nontemporal_store(f32x4v{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4v*>(obase + t * ts + col0 + 4 * g));
+                }
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -1284,6 +1345,10 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
             }
         }
         }
+        }
+        if constexpr (NORM) {
+            pob = obase;
+            pnt = ntc;
         }
         if (!LW && more)
             issue_stage<CPW, NW, ST_KT>(a, ws, id + 1, tok0 + C, ntn, h, hk, ucol0, sb_, wave, lane);
@@ -1316,6 +1381,12 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
                     S[mt][nt][e] = __fmaf_rn(egl, S[mt][nt][e], iD * acc[nt][e]);
                     smax = fmaxf(smax, fabsf(S[mt][nt][e]));
                 }
+        }
+    }
+    if constexpr (NORM) {
+        if (outs && ce > cb) {
+            __syncthreads();                                 // every wave's sums of the last chunk
+            finish((ce - 1 - cb) & 1);
         }
     }
     // end state: S, or in segmented mode an entry state, R_j or M_j (or nothing). M_j
@@ -1390,13 +1461,13 @@ static int device_cu_count() {
     return cached[dev];
 }
 
-// The carry configurations: (tiles per wave, waves per workgroup).
-template <int NTW, int NW, bool LW = false>
+// The carry configurations: (tiles per wave, waves per workgroup, loader wave, fused norm).
+template <int NTW, int NW, bool LW = false, bool NORM = false>
 static hipError_t launch_carry(void** args, long long heads, hipStream_t stream) {
     constexpr int CPW = NW * NTW * 16;
     constexpr size_t lds = 2 * pf2::Stage<CPW>::BYTES;
-    static_assert(lds <= 160 * 1024, "LDS of one CU");
-    const void* k = reinterpret_cast<const void*>(&pf2::carry_kernel<NTW, NW, LW>);
+    static_assert(lds + 8 * 1024 <= 160 * 1024, "LDS of one CU (the stages and the kernel's static arrays)");
+    const void* k = reinterpret_cast<const void*>(&pf2::carry_kernel<NTW, NW, LW, NORM>);
     // dynamic LDS above 64 KB must be allowed per kernel before its first launch
     static const hipError_t allowed = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (allowed != hipSuccess) return allowed;
@@ -1424,15 +1495,18 @@ static hipError_t launch_mfma_t(const PrefillArgs& a, int in_dtype, hipStream_t 
         if (e != hipSuccess) return e;
     }
     // carry launches (plan::carry_plan: whole-head or half-head workgroups, one pass or
-    // the two of the segmented carry)
-    const plan::CarryPlan cp = plan::carry_plan(a.B, a.L, a.N, a.Hv, ragged, cus);
+    // the two of the segmented carry); with the gated RMSNorm fused into the output
+    // store, whole-head workgroups only
+    const bool norm = a.fu.z != nullptr;
+    const plan::CarryPlan cp = plan::carry_plan(a.B, a.L, a.N, a.Hv, ragged, cus, norm);
     for (int i = 0; i < cp.count; ++i) {
         pf2::Ws wp = ws;
         wp.pass = cp.l[i].pass;
         void* argp[] = {const_cast<PrefillArgs*>(&a), &wp};
         static_assert(kWholeNTW == 1, "the first pass writes the state maps from one column tile per wave");
-        e = cp.l[i].half ? launch_carry<1, 4, true>(argp, cp.l[i].units, stream)
-                         : launch_carry<kWholeNTW, kWholeNW>(argp, cp.l[i].units, stream);
+        if (norm) e = launch_carry<kWholeNTW, kWholeNW, false, true>(argp, cp.l[i].units, stream);
+        else if (cp.l[i].half) e = launch_carry<1, 4, true>(argp, cp.l[i].units, stream);
+        else e = launch_carry<kWholeNTW, kWholeNW>(argp, cp.l[i].units, stream);
         if (e != hipSuccess) return e;
     }
     if (fblocks > 0) return hipSuccess;   // the front kernel wrote the conv state
@@ -1440,6 +1514,7 @@ static hipError_t launch_mfma_t(const PrefillArgs& a, int in_dtype, hipStream_t 
     return launch_conv_state(ca, in_dtype, stream);
 }
 
+// Runs the gated RMSNorm of gdn_prefill_ex too when a.fu.z is set (fused into the carry).
 hipError_t launch_prefill_mfma(const PrefillArgs& a, int in_dtype, hipStream_t stream) {
     // bf16 inputs only: fp32 inputs take the fp32 path, whose tolerance the fp16 operands would not meet
     return in_dtype == 1 ? launch_mfma_t<bf16_t>(a, in_dtype, stream) : hipErrorInvalidValue;

@@ -189,7 +189,9 @@ constexpr Job carry_job(int nseg, int pass, int kind) {
 // packed prompts when it fits two (their chains differ in length and, dispatched
 // longest first, the halves finish sooner). The segmented carry runs pass 1 on
 // whole-head workgroups (2 nseg - 3 per head) and pass 2 on half-head ones
-// (2 (nseg - 1) per head).
+// (2 (nseg - 1) per head). With `whole` (the gated RMSNorm fused into the output
+// store, which needs all 128 columns of a token in one workgroup) every launch uses
+// whole-head workgroups: pass 2 then runs nseg - 1 per head.
 constexpr int kSortMax = 256;   // packed sequences ranked by length in every carry workgroup
 struct CarryLaunch {
     bool half;        // half-head workgroups (4 waves + loader) or whole-head ones (8 waves)
@@ -197,7 +199,7 @@ struct CarryLaunch {
     long long units;  // heads x kinds: workgroups = units * (half ? 2 : 1)
 };
 struct CarryPlan { int nseg, count; CarryLaunch l[2]; };
-constexpr CarryPlan carry_plan(int B, int L, int N, int Hv, bool ragged, int cus) {
+constexpr CarryPlan carry_plan(int B, int L, int N, int Hv, bool ragged, int cus, bool whole = false) {
     CarryPlan p{};
     p.nseg = imin(segments(B, L, N, Hv, ragged, kLayoutCUs), segments(B, L, N, Hv, ragged, cus));
     const long long heads = static_cast<long long>(N) * Hv;
@@ -205,11 +207,11 @@ constexpr CarryPlan carry_plan(int B, int L, int N, int Hv, bool ragged, int cus
     if (p.nseg > 1) {
         p.count = 2;
         p.l[0] = CarryLaunch{false, 1, (2 * p.nseg - 3) * heads};
-        p.l[1] = CarryLaunch{true, 2, (p.nseg - 1) * heads};
+        p.l[1] = CarryLaunch{!whole, 2, (p.nseg - 1) * heads};
     } else {
         const bool split = 2 * heads <= cus || (ragged && N <= kSortMax && heads <= cus);
         p.count = 1;
-        p.l[0] = CarryLaunch{split, 0, heads};
+        p.l[0] = CarryLaunch{split && !whole, 0, heads};
     }
     return p;
 }

@@ -7,12 +7,14 @@
 // buffer it indexes and every LDS slot against its stage region, counts the barriers
 // each wave role executes, and replays the prologue's hand-encoded vmcnt waits against
 // the loads each compute wave has issued. Segment 0's weight is swept over 4..7 eighths
-// (the kernels use 5). Exit status 0 and a summary line when every check holds; the
-// first violation is printed and the exit status is 1.
+// (the kernels use 5), and every configuration is replayed twice: as planned, and with
+// the gated RMSNorm fused (whole-head workgroups only, the second pass included, and
+// the gate rows read beside the outputs). Exit status 0 and a summary line when every
+// check holds; the first violation is printed and the exit status is 1.
 //
 // Build and run: g++ -O2 -std=c++17 -I linear_attention_sequence_amd/csrc tests/carry_model.cpp
 // An argument plants one mistake the model must report (exit status 1): wait32 (the
-// prologue waits for 32 outstanding loads instead of 16), loader_barrier (the loader wave
+// prologue waits for twice the loads of one map), loader_barrier (the loader wave
 // executes one barrier more than the compute waves), tail_row (the last chunk's output
 // rows run one past the sequence), seg0_wide (segment 0's weight empties later segments).
 #include "gdn_prefill_plan.hpp"
@@ -128,8 +130,9 @@ size_t check_map_geometry(int NW, int BYTES) {
     return top;
 }
 
-void model_launch(const Config& c, const Layout& lay, int nseg, const CarryLaunch& cl) {
+void model_launch(const Config& c, const Layout& lay, int nseg, const CarryLaunch& cl, bool norm) {
     const WG wg = cl.half ? WG{4, 1, true} : WG{8, 1, false};
+    REQUIRE(!norm || (!wg.LW && wg.NTW == 1 && wg.CPW() == D));   // the fused norm needs whole-head workgroups
     const int CPW = wg.CPW(), NS = 128 / CPW, nh = c.N * c.Hv;
     const int NK = carry_kinds(nseg, cl.pass);
     const long long blocks = cl.units * NS;
@@ -167,13 +170,13 @@ void model_launch(const Config& c, const Layout& lay, int nseg, const CarryLaunc
         for (int m0 : m0s) {
             char buf[256];
             std::snprintf(buf, sizeof buf, "B=%d L=%d N=%d Hk=%d Hv=%d ragged=%d cus=%d seg0=%d nseg=%d pass=%d half=%d "
-                          "block=%lld n=%d h=%d kind=%d m0=%d", c.B, c.L, c.N, c.Hk, c.Hv, c.ragged, c.cus, c.seg0, nseg,
-                          cl.pass, cl.half, blk, n, h, kind, m0);
+                          "norm=%d block=%lld n=%d h=%d kind=%d m0=%d", c.B, c.L, c.N, c.Hk, c.Hv, c.ragged, c.cus, c.seg0,
+                          nseg, cl.pass, cl.half, norm, blk, n, h, kind, m0);
             g_ctx = buf;
             const int np = (nseg > 1 && cl.pass == 2) ? job.sj - 1 - m0 : 0;
             REQUIRE(np >= 0 && np <= kMaxSeg - 2);
-            const bool prologue = wg.LW && wg.NTW == 1 && np > 0;
-            REQUIRE(!(np > 0) || prologue);   // maps are only ever formed by the half-head pass
+            const bool prologue = wg.NTW == 1 && np > 0;
+            REQUIRE(!(np > 0) || prologue);   // maps are only ever formed by one-tile waves
             const int cb = nseg > 1 ? seg_begin(nch, nseg, job.sj, c.seg0) : 0;
             const int ce = nseg > 1 ? seg_begin(nch, nseg, job.sj + 1, c.seg0) : nch;
             REQUIRE(cb >= 0 && cb <= ce && ce <= nch);
@@ -195,7 +198,7 @@ void model_launch(const Config& c, const Layout& lay, int nseg, const CarryLaunc
                 for (int t = 0; t < np * (D / 16); ++t)
                     REQUIRE((static_cast<size_t>(m0 + t / (D / 16)) * nhh + head) * (D / 16) + t % (D / 16) < lay.n_Mexp);
                 const int MI = 2 * D / 4 / wg.NW;   // 1 KB loads of one map per wave
-                REQUIRE(MI == 16);                  // the prologue's wait counts 16 per map
+                REQUIRE(MI * wg.NW * 1024 == 2 * D * D * 2 && MI < 64);   // one map; vmcnt holds it
                 for (int i = 1; i <= np; ++i) {
                     const int map = m0 + i - 1;
                     REQUIRE(map >= 0 && map < nseg - 2);
@@ -206,7 +209,7 @@ void model_launch(const Config& c, const Layout& lay, int nseg, const CarryLaunc
                     REQUIRE(rbase + static_cast<size_t>(D - 1) * D + ucol0 + CPW - 1 < lay.n_Rseg);
                 }
                 // the vmcnt waits: in-order completion; before map i is read, the wait leaves
-                // at most `w` of the wave's latest loads outstanding (w = 16 while map i + 1 is
+                // at most `w` of the wave's latest loads outstanding (w = MI while map i + 1 is
                 // in flight, else 0), and the R loads of the previous iteration have been
                 // consumed, which completes everything issued before them
                 std::vector<int> q;   // issued, possibly outstanding loads: the map index of each (-1: R)
@@ -214,7 +217,7 @@ void model_launch(const Config& c, const Layout& lay, int nseg, const CarryLaunc
                 issue(1, MI);
                 if (np >= 2) issue(2, MI);
                 for (int i = 1; i <= np; ++i) {
-                    const int wait = (i + 1 <= np) ? (g_plant == "wait32" ? 32 : 16) : 0;
+                    const int wait = (i + 1 <= np) ? (g_plant == "wait32" ? 2 * MI : MI) : 0;
                     const size_t done = q.size() > static_cast<size_t>(wait) ? q.size() - wait : 0;
                     for (size_t k = done; k < q.size(); ++k) REQUIRE(q[k] != i);   // map i has landed
                     q.erase(q.begin(), q.begin() + static_cast<long>(done));
@@ -247,7 +250,9 @@ void model_launch(const Config& c, const Layout& lay, int nseg, const CarryLaunc
                     REQUIRE(pbase + 63 * C + 8 * 7 + 8 <= lay.n_P);
                     // q_hat rows past the end load row ntc - 1
                     REQUIRE(((tok0 + ntc - 1) * c.Hk + hk) * D + 8 * 15 + 8 <= lay.n_qh);
-                    // output rows tok0 .. tok0 + ntc - 1, columns of this workgroup
+                    // output rows tok0 .. tok0 + ntc - 1, columns of this workgroup (and with the
+                    // fused norm the gate rows, which have o's shape: rows past the end read row
+                    // ntc - 1)
                     REQUIRE(((tok0 + ntc - 1) * c.Hv + h) * D + ucol0 + CPW <= o_elems);
                 }
             }
@@ -266,7 +271,9 @@ void model_launch(const Config& c, const Layout& lay, int nseg, const CarryLaunc
             }
             // barriers per wave role
             const int sortb = sort ? 2 : 0;
-            const int compute = sortb + (prologue ? 2 * np : 0) + (ce - cb) + ((!wg.LW && wg.NTW == 1 && job.map >= 0) ? 2 : 0);
+            const int compute = sortb + (prologue ? 2 * np : 0) + (ce - cb) + ((!wg.LW && wg.NTW == 1 && job.map >= 0) ? 2 : 0) +
+                                (norm && job.outs && ce > cb ? 1 : 0);
+            REQUIRE(!(norm && job.outs) || job.map < 0);   // a job forms outputs or writes a map, not both
             if (wg.LW) {
                 const int loader = sortb + (prologue ? 2 * np : 0) + (ce - cb) + (g_plant == "loader_barrier" && np > 1 ? 1 : 0);
                 REQUIRE(loader == compute);
@@ -277,13 +284,14 @@ void model_launch(const Config& c, const Layout& lay, int nseg, const CarryLaunc
     for (int v : covered) REQUIRE(v == 1);   // every (slice, slot) has exactly one workgroup
 }
 
-void model(const Config& c) {
+void model(const Config& c, bool norm) {
     char buf[160];
     std::snprintf(buf, sizeof buf, "B=%d L=%d N=%d Hk=%d Hv=%d ragged=%d cus=%d seg0=%d", c.B, c.L, c.N, c.Hk, c.Hv,
                   c.ragged, c.cus, c.seg0);
     g_ctx = buf;
     const Layout lay = layout(c.B, c.L, c.N, c.Hk, c.Hv, c.ragged);
-    const CarryPlan cp = carry_plan(c.B, c.L, c.N, c.Hv, c.ragged, c.cus);
+    const CarryPlan cp = carry_plan(c.B, c.L, c.N, c.Hv, c.ragged, c.cus, norm);
+    REQUIRE(cp.nseg == carry_plan(c.B, c.L, c.N, c.Hv, c.ragged, c.cus, !norm).nseg);   // the workspace's segments
     REQUIRE(cp.nseg >= 1 && cp.nseg <= lay.nseg + (lay.nseg == 1 ? 0 : 0));
     REQUIRE(cp.nseg == 1 || (cp.nseg >= 3 && cp.nseg <= kMaxSeg && cp.nseg <= lay.nseg));
     // segments are non-empty and ordered for every sequence the launch can meet
@@ -302,7 +310,7 @@ void model(const Config& c) {
         }
         for (int v : seen) REQUIRE(v == 1);
     }
-    for (int i = 0; i < cp.count; ++i) model_launch(c, lay, cp.nseg, cp.l[i]);
+    for (int i = 0; i < cp.count; ++i) model_launch(c, lay, cp.nseg, cp.l[i], norm);
 }
 
 Config unpacked(int B, int L, int Hk, int Hv, int cus, int seg0) {
@@ -336,8 +344,9 @@ int main(int argc, char** argv) {
                 for (int B = 1; B <= 3; ++B)
                     for (int L : lengths) {
                         const Config c = unpacked(B, L, hh[0], hh[1], cus, seg0);
-                        model(c);
-                        ++configs;
+                        model(c, false);
+                        model(c, true);
+                        configs += 2;
                         if (carry_plan(B, L, B, hh[1], false, cus).nseg > 1) ++segmented;
                     }
     // packed prompts: the ragged workload's shape, empty and one-token sequences, more
@@ -350,8 +359,10 @@ int main(int argc, char** argv) {
             for (const auto& hh : heads)
                 for (const auto& p : packs)
                     for (int tail : {0, 7}) {
-                        model(packed(p, hh[0], hh[1], cus, seg0, tail));
-                        ++configs;
+                        const Config c = packed(p, hh[0], hh[1], cus, seg0, tail);
+                        model(c, false);
+                        model(c, true);
+                        configs += 2;
                     }
     std::printf("carry model: %d launch configurations (%d segmented), %lld checks, all hold\n", configs, segmented,
                 g_checks);

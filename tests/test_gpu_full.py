@@ -112,6 +112,60 @@ def test_ragged_prefill_8_sequences():
     assert np.array_equal(cout.float().cpu().numpy(), ref["conv_out"])
 
 
+def _fused_prefill_case(seed, L, N, cu=None):
+    """The fused workloads' inputs (raw a/b through the gate/beta prologue, gated RMSNorm
+    with z): device results and the oracle's."""
+    x = gi.qkv(SH, 1, L, seed, "bf16")
+    a_raw, b_raw = gi.a_raw(SH, 1, L, seed, "bf16"), gi.b_raw(SH, 1, L, seed, "bf16")
+    A_log, dt_bias = gi.a_log(SH, seed, "bf16"), gi.dt_bias(SH, seed, "bf16")
+    z, nw = gi.z_gate(SH, 1, L, seed, "bf16"), gi.norm_weight(SH, seed, "bf16")
+    w = gi.conv_weight(SH, seed, "bf16")
+    p = params(SH, "bf16")
+    S = torch.zeros((N, SH.Hv, SH.dk, SH.dv), device="cuda")
+    o = torch.full((1, L, SH.Hv, SH.dv), float("nan"), device="cuda")
+    c0 = torch.zeros((N, SH.D, SH.K - 1), device="cuda", dtype=torch.bfloat16)
+    cout = torch.empty_like(c0)
+    ws = gdn.prefill_workspace(p, 1, L, N)
+    fus = gdn.GdnFusion(dev(A_log, "bf16"), dev(dt_bias, "bf16"), dev(z, "bf16"), dev(nw, "bf16"), 1e-6)
+    gdn.gdn_prefill_ex(p, fus, dev(x, "bf16"), dev(a_raw, "bf16"), dev(b_raw, "bf16"), dev(w, "bf16"), c0, cout,
+                       S, o, ws, cu_seqlens=None if cu is None else dev(cu))
+    torch.cuda.synchronize()
+    g, b = oracle.gate_beta(a_raw, b_raw, A_log, dt_bias)
+    ref = oracle.gdn_forward(oparams(SH), x, g, b, w, np.zeros((N, SH.D, 3)), np.zeros((N, SH.Hv, 128, 128)),
+                             cu_seqlens=cu)
+    ref["o"] = oracle.gated_rmsnorm(ref["o"], z, nw, 1e-6)
+    return o, S, cout, ref
+
+
+def test_prefill_L4096_fused():
+    """The gated RMSNorm in the carry's output store (whole-head workgroups in both
+    passes of the segmented carry), every head of the 4096-token prompt."""
+    seed, L = gi.WORKLOADS[2].seed, gi.PREFILL_L
+    print(f"prefill fused full L={L}", flush=True)
+    o, S, cout, ref = _fused_prefill_case(seed, L, 1)
+    assert not torch.isnan(o).any()
+    for h in range(SH.Hv):
+        assert rel_err(o[0, :, h], ref["o"][0, :, h]) <= TOL["bf16"], h
+        assert rel_err(S[0, h], ref["S"][0, h]) <= TOL["bf16"], h
+    assert np.array_equal(cout.float().cpu().numpy(), ref["conv_out"])
+
+
+def test_ragged_prefill_fused():
+    seed = gi.WORKLOADS[3].seed
+    lens = gi.seq_lens(gi.RAGGED_N, gi.RAGGED_LO, gi.RAGGED_HI, seed)
+    cu = gi.cu_seqlens(lens)
+    L, N = int(cu[-1]), gi.RAGGED_N
+    print(f"ragged prefill fused full total={L}", flush=True)
+    o, S, cout, ref = _fused_prefill_case(seed, L, N, cu=cu)
+    assert not torch.isnan(o).any()
+    for n in range(N):
+        s, e = int(cu[n]), int(cu[n + 1])
+        for h in range(SH.Hv):
+            assert rel_err(o[0, s:e, h], ref["o"][0, s:e, h]) <= TOL["bf16"], (n, h)
+            assert rel_err(S[n, h], ref["S"][n, h]) <= TOL["bf16"], (n, h)
+    assert np.array_equal(cout.float().cpu().numpy(), ref["conv_out"])
+
+
 def test_verify_B128_T4_and_commit():
     seed, B, T = gi.WORKLOADS[4].seed, gi.VERIFY_B, gi.VERIFY_T
     print(f"verify full B={B} T={T}", flush=True)
