@@ -869,7 +869,7 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
     constexpr bool BATCH = NW <= 4;
     using SG = Stage<CPW>;
     constexpr int NS = 128 / CPW;                        // workgroups per head
-    const int nh = a.N * a.Hv;
+
     const int tid = threadIdx.x, lane = tid & 63;
     // Segmented mode (ws.nseg > 1): the chunks of each sequence split into nseg
     // segments and the carry runs in two passes. A chunk step is affine in the state
@@ -881,12 +881,12 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
     // outputs, each from its entry state S_j = M_{j-1} S_{j-1} + R_{j-1}, which its
     // workgroups form first on their own columns; the last one ends in the final state.
     const int NK = plan::carry_kinds(ws.nseg, ws.pass);   // kinds per head
-    const plan::Slice sl = plan::carry_slice(blockIdx.x, NK * NS, nh);
-    const int slice = sl.slice, slot = sl.slot;
+    const plan::CarryUnit un = plan::carry_unit(blockIdx.x, NK * NS, a.N, a.Hk, a.Hv);
+    const int slice = un.slice;
     const int cs = slice % NS;
     const int kind = slice / NS;
-    const int h = slot % a.Hv;
-    int n = slot / a.Hv;
+    const int h = un.h;
+    int n = un.n;
     // Packed prompts: slots go to sequences longest first, so that the in-order
     // dispatch of workgroups to free CUs schedules the longest chains first.
     if (a.cu != nullptr && a.N <= kSortMax) n = sequence_of_rank(a, n);

@@ -158,6 +158,16 @@ constexpr Slice carry_slice(int block, int nsl, int nh) {
     return Slice{rem / tail, 8 * grp + rem % tail};
 }
 
+// blockIdx -> (slice, sequence slot, V head) of the carry: the f = Hv / Hk V heads that
+// share a K head form one dispatch unit of f * nsl slices (carry_slice over (sequence,
+// K head) units), so every workgroup that reads a chunk's keys and queries runs on one XCD.
+struct CarryUnit { int slice, n, h; };
+constexpr CarryUnit carry_unit(int block, int nsl, int N, int Hk, int Hv) {
+    const int f = Hv / Hk;
+    const Slice s = carry_slice(block, nsl * f, N * Hk);
+    return CarryUnit{s.slice % nsl, s.slot / Hk, (s.slot % Hk) * f + s.slice / nsl};
+}
+
 // What a carry workgroup of a given kind does: segment sj, its entry state, whether it
 // forms outputs and loads U, and where its end state goes.
 enum Entry { kFromState = 0, kFromZero = 1, kFromIdentity = 2 };

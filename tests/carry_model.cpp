@@ -145,11 +145,11 @@ void model_launch(const Config& c, const Layout& lay, int nseg, const CarryLaunc
     std::vector<int> covered(static_cast<size_t>(NK) * NS * nh, 0);
     const bool sort = c.ragged && c.N <= kSortMax;
     for (long long blk = 0; blk < blocks; ++blk) {
-        const Slice sl = carry_slice(static_cast<int>(blk), NK * NS, nh);
-        REQUIRE(sl.slice >= 0 && sl.slice < NK * NS && sl.slot >= 0 && sl.slot < nh);
-        ++covered[static_cast<size_t>(sl.slice) * nh + sl.slot];
-        const int cs = sl.slice % NS, kind = sl.slice / NS, h = sl.slot % c.Hv;
-        int n = sl.slot / c.Hv;
+        const CarryUnit un = carry_unit(static_cast<int>(blk), NK * NS, c.N, c.Hk, c.Hv);
+        REQUIRE(un.slice >= 0 && un.slice < NK * NS && un.n >= 0 && un.n < c.N && un.h >= 0 && un.h < c.Hv);
+        ++covered[static_cast<size_t>(un.slice) * nh + un.n * c.Hv + un.h];
+        const int cs = un.slice % NS, kind = un.slice / NS, h = un.h;
+        int n = un.n;
         if (sort) n = sort_rank_sequence(c, n);
         const int f = c.Hv / c.Hk, hk = h / f;
         int base = 0;
