@@ -278,7 +278,7 @@ gdn_status gdn_prefill_ex(const gdn_params* p, const gdn_fusion* fusion, int32_t
  * up once per device (hipGetSymbolAddress, on the first call made with that device
  * current) and the device holds the array until the process ends.
  *   Limit: a call whose gdn_prefill_workspace_size() exceeds 134217728 bytes returns
- *   GDN_ERR_TOO_LARGE and enqueues nothing (with bf16 inputs about 2,800 tokens at
+ *   GDN_ERR_TOO_LARGE and enqueues nothing (with bf16 inputs about 3,500 tokens at
  *   16 K / 32 V heads of dimension 128; gdn_prefill_workspace_size gives the exact
  *   need).
  *   Sharing: every call on one device uses that device's one array. Calls that can run

@@ -11,19 +11,22 @@
 // (exact to apply and to undo); q and k are unit-norm and P, W are bounded by
 // them.
 //
-//   front_kernel   steps 1-4 on a (32-token, 128-channel) tile: coalesced
-//                  channel-major loads, conv + SiLU, transpose through LDS,
-//                  per-token L2 norms and the q scale; fp16 token-major q, k, v.
-//   chunk_kernel   per (chunk, V head), all chunks in parallel: Gam (cumulative
-//                  log-decay), the Gram matrices K K^T and Q K^T on MFMA,
+//   front_kernel   steps 1-4 for the q and k channels on a (32-token,
+//                  128-channel) tile: coalesced channel-major loads, conv + SiLU,
+//                  transpose through LDS, per-token L2 norms and the q scale;
+//                  fp16 token-major q and k.
+//   chunk_kernel   per (chunk, V head), all chunks in parallel: the head's values
+//                  (conv + SiLU of its raw channel-major input; v is never stored),
+//                  Gam (cumulative log-decay), the Gram matrices K K^T and Q K^T on MFMA,
 //                  A and P, T = (I + A)^-1 by a blocked fp32 inverse (16 x 16
 //                  diagonal blocks by substitution, off-diagonal blocks by
 //                  block products), then W = T diag(beta exp(Gam)) K and
 //                  U = T diag(beta) V on MFMA. Writes W, U, P, Gam and a
 //                  transposed copy of the chunk's keys.
 //   carry_kernel   per (sequence, V head): the state lives in registers in MFMA
-//                  accumulator layout (each of the 4 waves owns 32 of the 128
-//                  columns; the columns of S evolve independently); chunk by
+//                  accumulator layout (each wave owns 16 of the 128 columns; a
+//                  head takes one workgroup of 8 waves or two of 4; the columns
+//                  of S evolve independently); chunk by
 //                  chunk it forms Delta = U - W S, O = diag(exp(Gam)) Q S +
 //                  P Delta and S = exp(Gam_last) S + K^T diag(exp(Gam_last -
 //                  Gam)) Delta. The next chunk's operands stream into the other
@@ -53,6 +56,11 @@ using plan::kMaxSeg;
 using plan::kpos;
 using plan::seg_begin;
 using plan::Stage;
+// 16- and 8-byte vectors that need only 4-byte alignment (global loads of several
+// dwords need dword alignment only)
+typedef unsigned u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef unsigned u32x2a4 __attribute__((ext_vector_type(2), aligned(4)));
+
 constexpr int TT = 32;     // front-end tile (tokens): 19 KB of LDS, eight workgroups per CU
 constexpr int RAW = TT + 5;  // raw tile row stride (floats): TT + 3 used, odd stride against bank conflicts
 
@@ -60,7 +68,6 @@ constexpr int RAW = TT + 5;  // raw tile row stride (floats): TT + 3 used, odd s
 struct Ws {
     _Float16* qh;   // [Ttot, Hk, D] q_hat (normalised, scaled), features in k order
     _Float16* kh;   // [Ttot, Hk, D] k_hat, features in k order
-    _Float16* vh;   // [Ttot, Hv, D] v
     _Float16* W;    // [NC, Hv, C, D] features in k order
     _Float16* U;    // [NC, Hv, D, C] transposed, scaled by 2^-uexp
     _Float16* P;    // [NC, Hv, C, C] keys in k order
@@ -85,7 +92,6 @@ static Ws layout(void* base, int B, int L, int N, int Hk, int Hv, bool ragged) {
     Ws w;
     w.qh = static_cast<_Float16*>(at(l.qh, l.n_qh));
     w.kh = static_cast<_Float16*>(at(l.kh, l.n_kh));
-    w.vh = static_cast<_Float16*>(at(l.vh, l.n_vh));
     w.W = static_cast<_Float16*>(at(l.W, l.n_W));
     w.U = static_cast<_Float16*>(at(l.U, l.n_U));
     w.P = static_cast<_Float16*>(at(l.P, l.n_P));
@@ -153,17 +159,17 @@ __global__ __launch_bounds__(256) void front_kernel(PrefillArgs a, Ws ws) {
     __shared__ int s_n[TT], s_start[TT];
     __shared__ unsigned s_endmask;           // bit t: token t is the last of its sequence
     static_assert(TT * (D + 1) <= D * RAW, "the transposed outputs reuse the raw tile");
-    const int units = 2 * a.Hk + a.Hv;
+    const int units = 2 * a.Hk;              // q and k heads (v is formed by the chunk kernel)
     const int tiles = (a.L + TT - 1) / TT;
     long long blk = blockIdx.x;
     const int u = static_cast<int>(blk % units); blk /= units;
     const int tile = static_cast<int>(blk % tiles);
     const int row = static_cast<int>(blk / tiles);
     const int p0 = tile * TT;
-    const int ch0 = u * D;   // [Q | K | V] blocks of D channels
+    const int ch0 = u * D;   // [Q | K] blocks of D channels
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const Tin* x = static_cast<const Tin*>(a.qkv) + (static_cast<size_t>(row) * a.D + ch0) * a.L;
-    const bool is_q = u < a.Hk, is_k = !is_q && u < 2 * a.Hk;
+    const bool is_q = u < a.Hk;
 
     // Interior tiles of unpacked bf16 rows whose length is a multiple of 8 (so that every
     // 8-token group is 16-byte aligned): each lane loads 8 tokens of a channel and the 4
@@ -196,7 +202,7 @@ __global__ __launch_bounds__(256) void front_kernel(PrefillArgs a, Ws ws) {
                                   lo(xr[i].x), hi(xr[i].x), lo(xr[i].y), hi(xr[i].y),
                                   lo(xr[i].z), hi(xr[i].z), lo(xr[i].w), hi(xr[i].w)};
             const float w0 = lo(wr[i].x), w1 = hi(wr[i].x), w2 = lo(wr[i].y), w3 = hi(wr[i].y);
-            const int cpos = is_q || is_k ? kpos(cc) : cc;
+            const int cpos = kpos(cc);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 float acc = w0 * xv[j];
@@ -359,7 +365,7 @@ __global__ __launch_bounds__(256) void front_kernel(PrefillArgs a, Ws ws) {
     }
     __syncthreads();
     // q and k channels are placed in k order here (the norms below do not depend on the order)
-    const int cpos = is_q || is_k ? kpos(c) : c;
+    const int cpos = kpos(c);
 #pragma unroll
     for (int j = 0; j < TT / 2; ++j) buf[(th * (TT / 2) + j) * (D + 1) + cpos] = y[j];
     }
@@ -369,7 +375,7 @@ __global__ __launch_bounds__(256) void front_kernel(PrefillArgs a, Ws ws) {
     constexpr int NPART = 256 / TT, PW = D / NPART;
     __shared__ float s_part[NPART][TT];
     __shared__ float s_scale[TT];
-    if (is_q || is_k) {
+    {
         const int t = tid % TT, qq = tid / TT;
         float ss = 0.f;
 #pragma unroll 8
@@ -382,13 +388,11 @@ __global__ __launch_bounds__(256) void front_kernel(PrefillArgs a, Ws ws) {
     __syncthreads();
     if (tid < TT) {
         float r = 1.f;
-        if (is_q || is_k) {
-            float ss = 0.f;
+        float ss = 0.f;
 #pragma unroll
-            for (int q = 0; q < NPART; ++q) ss += s_part[q][tid];
-            if (a.use_l2) r = 1.0f / sqrtf(ss + a.eps);
-            if (is_q) r *= 1.0f / sqrtf(static_cast<float>(D));
-        }
+        for (int q = 0; q < NPART; ++q) ss += s_part[q][tid];
+        if (a.use_l2) r = 1.0f / sqrtf(ss + a.eps);
+        if (is_q) r *= 1.0f / sqrtf(static_cast<float>(D));
         s_scale[tid] = r;
     }
     __syncthreads();
@@ -396,8 +400,8 @@ __global__ __launch_bounds__(256) void front_kernel(PrefillArgs a, Ws ws) {
     // per instruction, 16 tokens in all
     {
         const int tq = lane >> 4, j = lane & 15;
-        _Float16* base = is_q ? ws.qh + u * D : is_k ? ws.kh + (u - a.Hk) * D : ws.vh + (u - 2 * a.Hk) * D;
-        const int hs = is_q || is_k ? a.Hk : a.Hv;   // heads per token in the destination
+        _Float16* base = is_q ? ws.qh + u * D : ws.kh + (u - a.Hk) * D;
+        const int hs = a.Hk;                         // heads per token in the destination
 #pragma unroll
         for (int i = 0; i < TT / 16; ++i) {
             const int t = wave * (TT / 4) + 4 * i + tq;
@@ -451,7 +455,7 @@ __global__ __launch_bounds__(256, 4) void chunk_kernel(PrefillArgs a, Ws ws) {
     constexpr int REGION = 2 * D * TS * 2;  // 36864 B >= 64*136*2 + 64*65*4 = 34048 B
     static_assert(C * AS * 4 <= C * KS * 2, "T must fit where the keys were");
     __shared__ __align__(16) unsigned char region[REGION];
-    __shared__ float s_g[C], s_b[C], s_gam[C], s_red[4];
+    __shared__ __align__(16) float s_g[C], s_b[C], s_gam[C], s_red[4];
     _Float16* Kc = reinterpret_cast<_Float16*>(region);
     float* Am = reinterpret_cast<float*>(region + C * KS * 2);
     float* Tm = reinterpret_cast<float*>(region);   // written only after the Gram phase's last read of Kc
@@ -464,6 +468,16 @@ __global__ __launch_bounds__(256, 4) void chunk_kernel(PrefillArgs a, Ws ws) {
     const int hk = cu.hk, id = cu.id, h = cu.h;
     int n, c;
     Seg seg;
+    if (id == 0 && a.cu != nullptr && threadIdx.x < D) {   // empty sequences keep the value channels' conv state
+        const int ch = 2 * a.Hk * D + h * D + threadIdx.x;
+        for (int m = 0; m < a.N; ++m) {
+            if (segment_of(m, a.L, a.cu).len != 0) continue;
+            const size_t cb = (static_cast<size_t>(m) * a.D + ch) * (kConvK - 1);
+#pragma unroll
+            for (int j = 0; j < kConvK - 1; ++j)
+                static_cast<Tin*>(a.conv_out)[cb + j] = static_cast<const Tin*>(a.conv_in)[cb + j];
+        }
+    }
     if (id >= ws.nc_max || !find_chunk(id, a, &n, &c, &seg)) return;
     const int nt = min(C, seg.len - c * C);
     const size_t tok0 = static_cast<size_t>(seg.row) * a.L + seg.start + static_cast<size_t>(c) * C;
@@ -569,14 +583,38 @@ __global__ __launch_bounds__(256, 4) void chunk_kernel(PrefillArgs a, Ws ws) {
     }
     __syncthreads();
 
-    // values of step 4, loaded now so that the solve hides their latency
-    f16x8 vreg[4];
+    // Steps 1-2 for this V head's value channels (v needs no norm), formed here from the
+    // raw channel-major input: item i of a thread is channel f0 + 32 i of the head and
+    // tokens 8 g8 .. 8 g8 + 7 of the chunk, whose conv windows span the raw positions
+    // p - 3 .. p + 7 (p = the item's first token). Chunks after a sequence's first whose
+    // loads stay inside the row fetch the 12 positions [p - 4, p + 8) or [p - 3, p + 9),
+    // whichever starts on a 4-byte boundary, in two vector loads issued now, so that the
+    // solve hides their latency; the other chunks gather theirs in step 4 (a first
+    // chunk's windows start in the incoming conv state).
+    static_assert(sizeof(Tin) == 2, "the raw value loads assume bf16 inputs");
+    const int g8 = tid & 7, f0 = tid >> 3;
+    const int cv0 = 2 * a.Hk * D + h * D;                 // first channel of this V head
+    const int pc = seg.start + c * C;                      // row position of the chunk's first token
+    const uint16_t* xr = reinterpret_cast<const uint16_t*>(a.qkv) + static_cast<size_t>(seg.row) * a.D * a.L;
+    const bool vfast = c > 0 && nt == C && pc + C + 1 <= a.L && (reinterpret_cast<uintptr_t>(a.qkv) & 3) == 0;
+    u32x4a4 vlo[4];
+    u32x2a4 vhi[4];
+    uint2 wraw[4];                                         // conv taps of the item's channel
     {
-        const int sc = lane < nt ? lane : nt - 1;
+        const uint16_t* wb = reinterpret_cast<const uint16_t*>(a.w);
+        const bool wal = (reinterpret_cast<uintptr_t>(a.w) & 7) == 0;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const f16x8 vl = *reinterpret_cast<const f16x8*>(ws.vh + ((tok0 + sc) * a.Hv + h) * D + 8 * (wave + 4 * q));
-            vreg[q] = lane < nt ? vl : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        for (int i = 0; i < 4; ++i) {
+            const size_t ch = static_cast<size_t>(cv0 + f0 + 32 * i);
+            if (vfast) {
+                const size_t e = ch * a.L + pc + 8 * g8 - 4;   // position p - 4
+                const size_t q0 = e + (e & 1);
+                vlo[i] = *reinterpret_cast<const u32x4a4*>(xr + q0);
+                vhi[i] = *reinterpret_cast<const u32x2a4*>(xr + q0 + 8);
+            }
+            const uint16_t* wp = wb + ch * kConvK;
+            wraw[i] = wal ? *reinterpret_cast<const uint2*>(wp)
+                          : make_uint2(wp[0] | static_cast<unsigned>(wp[1]) << 16, wp[2] | static_cast<unsigned>(wp[3]) << 16);
         }
     }
 
@@ -648,17 +686,57 @@ __global__ __launch_bounds__(256, 4) void chunk_kernel(PrefillArgs a, Ws ws) {
     //    VbT[j][s] = beta_s v_s[j] 2^-eV
     // lanes run along tokens, so the transposed LDS writes of a wave hit
     // consecutive halfs (no bank conflicts); item (s, j) = granule j of token s
+    {
+        const int s = lane;
+        const float fk = s_b[s] * __expf(s_gam[s]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int j = wave + 4 * q;
+            const f16x8 kv = kreg[q];   // zero past the end
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                KbT[kidx(8 * j + e) * TS + s] = static_cast<_Float16>(fk * static_cast<float>(kv[e]));   // row: feature
+        }
+    }
+    // v = SiLU(conv) of the items (zero past the end), the taps applied oldest first
+    const f32x4v bt0 = *reinterpret_cast<const f32x4v*>(s_b + 8 * g8), bt1 = *reinterpret_cast<const f32x4v*>(s_b + 8 * g8 + 4);
+    const float bt[8] = {bt0[0], bt0[1], bt0[2], bt0[3], bt1[0], bt1[1], bt1[2], bt1[3]};
+    float vv[4][8];
     float vmax = 0.f;
-    const int s = lane;
-    const float fk = s_b[s] * __expf(s_gam[s]);
+    {
+        const auto lo = [](unsigned v) { return __uint_as_float(v << 16); };
+        const auto hi = [](unsigned v) { return __uint_as_float(v & 0xffff0000u); };
+        const uint16_t* cin = static_cast<const uint16_t*>(a.conv_in);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int j = wave + 4 * q;
-        const f16x8 kv = kreg[q];   // zero past the end, as vreg
+        for (int i = 0; i < 4; ++i) {
+            const size_t ch = static_cast<size_t>(cv0 + f0 + 32 * i);
+            float xv[11];
+            if (vfast) {
+                const float r[12] = {lo(vlo[i].x), hi(vlo[i].x), lo(vlo[i].y), hi(vlo[i].y), lo(vlo[i].z), hi(vlo[i].z),
+                                     lo(vlo[i].w), hi(vlo[i].w), lo(vhi[i].x), hi(vhi[i].x), lo(vhi[i].y), hi(vhi[i].y)};
+                const bool from4 = ((ch * a.L + pc + 8 * g8 - 4) & 1) == 0;   // the loads start at p - 4
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            KbT[kidx(8 * j + e) * TS + s] = static_cast<_Float16>(fk * static_cast<float>(kv[e]));   // row: feature
-            vmax = fmaxf(vmax, fabsf(s_b[s] * static_cast<float>(vreg[q][e])));
+                for (int k = 0; k < 11; ++k) xv[k] = from4 ? r[k + 1] : r[k];
+            } else {
+#pragma unroll
+                for (int k = 0; k < 11; ++k) {
+                    const int u = c * C + 8 * g8 - 3 + k;            // position inside the sequence
+                    float x = 0.f;                                   // past the end: masked below
+                    if (u < 0) x = __uint_as_float(static_cast<unsigned>(cin[(static_cast<size_t>(n) * a.D + ch) * (kConvK - 1) + (kConvK - 1) + u]) << 16);
+                    else if (u < seg.len) x = __uint_as_float(static_cast<unsigned>(xr[ch * a.L + seg.start + u]) << 16);
+                    xv[k] = x;
+                }
+            }
+            const float w0 = lo(wraw[i].x), w1 = hi(wraw[i].x), w2 = lo(wraw[i].y), w3 = hi(wraw[i].y);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                float acc = w0 * xv[j];
+                acc = __fmaf_rn(w1, xv[j + 1], acc);
+                acc = __fmaf_rn(w2, xv[j + 2], acc);
+                acc = __fmaf_rn(w3, xv[j + 3], acc);
+                vv[i][j] = 8 * g8 + j < nt ? fast_silu(acc) : 0.f;
+                vmax = fmaxf(vmax, fabsf(bt[j] * vv[i][j]));
+            }
         }
     }
     vmax = wave_max(vmax);
@@ -667,11 +745,25 @@ __global__ __launch_bounds__(256, 4) void chunk_kernel(PrefillArgs a, Ws ws) {
     const int eV = pow2_exponent(fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3])));
     const float sV = ldexpf(1.f, -eV);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int j = wave + 4 * q;
+    for (int i = 0; i < 4; ++i) {   // row f of VbT, tokens 8 g8 .. + 7: one 16-byte store
+        f16x8 hv;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            VbT[(8 * j + e) * TS + s] = static_cast<_Float16>(s_b[s] * static_cast<float>(vreg[q][e]) * sV);
+        for (int j = 0; j < 8; ++j) hv[j] = static_cast<_Float16>(bt[j] * vv[i][j] * sV);
+        *reinterpret_cast<f16x8*>(VbT + (f0 + 32 * i) * TS + 8 * g8) = hv;
+    }
+    // the value channels' conv state after the sequence: its last K-1 raw inputs (or the
+    // incoming state's for a sequence shorter than K-1)
+    if (c == chunks_of(seg) - 1 && tid < D) {
+        const size_t ch = static_cast<size_t>(cv0 + tid);
+        const size_t cb = (static_cast<size_t>(n) * a.D + ch) * (kConvK - 1);
+        const Tin* cin = static_cast<const Tin*>(a.conv_in);
+        const Tin* xt = static_cast<const Tin*>(a.qkv) + static_cast<size_t>(seg.row) * a.D * a.L + ch * a.L + seg.start;
+        Tin* co = static_cast<Tin*>(a.conv_out);
+#pragma unroll
+        for (int j = 0; j < kConvK - 1; ++j) {
+            const int m = seg.len + j;                     // position in concat(state, x[seq])
+            co[cb + j] = m < kConvK - 1 ? cin[cb + m] : xt[m - (kConvK - 1)];
+        }
     }
     __syncthreads();
 
@@ -1482,7 +1574,7 @@ static hipError_t launch_mfma_t(const PrefillArgs& a, int in_dtype, hipStream_t 
     ws.nseg = plan::carry_plan(a.B, a.L, a.N, a.Hv, ragged, cus).nseg;   // within the workspace's
     void* args[] = {const_cast<PrefillArgs*>(&a), &ws};
     hipError_t e;
-    const long long fblocks = static_cast<long long>(a.B) * ((a.L + pf2::TT - 1) / pf2::TT) * (2 * a.Hk + a.Hv);
+    const long long fblocks = static_cast<long long>(a.B) * ((a.L + pf2::TT - 1) / pf2::TT) * (2 * a.Hk);
     if (fblocks > 0) {
         e = hipLaunchKernel(reinterpret_cast<const void*>(&pf2::front_kernel<Tin>), dim3(static_cast<unsigned>(fblocks)),
                             dim3(256), args, 0, stream);

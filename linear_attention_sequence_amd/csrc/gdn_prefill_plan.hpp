@@ -82,8 +82,8 @@ constexpr size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(25
 // Byte offsets of the workspace regions (from a 256-byte aligned base) and their sizes
 // in elements of their types.
 struct Layout {
-    size_t qh, kh, vh, W, U, P, KT, coef, Sent, Mhl, Mexp, Rseg, bytes;
-    size_t n_qh, n_kh, n_vh, n_W, n_U, n_P, n_KT, n_coef, n_Sent, n_Mhl, n_Mexp, n_Rseg;
+    size_t qh, kh, W, U, P, KT, coef, Sent, Mhl, Mexp, Rseg, bytes;
+    size_t n_qh, n_kh, n_W, n_U, n_P, n_KT, n_coef, n_Sent, n_Mhl, n_Mexp, n_Rseg;
     int nc_max, nseg;
 };
 
@@ -94,7 +94,6 @@ constexpr Layout layout(int B, int L, int N, int Hk, int Hv, bool ragged) {
     size_t off = 0;
     w.n_qh = T * Hk * D;       w.qh = off;   off = align256(off + w.n_qh * 2);
     w.n_kh = T * Hk * D;       w.kh = off;   off = align256(off + w.n_kh * 2);
-    w.n_vh = T * Hv * D;       w.vh = off;   off = align256(off + w.n_vh * 2);
     w.n_W = nc * Hv * C * D;   w.W = off;    off = align256(off + w.n_W * 2);
     w.n_U = nc * Hv * C * D;   w.U = off;    off = align256(off + w.n_U * 2);
     w.n_P = nc * Hv * C * C;   w.P = off;    off = align256(off + w.n_P * 2);

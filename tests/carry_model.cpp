@@ -1,5 +1,5 @@
 // Host-side bounds model of the MFMA prefill's carry kernel (and of the chunk kernel's
-// blockIdx map). It includes the index header the kernels themselves compute every
+// blockIdx map and raw value loads). It includes the index header the kernels themselves compute every
 // address from (gdn_prefill_plan.hpp) and, for every launch configuration the launcher
 // can choose, replays each workgroup's job: its segment, entry state, every stage load
 // (global source row and granule, LDS slot), the state-map prologue of the second pass,
@@ -284,6 +284,38 @@ void model_launch(const Config& c, const Layout& lay, int nseg, const CarryLaunc
     for (int v : covered) REQUIRE(v == 1);   // every (slice, slot) has exactly one workgroup
 }
 
+// The chunk kernel's raw value loads (v is formed there from the channel-major input):
+// for every chunk, token group g8 and both parities of the channel row's offset, the
+// two vector loads of the fast path stay inside the channel's row and cover the item's
+// conv windows, and the gathered path reads the conv state or positions of the sequence.
+void check_value_loads(const Config& c) {
+    for (int n = 0; n < c.N; ++n) {
+        const int nch = chunks_of_len(c.lens[n]);
+        for (int cc = 0; cc < nch; ++cc) {
+            const int nt = imin(C, c.lens[n] - cc * C), pc = c.starts[n] + cc * C;
+            REQUIRE(nt >= 1 && pc + nt <= c.L);
+            const bool vfast = cc > 0 && nt == C && pc + C + 1 <= c.L;
+            for (int g8 = 0; g8 < 8; ++g8) {
+                const int p = pc + 8 * g8;
+                if (vfast) {
+                    for (int parity = 0; parity < 2; ++parity) {   // of (channel row offset + p - 4)
+                        const int q0 = p - 4 + parity;             // the loads start on a 4-byte boundary
+                        REQUIRE(q0 >= 0 && q0 + 12 <= c.L);        // inside the channel's row
+                        REQUIRE(q0 <= p - 3 && p + 8 <= q0 + 12);  // the windows of tokens p .. p + 7
+                        REQUIRE(p - 3 >= c.starts[n]);             // inside the sequence
+                    }
+                } else {
+                    for (int k = 0; k < 11; ++k) {
+                        const int u = cc * C + 8 * g8 - 3 + k;
+                        if (u < 0) REQUIRE(u >= -(3));             // conv state slot 3 + u
+                        else if (u < c.lens[n]) REQUIRE(c.starts[n] + u < c.L);
+                    }
+                }
+            }
+        }
+    }
+}
+
 void model(const Config& c, bool norm) {
     char buf[160];
     std::snprintf(buf, sizeof buf, "B=%d L=%d N=%d Hk=%d Hv=%d ragged=%d cus=%d seg0=%d", c.B, c.L, c.N, c.Hk, c.Hv,
@@ -311,6 +343,7 @@ void model(const Config& c, bool norm) {
         for (int v : seen) REQUIRE(v == 1);
     }
     for (int i = 0; i < cp.count; ++i) model_launch(c, lay, cp.nseg, cp.l[i], norm);
+    if (!norm) check_value_loads(c);
 }
 
 Config unpacked(int B, int L, int Hk, int Hv, int cus, int seg0) {
