@@ -508,13 +508,13 @@ def bench_prefill(args, torch, gdn, gi, ragged=False, fused=False):
     }
 
 
-# (timed steps, untimed warm-up steps). The prefill workloads keep the GPU busy for
-# 30-40 ms before timing: their per-call time still fell by about 10% over the first
-# ~10 ms of back-to-back calls (the clocks settling), which a 3 ms warm-up left in the
-# timed region.
-DEFAULT_STEPS = {"decode": (256, 32), "decode_fused": (256, 32), "verify": (50, 5), "commit": (50, 5),
+# (timed steps, untimed warm-up steps). Every workload keeps the GPU busy for 10-40 ms
+# before timing: the prefill calls' time still fell by about 10% over the first ~10 ms of
+# back-to-back calls (the clocks settling), which a 3 ms warm-up left in the timed
+# region, and decode's first repetition after a 1.6 ms warm-up ran about 3% slow.
+DEFAULT_STEPS = {"decode": (256, 256), "decode_fused": (256, 256), "verify": (50, 40), "commit": (50, 100),
                  "prefill": (60, 200), "ragged": (20, 40), "prefill_fused": (60, 200), "ragged_fused": (20, 40),
-                 "spec_round_copy": (50, 5), "spec_round_slots": (50, 5)}
+                 "spec_round_copy": (50, 30), "spec_round_slots": (50, 40)}
 EXTRAS = ("prefill", "ragged", "verify", "commit")
 
 
