@@ -60,6 +60,7 @@ using plan::Stage;
 // dwords need dword alignment only)
 typedef unsigned u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
 typedef unsigned u32x2a4 __attribute__((ext_vector_type(2), aligned(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));   // a packed pair, operand of v_dot2_f32_bf16
 
 constexpr int TT = 32;     // front-end tile (tokens): 19 KB of LDS, eight workgroups per CU
 constexpr int RAW = TT + 5;  // raw tile row stride (floats): TT + 3 used, odd stride against bank conflicts
@@ -698,42 +699,49 @@ __global__ __launch_bounds__(256, 4) void chunk_kernel(PrefillArgs a, Ws ws) {
                 KbT[kidx(8 * j + e) * TS + s] = static_cast<_Float16>(fk * static_cast<float>(kv[e]));   // row: feature
         }
     }
-    // v = SiLU(conv) of the items (zero past the end), the taps applied oldest first
+    // v = SiLU(conv) of the items (zero past the end). The window's 11 raw values stay
+    // packed as bf16 pairs: A[k] = (x_2k, x_2k+1), B[k] = (x_2k+1, x_2k+2) (x_0 = position
+    // p - 3), and each token's four taps are two bf16 dot products (exact products, fp32 sums).
     const f32x4v bt0 = *reinterpret_cast<const f32x4v*>(s_b + 8 * g8), bt1 = *reinterpret_cast<const f32x4v*>(s_b + 8 * g8 + 4);
     const float bt[8] = {bt0[0], bt0[1], bt0[2], bt0[3], bt1[0], bt1[1], bt1[2], bt1[3]};
     float vv[4][8];
     float vmax = 0.f;
     {
-        const auto lo = [](unsigned v) { return __uint_as_float(v << 16); };
-        const auto hi = [](unsigned v) { return __uint_as_float(v & 0xffff0000u); };
         const uint16_t* cin = static_cast<const uint16_t*>(a.conv_in);
+        const auto pair = [](unsigned v) { return __builtin_bit_cast(bf16x2, v); };
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const size_t ch = static_cast<size_t>(cv0 + f0 + 32 * i);
-            float xv[11];
+            unsigned A[6];
             if (vfast) {
-                const float r[12] = {lo(vlo[i].x), hi(vlo[i].x), lo(vlo[i].y), hi(vlo[i].y), lo(vlo[i].z), hi(vlo[i].z),
-                                     lo(vlo[i].w), hi(vlo[i].w), lo(vhi[i].x), hi(vhi[i].x), lo(vhi[i].y), hi(vhi[i].y)};
-                const bool from4 = ((ch * a.L + pc + 8 * g8 - 4) & 1) == 0;   // the loads start at p - 4
+                const unsigned d[7] = {vlo[i].x, vlo[i].y, vlo[i].z, vlo[i].w, vhi[i].x, vhi[i].y, 0u};
+                // the loads start at p - 4 (drop one value: shift by 2 bytes) or at p - 3
+                const unsigned sh = ((ch * a.L + pc + 8 * g8 - 4) & 1) == 0 ? 2u : 0u;
 #pragma unroll
-                for (int k = 0; k < 11; ++k) xv[k] = from4 ? r[k + 1] : r[k];
+                for (int k = 0; k < 6; ++k) A[k] = __builtin_amdgcn_alignbyte(d[k + 1], d[k], sh);
             } else {
+                unsigned xs[12];
 #pragma unroll
-                for (int k = 0; k < 11; ++k) {
+                for (int k = 0; k < 12; ++k) {
                     const int u = c * C + 8 * g8 - 3 + k;            // position inside the sequence
-                    float x = 0.f;                                   // past the end: masked below
-                    if (u < 0) x = __uint_as_float(static_cast<unsigned>(cin[(static_cast<size_t>(n) * a.D + ch) * (kConvK - 1) + (kConvK - 1) + u]) << 16);
-                    else if (u < seg.len) x = __uint_as_float(static_cast<unsigned>(xr[ch * a.L + seg.start + u]) << 16);
-                    xv[k] = x;
+                    unsigned x = 0u;                                 // past the end: masked below
+                    if (k < 11 && u < 0) x = cin[(static_cast<size_t>(n) * a.D + ch) * (kConvK - 1) + (kConvK - 1) + u];
+                    else if (k < 11 && u < seg.len) x = xr[ch * a.L + seg.start + u];
+                    xs[k] = x;
                 }
+#pragma unroll
+                for (int k = 0; k < 6; ++k) A[k] = xs[2 * k] | xs[2 * k + 1] << 16;
             }
-            const float w0 = lo(wraw[i].x), w1 = hi(wraw[i].x), w2 = lo(wraw[i].y), w3 = hi(wraw[i].y);
+            unsigned Bp[5];
+#pragma unroll
+            for (int k = 0; k < 5; ++k) Bp[k] = __builtin_amdgcn_alignbyte(A[k + 1], A[k], 2u);
+            const bf16x2 w01 = pair(wraw[i].x), w23 = pair(wraw[i].y);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                float acc = w0 * xv[j];
-                acc = __fmaf_rn(w1, xv[j + 1], acc);
-                acc = __fmaf_rn(w2, xv[j + 2], acc);
-                acc = __fmaf_rn(w3, xv[j + 3], acc);
+                const unsigned lo2 = (j & 1) ? Bp[j >> 1] : A[j >> 1];           // (x_j, x_j+1)
+                const unsigned hi2 = (j & 1) ? Bp[(j >> 1) + 1] : A[(j >> 1) + 1];   // (x_j+2, x_j+3)
+                const float acc = __builtin_amdgcn_fdot2_f32_bf16(w23, pair(hi2),
+                                                                  __builtin_amdgcn_fdot2_f32_bf16(w01, pair(lo2), 0.f, false), false);
                 vv[i][j] = 8 * g8 + j < nt ? fast_silu(acc) : 0.f;
                 vmax = fmaxf(vmax, fabsf(bt[j] * vv[i][j]));
             }
@@ -744,11 +752,14 @@ __global__ __launch_bounds__(256, 4) void chunk_kernel(PrefillArgs a, Ws ws) {
     __syncthreads();
     const int eV = pow2_exponent(fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3])));
     const float sV = ldexpf(1.f, -eV);
+    float bs[8];                    // beta_s 2^-eV (exact: a power of two)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) bs[j] = bt[j] * sV;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {   // row f of VbT, tokens 8 g8 .. + 7: one 16-byte store
         f16x8 hv;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) hv[j] = static_cast<_Float16>(bt[j] * vv[i][j] * sV);
+        for (int j = 0; j < 8; ++j) hv[j] = static_cast<_Float16>(bs[j] * vv[i][j]);
         *reinterpret_cast<f16x8*>(VbT + (f0 + 32 * i) * TS + 8 * g8) = hv;
     }
     // the value channels' conv state after the sequence: its last K-1 raw inputs (or the
