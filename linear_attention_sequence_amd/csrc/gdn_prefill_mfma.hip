@@ -456,7 +456,7 @@ __global__ __launch_bounds__(256, 4) void chunk_kernel(PrefillArgs a, Ws ws) {
     constexpr int REGION = 2 * D * TS * 2;  // 36864 B >= 64*136*2 + 64*65*4 = 34048 B
     static_assert(C * AS * 4 <= C * KS * 2, "T must fit where the keys were");
     __shared__ __align__(16) unsigned char region[REGION];
-    __shared__ __align__(16) float s_g[C], s_b[C], s_gam[C], s_red[4];
+    __shared__ __align__(16) float s_b[C], s_gam[C], s_red[4];
     _Float16* Kc = reinterpret_cast<_Float16*>(region);
     float* Am = reinterpret_cast<float*>(region + C * KS * 2);
     float* Tm = reinterpret_cast<float*>(region);   // written only after the Gram phase's last read of Kc
@@ -500,12 +500,10 @@ __global__ __launch_bounds__(256, 4) void chunk_kernel(PrefillArgs a, Ws ws) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) *reinterpret_cast<f16x8*>(Kc + r * KS + 8 * (wave + 4 * q)) = kreg[q];
     }
-    if (tid < C) {
-        float gv = 0.f, bv = 0.f;
-        if (tid < nt) gate_beta_at<Tin>(gate, beta, a.fu.A_log, a.fu.dt_bias, (tok0 + tid) * a.Hv + h, h, &gv, &bv);
-        s_g[tid] = gv;
-        s_b[tid] = bv;
-    }
+    // gate and beta of token `lane` (wave 0; zero past the end)
+    static_assert(C == kWave, "one wave holds the chunk's gates");
+    float gv = 0.f, bv = 0.f;
+    if (wave == 0 && tid < nt) gate_beta_at<Tin>(gate, beta, a.fu.A_log, a.fu.dt_bias, (tok0 + tid) * a.Hv + h, h, &gv, &bv);
     // q rows of this wave's 16-token tile, straight into registers (A operands)
     f16x8 aq[4];
     {
@@ -517,15 +515,15 @@ __global__ __launch_bounds__(256, 4) void chunk_kernel(PrefillArgs a, Ws ws) {
             aq[ks] = t < nt ? v : f16x8{0, 0, 0, 0, 0, 0, 0, 0};
         }
     }
-    __syncthreads();
-    if (wave == 0) {   // Gam = inclusive cumulative sum of g (wave scan)
-        float v = s_g[lane];
+    if (wave == 0) {   // Gam = inclusive cumulative sum of g (wave scan, from the registers)
+        float v = gv;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             const float o = __shfl_up(v, off, 64);
             if (lane >= off) v += o;
         }
         s_gam[lane] = v;
+        s_b[lane] = bv;
     }
     __syncthreads();
 
