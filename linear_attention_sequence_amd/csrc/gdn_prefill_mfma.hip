@@ -452,7 +452,7 @@ __global__ __launch_bounds__(256, 4) void chunk_kernel(PrefillArgs a, Ws ws) {
     // region: {Kc [C][KS] halfs, Am [C][AS] floats} during the Gram phase,
     //         {Tm [C][AS] floats over Kc, Am} during the solve,
     //         {KbT [D][TS], VbT [D][TS] halfs} during the W/U phase.
-    // 37.7 KB of LDS in all (and 119 registers): four workgroups per CU.
+    // 37.4 KB of LDS in all (and 114 registers): four workgroups per CU.
     constexpr int REGION = 2 * D * TS * 2;  // 36864 B >= 64*136*2 + 64*65*4 = 34048 B
     static_assert(C * AS * 4 <= C * KS * 2, "T must fit where the keys were");
     __shared__ __align__(16) unsigned char region[REGION];
@@ -956,12 +956,13 @@ __device__ int sequence_of_rank(const PrefillArgs& a, int r) {
     return s_pick;
 }
 
-template <int NTW, int NW, bool LW, bool NORM>
-__global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws ws) {
+template <int NTW, int NW, bool LW, bool NORM, int NL>
+__global__ __launch_bounds__((NW + (LW ? NL : 0)) * 64) void carry_kernel(PrefillArgs a, Ws ws) {
     constexpr int CPW = NW * NTW * 16;
     // NORM: the gated RMSNorm of each token's head row is applied before its store,
     // which needs the whole row (all 128 columns) in this workgroup
     static_assert(!NORM || (NTW == 1 && NW * 16 == D && !LW), "a fused norm needs a whole-head workgroup");
+    static_assert(NL == 1 || (LW && NL == 2 && NW % NL == 0), "one or two loader waves");
     // One wave per SIMD (NW <= 4) leaves registers to hold a whole phase's operands:
     // their LDS reads are then issued ahead of the phase's MFMAs under one wait (a
     // scheduling barrier keeps them there). With two waves per SIMD the waves hide
@@ -993,9 +994,10 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
     if (a.cu != nullptr && a.N <= kSortMax) n = sequence_of_rank(a, n);
     const int f = a.Hv / a.Hk, hk = h / f;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    // With LW an extra wave (wave NW) issues every stage load and waits for it, so the
+    // With LW NL extra waves (waves NW ..) issue every stage load and wait for them, so the
     // compute waves never stall on the memory pipeline's queue.
-    const bool loader = LW && wave == NW;
+    const bool loader = LW && wave >= NW;
+    const int li = loader ? wave - NW : 0;               // loader li issues the compute waves li, li + NL, ...
     const int g = lane >> 4, r16 = lane & 15;
     const int ucol0 = cs * CPW;                          // first column of this workgroup
     const int lcol0 = wave * 16 * NTW;                   // first column of this wave, inside the workgroup
@@ -1075,8 +1077,8 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
     const bool prologue = NTW == 1 && np > 0;
     if ((!LW || loader) && cb < ce && !prologue) {
 #pragma unroll
-        for (int w = LW ? 0 : wave; w < (LW ? NW : wave + 1); ++w)
-            issue_all(base + cb, row_tok + static_cast<size_t>(cb) * C, min(C, seg.len - cb * C), 0, w);
+        for (int k = 0; k < (LW ? NW / NL : 1); ++k)   // a loader: compute waves li, li + NL, ...; else its own
+            issue_all(base + cb, row_tok + static_cast<size_t>(cb) * C, min(C, seg.len - cb * C), 0, LW ? li + NL * k : wave);
     }
     // Segmented mode, pass 2: segment sj >= 2 enters with S_sj = M_{sj-1} S_{sj-1} + R_{sj-1}
     // from S_{m0+1} (S_1, or R_m0 after a zero map), formed here on this workgroup's columns
@@ -1095,8 +1097,8 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
                 }
                 if (cb < ce)
 #pragma unroll
-                    for (int w = 0; w < NW; ++w)
-                        issue_all(base + cb, row_tok + static_cast<size_t>(cb) * C, min(C, seg.len - cb * C), 0, w);
+                    for (int k = 0; k < NW / NL; ++k)
+                        issue_all(base + cb, row_tok + static_cast<size_t>(cb) * C, min(C, seg.len - cb * C), 0, li + NL * k);
             } else {
                 __shared__ int s_ek[kMaxSeg - 2][D / 16];
                 static_assert(2 * D * D * 2 <= SG::BYTES, "a map fits a stage buffer");
@@ -1196,7 +1198,7 @@ __global__ __launch_bounds__((NW + LW) * 64) void carry_kernel(PrefillArgs a, Ws
                 const int ntn = min(C, seg.len - (c + 1) * C);
                 const int sbn = (c - cb + 1) & 1;
 #pragma unroll
-                for (int w = 0; w < NW; ++w) issue_all(base + c + 1, tokn, ntn, sbn, w);
+                for (int k = 0; k < NW / NL; ++k) issue_all(base + c + 1, tokn, ntn, sbn, li + NL * k);
             }
         }
         return;
@@ -1562,17 +1564,19 @@ static int device_cu_count() {
     return cached[dev];
 }
 
-// The carry configurations: (tiles per wave, waves per workgroup, loader wave, fused norm).
-template <int NTW, int NW, bool LW = false, bool NORM = false>
+// The carry configurations: (tiles per wave, waves per workgroup, loader waves, fused
+// norm, number of loader waves).
+template <int NTW, int NW, bool LW = false, bool NORM = false, int NL = 1>
 static hipError_t launch_carry(void** args, long long heads, hipStream_t stream) {
     constexpr int CPW = NW * NTW * 16;
     constexpr size_t lds = 2 * pf2::Stage<CPW>::BYTES;
     static_assert(lds + 8 * 1024 <= 160 * 1024, "LDS of one CU (the stages and the kernel's static arrays)");
-    const void* k = reinterpret_cast<const void*>(&pf2::carry_kernel<NTW, NW, LW, NORM>);
+    const void* k = reinterpret_cast<const void*>(&pf2::carry_kernel<NTW, NW, LW, NORM, NL>);
     // dynamic LDS above 64 KB must be allowed per kernel before its first launch
     static const hipError_t allowed = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (allowed != hipSuccess) return allowed;
-    return hipLaunchKernel(k, dim3(static_cast<unsigned>(heads * (128 / CPW))), dim3((NW + LW) * 64), args, lds, stream);
+    return hipLaunchKernel(k, dim3(static_cast<unsigned>(heads * (128 / CPW))), dim3((NW + (LW ? NL : 0)) * 64), args, lds,
+                           stream);
 }
 
 template <typename Tin>
@@ -1606,6 +1610,10 @@ static hipError_t launch_mfma_t(const PrefillArgs& a, int in_dtype, hipStream_t 
         void* argp[] = {const_cast<PrefillArgs*>(&a), &wp};
         static_assert(kWholeNTW == 1, "the first pass writes the state maps from one column tile per wave");
         if (norm) e = launch_carry<kWholeNTW, kWholeNW, false, true>(argp, cp.l[i].units, stream);
+        // the second pass (entry states from the maps first) with two loader waves: the
+        // first chunk's stage goes out faster after the prologue (L=4096 138.5 -> 135.3 us);
+        // one loader for the unsegmented carry, where two measured no gain
+        else if (cp.l[i].half && cp.l[i].pass == 2) e = launch_carry<1, 4, true, false, 2>(argp, cp.l[i].units, stream);
         else if (cp.l[i].half) e = launch_carry<1, 4, true>(argp, cp.l[i].units, stream);
         else e = launch_carry<kWholeNTW, kWholeNW>(argp, cp.l[i].units, stream);
         if (e != hipSuccess) return e;

@@ -57,6 +57,7 @@ struct Config {
 struct WG {   // one carry workgroup's template shape
     int NW, NTW;
     bool LW;
+    int NL;       // loader waves (with LW)
     int CPW() const { return NW * NTW * 16; }
 };
 
@@ -131,7 +132,14 @@ size_t check_map_geometry(int NW, int BYTES) {
 }
 
 void model_launch(const Config& c, const Layout& lay, int nseg, const CarryLaunch& cl, bool norm) {
-    const WG wg = cl.half ? WG{4, 1, true} : WG{8, 1, false};
+    // the launcher's choice: half-head workgroups with one loader wave, two in the second pass
+    const WG wg = cl.half ? WG{4, 1, true, cl.pass == 2 ? 2 : 1} : WG{8, 1, false, 1};
+    if (wg.LW) {   // loader li issues the stage shares of compute waves li + NL k: each share exactly once
+        std::vector<int> share(wg.NW, 0);
+        for (int li = 0; li < wg.NL; ++li)
+            for (int k = 0; k < wg.NW / wg.NL; ++k) ++share[li + wg.NL * k];
+        for (int v : share) REQUIRE(v == 1);
+    }
     REQUIRE(!norm || (!wg.LW && wg.NTW == 1 && wg.CPW() == D));   // the fused norm needs whole-head workgroups
     const int CPW = wg.CPW(), NS = 128 / CPW, nh = c.N * c.Hv;
     const int NK = carry_kinds(nseg, cl.pass);
@@ -275,6 +283,7 @@ void model_launch(const Config& c, const Layout& lay, int nseg, const CarryLaunc
                                 (norm && job.outs && ce > cb ? 1 : 0);
             REQUIRE(!(norm && job.outs) || job.map < 0);   // a job forms outputs or writes a map, not both
             if (wg.LW) {
+                // every loader wave (one or two) runs the same loop
                 const int loader = sortb + (prologue ? 2 * np : 0) + (ce - cb) + (g_plant == "loader_barrier" && np > 1 ? 1 : 0);
                 REQUIRE(loader == compute);
             }

@@ -156,7 +156,8 @@ def test_verify_fused(shape, dtype, B, T, pro, epi):
 @pytest.mark.parametrize("pro,epi", FUSIONS)
 @pytest.mark.parametrize("shape,dtype,B,L", [(SMALL128, "bf16", 1, 200), (SMALL128, "f32", 2, 129),
                                              (gi.TINY_GQA, "bf16", 2, 70), (gi.TINY, "f32", 1, 64),
-                                             (SMALL128, "bf16", 1, 1300)])   # 1300: the 5-segment carry
+                                             (SMALL128, "bf16", 1, 1300),    # 1300: the 5-segment carry
+                                             (SMALL128, "bf16", 2, 777)])    # two rows, segmented, ragged tail chunk
 def test_prefill_fused(shape, dtype, B, L, pro, epi):
     _say(f"prefill_ex {shape} {dtype} B={B} L={L} prologue={pro} epilogue={epi}")
     inp = fused_inputs(shape, B, L, 53, dtype, pro, epi)
