@@ -142,6 +142,9 @@ def _ceiling_lib():
     lib.gdn_ceiling_copy.argtypes = [V, V, SZ, I, I, V]
     lib.gdn_ceiling_mfma.argtypes = [V, I, I, I, V]
     lib.gdn_ceiling_device_info.argtypes = [I] + [ctypes.POINTER(I)] * 4
+    lib.gdn_ceiling_read_blocked.argtypes = [V, SZ, V, I, V]
+    lib.gdn_ceiling_write_blocked.argtypes = [V, SZ, I, I, V]
+    lib.gdn_ceiling_copy_blocked.argtypes = [V, V, SZ, I, I, V]
     return lib
 
 
@@ -177,15 +180,34 @@ def measure_ceilings(torch, lib, cus):
             raise RuntimeError(f"ceiling kernel failed ({st})")
 
     grids = [cus * k for k in (4, 8, 16, 32)]
-    out = {}
-    out["hbm_read_GBs"] = max(rate(lambda g=g: check(lib.gdn_ceiling_read(P(src), nbytes, P(sink), g, s)), nbytes)
-                              for g in grids) / 1e9
+    per_thread = (4, 8, 16)
+    out, best = {}, {}
+
+    def best_of(key, forms):
+        """forms: (label, fn, units); keeps the fastest and which form it was"""
+        rates = [(rate(fn, units), label) for label, fn, units in forms]
+        r, label = max(rates)
+        out[key] = r / 1e9
+        best[key] = label
+
+    best_of("hbm_read_GBs",
+            [(f"grid-stride, {g // cus} workgroups/CU",
+              lambda g=g: check(lib.gdn_ceiling_read(P(src), nbytes, P(sink), g, s)), nbytes) for g in grids] +
+            [(f"blocked, {u} per thread", lambda u=u: check(lib.gdn_ceiling_read_blocked(P(src), nbytes, P(sink), u, s)),
+              nbytes) for u in per_thread])
     for nt, key in ((1, "hbm_write_nt_GBs"), (0, "hbm_write_GBs")):
-        out[key] = max(rate(lambda g=g: check(lib.gdn_ceiling_write(P(dst), nbytes, nt, g, s)), nbytes)
-                       for g in grids) / 1e9
+        best_of(key,
+                [(f"grid-stride, {g // cus} workgroups/CU",
+                  lambda g=g: check(lib.gdn_ceiling_write(P(dst), nbytes, nt, g, s)), nbytes) for g in grids] +
+                [(f"blocked, {u} per thread", lambda u=u: check(lib.gdn_ceiling_write_blocked(P(dst), nbytes, nt, u, s)),
+                  nbytes) for u in per_thread])
     for nt, key in ((1, "hbm_copy_nt_GBs"), (0, "hbm_copy_GBs")):
-        out[key] = max(rate(lambda g=g: check(lib.gdn_ceiling_copy(P(src), P(dst), nbytes, nt, g, s)), 2 * nbytes)
-                       for g in grids) / 1e9
+        best_of(key,
+                [(f"grid-stride, {g // cus} workgroups/CU",
+                  lambda g=g: check(lib.gdn_ceiling_copy(P(src), P(dst), nbytes, nt, g, s)), 2 * nbytes) for g in grids] +
+                [(f"blocked, {u} per thread",
+                  lambda u=u: check(lib.gdn_ceiling_copy_blocked(P(src), P(dst), nbytes, nt, u, s)), 2 * nbytes)
+                 for u in per_thread])
     iters = 2000
     for dt, key, fl in ((0, "mfma_f16_16x16x32_TFLOPs", 16384), (1, "mfma_bf16_16x16x32_TFLOPs", 16384),
                         (2, "mfma_f16_32x32x16_TFLOPs", 32768), (3, "mfma_bf16_32x32x16_TFLOPs", 32768)):
@@ -193,9 +215,11 @@ def measure_ceilings(torch, lib, cus):
                             g * 4 * iters * 8 * fl, per_rep=3) for g in (cus * 2, cus * 4)) / 1e12
     out["mfma_f16_TFLOPs"] = max(out["mfma_f16_16x16x32_TFLOPs"], out["mfma_f16_32x32x16_TFLOPs"])
     out["copy_best_GBs"] = max(out["hbm_copy_GBs"], out["hbm_copy_nt_GBs"])
-    out["note"] = ("1 GiB per memory kernel (4x the Infinity Cache), grid sizes 4-32 workgroups per CU, "
-                   "median of 5 repetitions of 10 launches back to back, best grid; copy counts read + write "
-                   "bytes; MFMA: 8 independent chains per wave, 2 or 4 workgroups of 4 waves per CU")
+    out["best_form"] = best
+    out["note"] = ("1 GiB per memory kernel (4x the Infinity Cache): grid-stride loops at 4-32 workgroups per CU and "
+                   "blocked forms (4, 8 or 16 granules per thread, all loads before the stores); median of 5 "
+                   "repetitions of 10 launches back to back, best form; copy counts read + write bytes; MFMA: 8 "
+                   "independent chains per wave, 2 or 4 workgroups of 4 waves per CU")
     del src, dst, sink
     torch.cuda.empty_cache()
     return out

@@ -34,6 +34,16 @@ int gdn_ceiling_write(void* dst, size_t bytes, int nontemporal, int grid, void* 
 int gdn_ceiling_copy(const void* src, void* dst, size_t bytes, int nontemporal, int grid,
                      void* stream);
 
+/* Blocked forms of the three: workgroup b (256 threads) moves the contiguous block of
+ * per_thread * 4096 bytes at offset b * per_thread * 4096, a thread's per_thread 16-byte
+ * granules 4096 bytes apart, all its loads issued before any of its stores (the access
+ * pattern of the layer's commit kernel). per_thread is 4, 8 or 16; bytes a multiple of
+ * per_thread * 4096 and at most 2^20 blocks; the grid is bytes / (per_thread * 4096). */
+int gdn_ceiling_read_blocked(const void* src, size_t bytes, float* sink, int per_thread, void* stream);
+int gdn_ceiling_write_blocked(void* dst, size_t bytes, int nontemporal, int per_thread, void* stream);
+int gdn_ceiling_copy_blocked(const void* src, void* dst, size_t bytes, int nontemporal, int per_thread,
+                             void* stream);
+
 /* `iters` rounds of 8 independent MFMA products per wave, 4 waves per workgroup. dtype
  * 0: v_mfma_f32_16x16x32_f16, 1: ..._16x16x32_bf16 (16384 flops each: grid * 4 * iters *
  * 8 * 16384 in all); 2: v_mfma_f32_32x32x16_f16, 3: ..._32x32x16_bf16 (32768 flops each).

@@ -1,7 +1,8 @@
 // Measurement kernels: achievable HBM read / write / copy rates and the MFMA
-// throughput of the device (see include/gdn_ceiling.h). Each is the simplest form that
-// keeps the unit under test saturated: 16-byte accesses with several in flight per
-// thread for memory, eight independent accumulator chains per wave for MFMA.
+// throughput of the device (see include/gdn_ceiling.h). Each is a simple form that
+// keeps the unit under test saturated: 16-byte accesses, grid-stride or in blocks with
+// up to 16 in flight per thread, for memory; eight independent accumulator chains per
+// wave for MFMA.
 #include "gdn_ceiling.h"
 
 #include <hip/hip_runtime.h>
@@ -40,6 +41,46 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(const f32x4* __restrict_
     for (size_t i = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x; i < n; i += stride) {
         if constexpr (NT) __builtin_nontemporal_store(src[i], dst + i);
         else dst[i] = src[i];
+    }
+}
+
+// Blocked forms: workgroup b moves the contiguous block of U * 256 granules starting at
+// granule b * U * 256, each thread's U granules 256 apart (every load instruction of a
+// wave covers 1 KB of consecutive memory), all of a thread's loads issued before any of
+// its stores (the pattern of the layer's commit kernel).
+template <int U>
+__global__ __launch_bounds__(kThreads) void read_blocked(const f32x4* __restrict__ src, float* sink) {
+    const size_t base = static_cast<size_t>(blockIdx.x) * U * kThreads + threadIdx.x;
+    f32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = src[base + static_cast<size_t>(u) * kThreads];
+    f32x4 acc = v[0];
+#pragma unroll
+    for (int u = 1; u < U; ++u) acc += v[u];
+    if (acc.x == -1.2345e30f) sink[blockIdx.x] = acc.y + acc.z + acc.w;   // never true for the data read
+}
+
+template <bool NT, int U>
+__global__ __launch_bounds__(kThreads) void write_blocked(f32x4* __restrict__ dst) {
+    const size_t base = static_cast<size_t>(blockIdx.x) * U * kThreads + threadIdx.x;
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if constexpr (NT) __builtin_nontemporal_store(z, dst + base + static_cast<size_t>(u) * kThreads);
+        else dst[base + static_cast<size_t>(u) * kThreads] = z;
+    }
+}
+
+template <bool NT, int U>
+__global__ __launch_bounds__(kThreads) void copy_blocked(const f32x4* __restrict__ src, f32x4* __restrict__ dst) {
+    const size_t base = static_cast<size_t>(blockIdx.x) * U * kThreads + threadIdx.x;
+    f32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = src[base + static_cast<size_t>(u) * kThreads];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if constexpr (NT) __builtin_nontemporal_store(v[u], dst + base + static_cast<size_t>(u) * kThreads);
+        else dst[base + static_cast<size_t>(u) * kThreads] = v[u];
     }
 }
 
@@ -124,6 +165,61 @@ int gdn_ceiling_copy(const void* src, void* dst, size_t bytes, int nontemporal, 
     f32x4* dp = static_cast<f32x4*>(dst);
     if (nontemporal) copy_kernel<true><<<grid, kThreads, 0, s>>>(sp, dp, bytes / 16);
     else copy_kernel<false><<<grid, kThreads, 0, s>>>(sp, dp, bytes / 16);
+    return launched();
+}
+
+// blocked forms: per_thread 4, 8 or 16 granules; bytes a multiple of one block
+static bool blocked_ok(size_t bytes, int per_thread) {
+    if (per_thread != 4 && per_thread != 8 && per_thread != 16) return false;
+    const size_t block = static_cast<size_t>(per_thread) * kThreads * 16;
+    return bytes > 0 && bytes % block == 0 && bytes / block <= (static_cast<size_t>(1) << 20);
+}
+
+int gdn_ceiling_read_blocked(const void* src, size_t bytes, float* sink, int per_thread, void* stream) {
+    if (!src || !sink || !blocked_ok(bytes, per_thread) || !al16(src)) return 1;
+    const unsigned grid = static_cast<unsigned>(bytes / (static_cast<size_t>(per_thread) * kThreads * 16));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const f32x4* sp = static_cast<const f32x4*>(src);
+    if (per_thread == 4) read_blocked<4><<<grid, kThreads, 0, s>>>(sp, sink);
+    else if (per_thread == 8) read_blocked<8><<<grid, kThreads, 0, s>>>(sp, sink);
+    else read_blocked<16><<<grid, kThreads, 0, s>>>(sp, sink);
+    return launched();
+}
+
+int gdn_ceiling_write_blocked(void* dst, size_t bytes, int nontemporal, int per_thread, void* stream) {
+    if (!dst || !blocked_ok(bytes, per_thread) || !al16(dst)) return 1;
+    const unsigned grid = static_cast<unsigned>(bytes / (static_cast<size_t>(per_thread) * kThreads * 16));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    f32x4* dp = static_cast<f32x4*>(dst);
+    if (nontemporal) {
+        if (per_thread == 4) write_blocked<true, 4><<<grid, kThreads, 0, s>>>(dp);
+        else if (per_thread == 8) write_blocked<true, 8><<<grid, kThreads, 0, s>>>(dp);
+        else write_blocked<true, 16><<<grid, kThreads, 0, s>>>(dp);
+    } else {
+        if (per_thread == 4) write_blocked<false, 4><<<grid, kThreads, 0, s>>>(dp);
+        else if (per_thread == 8) write_blocked<false, 8><<<grid, kThreads, 0, s>>>(dp);
+        else write_blocked<false, 16><<<grid, kThreads, 0, s>>>(dp);
+    }
+    return launched();
+}
+
+int gdn_ceiling_copy_blocked(const void* src, void* dst, size_t bytes, int nontemporal, int per_thread, void* stream) {
+    if (!src || !dst || !blocked_ok(bytes, per_thread) || !al16(src) || !al16(dst)) return 1;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+    if (a < b + bytes && b < a + bytes) return 1;
+    const unsigned grid = static_cast<unsigned>(bytes / (static_cast<size_t>(per_thread) * kThreads * 16));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const f32x4* sp = static_cast<const f32x4*>(src);
+    f32x4* dp = static_cast<f32x4*>(dst);
+    if (nontemporal) {
+        if (per_thread == 4) copy_blocked<true, 4><<<grid, kThreads, 0, s>>>(sp, dp);
+        else if (per_thread == 8) copy_blocked<true, 8><<<grid, kThreads, 0, s>>>(sp, dp);
+        else copy_blocked<true, 16><<<grid, kThreads, 0, s>>>(sp, dp);
+    } else {
+        if (per_thread == 4) copy_blocked<false, 4><<<grid, kThreads, 0, s>>>(sp, dp);
+        else if (per_thread == 8) copy_blocked<false, 8><<<grid, kThreads, 0, s>>>(sp, dp);
+        else copy_blocked<false, 16><<<grid, kThreads, 0, s>>>(sp, dp);
+    }
     return launched();
 }
 

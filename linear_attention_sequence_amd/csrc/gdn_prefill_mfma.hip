@@ -1611,7 +1611,7 @@ static hipError_t launch_mfma_t(const PrefillArgs& a, int in_dtype, hipStream_t 
         static_assert(kWholeNTW == 1, "the first pass writes the state maps from one column tile per wave");
         if (norm) e = launch_carry<kWholeNTW, kWholeNW, false, true>(argp, cp.l[i].units, stream);
         // the second pass (entry states from the maps first) with two loader waves: the
-        // first chunk's stage goes out faster after the prologue (L=4096 138.5 -> 135.3 us);
+        // first chunk's stage goes out sooner after the prologue (L=4096 1-3 us faster);
         // one loader for the unsegmented carry, where two measured no gain
         else if (cp.l[i].half && cp.l[i].pass == 2) e = launch_carry<1, 4, true, false, 2>(argp, cp.l[i].units, stream);
         else if (cp.l[i].half) e = launch_carry<1, 4, true>(argp, cp.l[i].units, stream);

@@ -45,8 +45,9 @@ def test_ceiling_library_exports_and_validation(lib):
     assert os.path.exists(path)
     cl = ctypes.CDLL(path)
     names = header_symbols("gdn_ceiling.h")
-    assert names == ["gdn_ceiling_copy", "gdn_ceiling_device_info", "gdn_ceiling_mfma",
-                     "gdn_ceiling_read", "gdn_ceiling_write"]
+    assert names == ["gdn_ceiling_copy", "gdn_ceiling_copy_blocked", "gdn_ceiling_device_info",
+                     "gdn_ceiling_mfma", "gdn_ceiling_read", "gdn_ceiling_read_blocked", "gdn_ceiling_write",
+                     "gdn_ceiling_write_blocked"]
     for name in names:
         assert hasattr(cl, name), name
     V, I, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
@@ -57,6 +58,14 @@ def test_ceiling_library_exports_and_validation(lib):
     assert cl.gdn_ceiling_copy(A(1), A(2), 100, 1, 1024, None) == 1               # not a multiple of 64
     assert cl.gdn_ceiling_read(A(1), 1 << 20, A(2), 0, None) == 1                 # empty grid
     assert cl.gdn_ceiling_mfma(A(1), 256, 10, 4, None) == 1                       # unknown dtype
+    cl.gdn_ceiling_copy_blocked.argtypes = [V, V, SZ, I, I, V]
+    cl.gdn_ceiling_read_blocked.argtypes = [V, SZ, V, I, V]
+    cl.gdn_ceiling_write_blocked.argtypes = [V, SZ, I, I, V]
+    assert cl.gdn_ceiling_copy_blocked(A(1), A(2), 1 << 20, 1, 5, None) == 1      # per_thread not 4, 8, 16
+    assert cl.gdn_ceiling_copy_blocked(A(1), A(2), 3 << 12, 1, 4, None) == 1      # not a multiple of the 16 KB block
+    assert cl.gdn_ceiling_copy_blocked(A(1), A(1), 1 << 20, 1, 16, None) == 1     # overlap
+    assert cl.gdn_ceiling_read_blocked(A(1), 1 << 20, None, 8, None) == 1         # no sink
+    assert cl.gdn_ceiling_write_blocked(A(1), 1 << 40, 1, 4, None) == 1           # more than 2^20 blocks
 
 
 def test_status_strings_and_version(lib):
