@@ -23,10 +23,21 @@
 // 4 consecutive columns 4*cg..4*cg+3 of rows rg, rg + RG, rg + 2*RG, ... as
 // float4 registers (CG = dv/4 column groups, RG = NT/CG row groups), so each
 // row is read by CG consecutive lanes with 16-byte loads (fully coalesced).
+//
+// Verify blocks at dk = dv = 128 (without the RMSNorm epilogue) run a narrow layout
+// on 1024 threads: thread (rg, cg) = (wave, lane) holds 2 columns of the same rows
+// rg + 16 r (r < 8), so each column's partial sums are the same FMA chains as in the
+// 512-thread layout, and the row groups 2w and 2w + 1 (one wave each here, two halves
+// of one wave there) are added before the waves' sums, in the same order: a verify
+// block still equals its decode steps bit for bit.
 #include "gdn_common.hpp"
 #include "gdn_launch.hpp"
 
+#include <type_traits>
+
 namespace gdn {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // Tile geometry: NT threads own a DK x CW slice (columns j0..j0+CW) of one
 // (sequence, V head) state tile.
@@ -254,18 +265,148 @@ __device__ __forceinline__ void recur_tail(const RecArgs& a, const Unit& u, cons
     }
 }
 
-// Any T (verify blocks, and decode at head dim 16): one unit per workgroup.
-template <typename Tin, int DK, int DV, int NT, int CW, bool NT_STORE, bool NT_LOAD, bool PRO, bool EPI>
-__global__ __launch_bounds__(NT) void recurrent_kernel(RecArgs a) {
+// The narrow layout (see the top of the file): DK x CW tile on NT threads of 2 columns.
+template <int DK, int CW, int NT>
+struct NarrowGeom {
+    static constexpr int CG = CW / 2;         // column pairs: one wave's lanes
+    static constexpr int RG = NT / CG;        // row groups: one per wave
+    static constexpr int RPT = DK / RG;
+    static constexpr int NW = NT / kWave;
+    static_assert(CG == kWave && RG == NW && RG % 2 == 0, "one row group per wave, pairs of waves");
+};
+
+template <int DK, int DV, int NT, int CW, bool NT_LOAD>
+__device__ __forceinline__ void load_tile_narrow(const RecArgs& a, const Unit& u, float2 (&s)[NarrowGeom<DK, CW, NT>::RPT]) {
+    using G = NarrowGeom<DK, CW, NT>;
+    const int cg = threadIdx.x % G::CG, rg = threadIdx.x / G::CG;
+    size_t src = u.bh;
+    if (a.slot != nullptr) {
+        int k = a.slot[u.b];
+        k = k < 0 ? 0 : (k > a.slot_T - 1 ? a.slot_T - 1 : k);
+        src = (static_cast<size_t>(u.b) * a.slot_T + k) * a.Hv + u.h;
+    }
+    const float* Sin = a.S_in + src * DK * DV + u.j0;
+#pragma unroll
+    for (int r = 0; r < G::RPT; ++r) {
+        const float* p = Sin + static_cast<size_t>(rg + r * G::RG) * DV + 2 * cg;
+        if constexpr (NT_LOAD) {
+            const f32x2 v = __builtin_nontemporal_load(reinterpret_cast<const f32x2*>(p));
+            s[r] = make_float2(v[0], v[1]);
+        } else {
+            s[r] = *reinterpret_cast<const float2*>(p);
+        }
+    }
+}
+
+// recur_tail on the narrow layout (no epilogue).
+template <typename Tin, int DK, int DV, int NT, int CW, bool NT_STORE>
+__device__ __forceinline__ void recur_tail_narrow(const RecArgs& a, const Unit& u, const RecLds& L, int T,
+                                                  float2 (&s)[NarrowGeom<DK, CW, NT>::RPT]) {
+    using G = NarrowGeom<DK, CW, NT>;
+    constexpr int CG = G::CG, RG = G::RG, RPT = G::RPT, NW = G::NW;
+    const int tid = threadIdx.x;
+    const int cg = tid % CG, rg = tid / CG;
+    const int lane = tid % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const float qscale = 1.0f / sqrtf(static_cast<float>(DK));
+    for (int t = wave; t < T; t += NW) {   // norms, as in recur_tail
+        float qq = 0.f, kk = 0.f, kq = 0.f;
+        for (int i = lane; i < DK; i += kWave) {
+            const float qv = L.sq[t * DK + i], kv = L.sk[t * DK + i];
+            qq = __fmaf_rn(qv, qv, qq);
+            kk = __fmaf_rn(kv, kv, kk);
+            kq = __fmaf_rn(kv, qv, kq);
+        }
+        qq = wave_sum(qq);
+        kk = wave_sum(kk);
+        kq = wave_sum(kq);
+        const float rq = a.use_l2 ? 1.0f / sqrtf(qq + a.eps) : 1.0f;
+        const float rk = a.use_l2 ? 1.0f / sqrtf(kk + a.eps) : 1.0f;
+        const float qs = rq * qscale;
+        if (lane == 0) {
+            L.s_kq[3 * t] = rk;
+            L.s_kq[3 * t + 1] = qs;
+            L.s_kq[3 * t + 2] = kq * rk * qs;
+        }
+    }
+    for (int t = 0; t < T; ++t) {
+        float pk[2] = {0.f, 0.f}, pq[2] = {0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+            const int i = rg + r * RG;
+            const float kv = L.sk[t * DK + i], qv = L.sq[t * DK + i];
+            pk[0] = __fmaf_rn(s[r].x, kv, pk[0]); pq[0] = __fmaf_rn(s[r].x, qv, pq[0]);
+            pk[1] = __fmaf_rn(s[r].y, kv, pk[1]); pq[1] = __fmaf_rn(s[r].y, qv, pq[1]);
+        }
+        // one row group per wave: its partials go to LDS as they are, S^T k and S^T q in
+        // separate planes (double-buffered by token)
+        float* redk = L.red + (t & 1) * (NW * CG * 4);
+        float* redq = redk + NW * CG * 2;
+        *reinterpret_cast<float2*>(redk + (wave * CG + cg) * 2) = make_float2(pk[0], pk[1]);
+        *reinterpret_cast<float2*>(redq + (wave * CG + cg) * 2) = make_float2(pq[0], pq[1]);
+        __syncthreads();
+        const float al = L.s_alpha[t], be = L.s_beta[t];
+        const float rk = L.s_kq[3 * t], qs = L.s_kq[3 * t + 1], kqh = L.s_kq[3 * t + 2];
+        // row groups 2w and 2w + 1 added first, then those sums in order of w
+        auto total = [&](const float* plane) {
+            float2 v = make_float2(0.f, 0.f);
+#pragma unroll
+            for (int w = 0; w < NW; w += 2) {
+                const float2 v0 = *reinterpret_cast<const float2*>(plane + (w * CG + cg) * 2);
+                const float2 v1 = *reinterpret_cast<const float2*>(plane + ((w + 1) * CG + cg) * 2);
+                v.x += v0.x + v1.x;
+                v.y += v0.y + v1.y;
+            }
+            return v;
+        };
+        const float2 PK = total(redk);   // S^T k of this lane's two columns
+        const float2 vv = *reinterpret_cast<const float2*>(L.sv + t * CW + 2 * cg);
+        const float2 d = make_float2(be * (vv.x - al * (PK.x * rk)), be * (vv.y - al * (PK.y * rk)));
+        const float2 dl = make_float2(d.x * rk, d.y * rk);
+        float* Sout = a.S_out + ((static_cast<size_t>(u.b) * T + t) * a.Hv + u.h) * DK * DV + u.j0;
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+            const float kv = L.sk[t * DK + rg + r * RG];
+            s[r].x = __fmaf_rn(kv, dl.x, al * s[r].x);
+            s[r].y = __fmaf_rn(kv, dl.y, al * s[r].y);
+            float* dst = Sout + static_cast<size_t>(rg + r * RG) * DV + 2 * cg;
+            if constexpr (NT_STORE) {
+                const f32x2 v = {s[r].x, s[r].y};
+                __builtin_nontemporal_store(v, reinterpret_cast<f32x2*>(dst));
+            } else {
+                *reinterpret_cast<float2*>(dst) = s[r];
+            }
+        }
+        if (wave == 0) {   // the output row: row group 0 is wave 0, two columns per lane
+            const float2 PQ = total(redq);
+            const float2 ov = make_float2(__fmaf_rn(d.x, kqh, al * (PQ.x * qs)), __fmaf_rn(d.y, kqh, al * (PQ.y * qs)));
+            const size_t orow = ((static_cast<size_t>(u.b) * T + t) * a.Hv + u.h) * DV + u.j0;
+            *reinterpret_cast<float2*>(a.o + orow + 2 * cg) = ov;
+        }
+    }
+}
+
+struct NoGeom { static constexpr int RPT = 1; };
+
+// Any T (verify blocks, and decode at head dim 16): one unit per workgroup. NARROW: the
+// narrow layout (verify blocks at dk = dv = 128, no epilogue).
+template <typename Tin, int DK, int DV, int NT, int CW, bool NT_STORE, bool NT_LOAD, bool PRO, bool EPI,
+          bool NARROW = false>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NARROW ? 8 : 1)))
+void recurrent_kernel(RecArgs a) {   // narrow: 64 registers, two workgroups per CU
     using G = RecGeom<DK, DV, NT, CW>;
+    using NG = std::conditional_t<NARROW, NarrowGeom<DK, CW, NT>, NoGeom>;
+    static_assert(!NARROW || (!EPI && DK == 128 && CW == DV), "the narrow layout: dk = dv = 128, no epilogue");
     extern __shared__ float lds[];
     const int T = a.T;
     const RecLds L = rec_lds<DK, CW, G::NW>(lds, T);
     const Unit u = unit_of<G::NSPLIT, CW>(a, blockIdx.x);
 
     // 1. state tile -> registers, issued first
-    float4 s[G::RPT];
-    load_tile<DK, DV, NT, CW, NT_LOAD>(a, u, s);
+    float4 s[NARROW ? 1 : G::RPT];
+    float2 s2[NG::RPT];
+    if constexpr (NARROW) load_tile_narrow<DK, DV, NT, CW, NT_LOAD>(a, u, s2);
+    else load_tile<DK, DV, NT, CW, NT_LOAD>(a, u, s);
 
     // gate and beta of token t = threadIdx.x, issued right behind the tile: their round trip
     // then overlaps the tile's instead of following the conv barrier, where it held up the
@@ -333,7 +474,8 @@ __global__ __launch_bounds__(NT) void recurrent_kernel(RecArgs a) {
         L.s_beta[tg] = bv;
     }
     __syncthreads();
-    recur_tail<Tin, DK, DV, NT, CW, NT_STORE, PRO, EPI>(a, u, L, T, s);
+    if constexpr (NARROW) recur_tail_narrow<Tin, DK, DV, NT, CW, NT_STORE>(a, u, L, T, s2);
+    else recur_tail<Tin, DK, DV, NT, CW, NT_STORE, PRO, EPI>(a, u, L, T, s);
 }
 
 // Commit: S_out[b,h] = S_snap[b, a_b, h]; the conv window after token a_b.
@@ -384,14 +526,16 @@ __global__ __launch_bounds__(256) void commit_kernel(CommitArgs a) {
     }
 }
 
-template <typename Tin, int DK, int DV, int NT, int CW, bool NT_STORE, bool NT_LOAD, bool PRO, bool EPI>
+template <typename Tin, int DK, int DV, int NT, int CW, bool NT_STORE, bool NT_LOAD, bool PRO, bool EPI,
+          bool NARROW = false>
 hipError_t launch_rec_t(const RecArgs& a, hipStream_t stream) {
     // the fused gated RMSNorm needs the whole dv row of a head in one workgroup
     static_assert(CW == DV, "column slices would split the RMSNorm row");
     const size_t lds = recurrent_lds_bytes<DK, CW, NT, EPI>(a.T);
     void* args[] = {const_cast<RecArgs*>(&a)};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&recurrent_kernel<Tin, DK, DV, NT, CW, NT_STORE, NT_LOAD, PRO, EPI>),
-                           dim3(a.B * a.Hv * (DV / CW)), dim3(NT), args, lds, stream);
+    return hipLaunchKernel(
+        reinterpret_cast<const void*>(&recurrent_kernel<Tin, DK, DV, NT, CW, NT_STORE, NT_LOAD, PRO, EPI, NARROW>),
+        dim3(a.B * a.Hv * (DV / CW)), dim3(NT), args, lds, stream);
 }
 
 // The fusions are compile-time variants, so the plain kernel carries none of
@@ -416,6 +560,18 @@ hipError_t launch_rec(const RecArgs& a, hipStream_t stream) {
 // read/write limit.)
 hipError_t launch_recurrent(const RecArgs& a, int in_dtype, int d, hipStream_t stream) {
     if (d == 128) {
+        // verify blocks without the epilogue on the narrow 1024-thread layout (the same sums as
+        // the 512-thread decode layout; shorter per-token chains: B=128, T=4 245 -> 232 us in a
+        // 4-row variant), decode and the fused verify on 512 threads (1024 measured 62 us
+        // against 48.6 for decode)
+        if (a.T > 1 && a.fu.z == nullptr) {
+            const bool pro = a.fu.A_log != nullptr;
+            if (in_dtype == 1)
+                return pro ? launch_rec_t<bf16_t, 128, 128, 1024, 128, true, false, true, false, true>(a, stream)
+                           : launch_rec_t<bf16_t, 128, 128, 1024, 128, true, false, false, false, true>(a, stream);
+            return pro ? launch_rec_t<float, 128, 128, 1024, 128, true, false, true, false, true>(a, stream)
+                       : launch_rec_t<float, 128, 128, 1024, 128, true, false, false, false, true>(a, stream);
+        }
         return in_dtype == 1 ? launch_rec<bf16_t, 128, 128, 512, 128, true, false>(a, stream)
                              : launch_rec<float, 128, 128, 512, 128, true, false>(a, stream);
     }
