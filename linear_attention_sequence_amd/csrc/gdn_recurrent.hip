@@ -561,9 +561,9 @@ hipError_t launch_rec(const RecArgs& a, hipStream_t stream) {
 hipError_t launch_recurrent(const RecArgs& a, int in_dtype, int d, hipStream_t stream) {
     if (d == 128) {
         // verify blocks without the epilogue on the narrow 1024-thread layout (the same sums as
-        // the 512-thread decode layout; shorter per-token chains: B=128, T=4 245 -> 232 us in a
-        // 4-row variant), decode and the fused verify on 512 threads (1024 measured 62 us
-        // against 48.6 for decode)
+        // the 512-thread decode layout, half the columns per thread: B=128, T=4 247 -> 238 us),
+        // decode and the fused verify on 512 threads (a 1024-thread decode measured 62 us
+        // against 48.6)
         if (a.T > 1 && a.fu.z == nullptr) {
             const bool pro = a.fu.A_log != nullptr;
             if (in_dtype == 1)
