@@ -298,8 +298,10 @@ __device__ __forceinline__ void load_tile_narrow(const RecArgs& a, const Unit& u
     }
 }
 
-// recur_tail on the narrow layout (no epilogue).
-template <typename Tin, int DK, int DV, int NT, int CW, bool NT_STORE>
+// recur_tail on the narrow layout. With the epilogue, each row's sum of squares is
+// formed in the 512-thread layout's pattern (lane j < 32 holds columns 4j .. 4j + 3 as
+// ((x^2 + y^2) + z^2) + w^2, the other lanes zero) before the same wave sum.
+template <typename Tin, int DK, int DV, int NT, int CW, bool NT_STORE, bool EPI>
 __device__ __forceinline__ void recur_tail_narrow(const RecArgs& a, const Unit& u, const RecLds& L, int T,
                                                   float2 (&s)[NarrowGeom<DK, CW, NT>::RPT]) {
     using G = NarrowGeom<DK, CW, NT>;
@@ -379,7 +381,16 @@ __device__ __forceinline__ void recur_tail_narrow(const RecArgs& a, const Unit& 
         }
         if (wave == 0) {   // the output row: row group 0 is wave 0, two columns per lane
             const float2 PQ = total(redq);
-            const float2 ov = make_float2(__fmaf_rn(d.x, kqh, al * (PQ.x * qs)), __fmaf_rn(d.y, kqh, al * (PQ.y * qs)));
+            float2 ov = make_float2(__fmaf_rn(d.x, kqh, al * (PQ.x * qs)), __fmaf_rn(d.y, kqh, al * (PQ.y * qs)));
+            if constexpr (EPI) {
+                const float z0 = __shfl_down(ov.x, 1, kWave), z1 = __shfl_down(ov.y, 1, kWave);   // the odd lane's columns
+                const float sq = ((ov.x * ov.x + ov.y * ov.y) + z0 * z0) + z1 * z1;                 // valid in even lanes
+                const float sj = __shfl(sq, 2 * (lane & 31), kWave);
+                const float ss = wave_sum_uniform(lane < 32 ? sj : 0.f);
+                const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / DV) + a.fu.norm_eps);
+                const float2 gz = *reinterpret_cast<const float2*>(L.s_gz + t * CW + 2 * cg);
+                ov = make_float2((ov.x * inv) * gz.x, (ov.y * inv) * gz.y);
+            }
             const size_t orow = ((static_cast<size_t>(u.b) * T + t) * a.Hv + u.h) * DV + u.j0;
             *reinterpret_cast<float2*>(a.o + orow + 2 * cg) = ov;
         }
@@ -396,7 +407,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NARROW ? 8 :
 void recurrent_kernel(RecArgs a) {   // narrow: 64 registers, two workgroups per CU
     using G = RecGeom<DK, DV, NT, CW>;
     using NG = std::conditional_t<NARROW, NarrowGeom<DK, CW, NT>, NoGeom>;
-    static_assert(!NARROW || (!EPI && DK == 128 && CW == DV), "the narrow layout: dk = dv = 128, no epilogue");
+    static_assert(!NARROW || (DK == 128 && CW == DV), "the narrow layout: dk = dv = 128");
     extern __shared__ float lds[];
     const int T = a.T;
     const RecLds L = rec_lds<DK, CW, G::NW>(lds, T);
@@ -474,7 +485,7 @@ void recurrent_kernel(RecArgs a) {   // narrow: 64 registers, two workgroups per
         L.s_beta[tg] = bv;
     }
     __syncthreads();
-    if constexpr (NARROW) recur_tail_narrow<Tin, DK, DV, NT, CW, NT_STORE>(a, u, L, T, s2);
+    if constexpr (NARROW) recur_tail_narrow<Tin, DK, DV, NT, CW, NT_STORE, EPI>(a, u, L, T, s2);
     else recur_tail<Tin, DK, DV, NT, CW, NT_STORE, PRO, EPI>(a, u, L, T, s);
 }
 
@@ -538,6 +549,17 @@ hipError_t launch_rec_t(const RecArgs& a, hipStream_t stream) {
         dim3(a.B * a.Hv * (DV / CW)), dim3(NT), args, lds, stream);
 }
 
+// Verify blocks at d = 128 on the narrow layout, with or without either fusion.
+template <typename Tin>
+hipError_t launch_rec_narrow(const RecArgs& a, hipStream_t stream) {
+    const bool pro = a.fu.A_log != nullptr, epi = a.fu.z != nullptr;
+    if (pro)
+        return epi ? launch_rec_t<Tin, 128, 128, 1024, 128, true, false, true, true, true>(a, stream)
+                   : launch_rec_t<Tin, 128, 128, 1024, 128, true, false, true, false, true>(a, stream);
+    return epi ? launch_rec_t<Tin, 128, 128, 1024, 128, true, false, false, true, true>(a, stream)
+               : launch_rec_t<Tin, 128, 128, 1024, 128, true, false, false, false, true>(a, stream);
+}
+
 // The fusions are compile-time variants, so the plain kernel carries none of
 // their registers (its occupancy decides how many state bytes are in flight).
 template <typename Tin, int DK, int DV, int NT, int CW, bool NT_STORE, bool NT_LOAD>
@@ -560,18 +582,11 @@ hipError_t launch_rec(const RecArgs& a, hipStream_t stream) {
 // read/write limit.)
 hipError_t launch_recurrent(const RecArgs& a, int in_dtype, int d, hipStream_t stream) {
     if (d == 128) {
-        // verify blocks without the epilogue on the narrow 1024-thread layout (the same sums as
-        // the 512-thread decode layout, half the columns per thread: B=128, T=4 247 -> 238 us),
-        // decode and the fused verify on 512 threads (a 1024-thread decode measured 62 us
-        // against 48.6)
-        if (a.T > 1 && a.fu.z == nullptr) {
-            const bool pro = a.fu.A_log != nullptr;
-            if (in_dtype == 1)
-                return pro ? launch_rec_t<bf16_t, 128, 128, 1024, 128, true, false, true, false, true>(a, stream)
-                           : launch_rec_t<bf16_t, 128, 128, 1024, 128, true, false, false, false, true>(a, stream);
-            return pro ? launch_rec_t<float, 128, 128, 1024, 128, true, false, true, false, true>(a, stream)
-                       : launch_rec_t<float, 128, 128, 1024, 128, true, false, false, false, true>(a, stream);
-        }
+        // verify blocks on the narrow 1024-thread layout (the same sums as the 512-thread
+        // decode layout, half the columns per thread: B=128, T=4 247 -> 238 us), decode on 512
+        // threads (a 1024-thread decode measured 62 us against 48.6)
+        if (a.T > 1)
+            return in_dtype == 1 ? launch_rec_narrow<bf16_t>(a, stream) : launch_rec_narrow<float>(a, stream);
         return in_dtype == 1 ? launch_rec<bf16_t, 128, 128, 512, 128, true, false>(a, stream)
                              : launch_rec<float, 128, 128, 512, 128, true, false>(a, stream);
     }
