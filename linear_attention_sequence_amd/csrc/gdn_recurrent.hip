@@ -543,10 +543,16 @@ hipError_t launch_rec_t(const RecArgs& a, hipStream_t stream) {
     // the fused gated RMSNorm needs the whole dv row of a head in one workgroup
     static_assert(CW == DV, "column slices would split the RMSNorm row");
     const size_t lds = recurrent_lds_bytes<DK, CW, NT, EPI>(a.T);
+    const void* k = reinterpret_cast<const void*>(&recurrent_kernel<Tin, DK, DV, NT, CW, NT_STORE, NT_LOAD, PRO, EPI, NARROW>);
+    // dynamic LDS above 64 KB (1024 threads with the epilogue at T = 16: 66 KB) must be
+    // allowed per kernel before its first launch; the largest block (T = 16) sets the bound
+    constexpr int kMaxBlock = 16;
+    static const hipError_t allowed =
+        hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(recurrent_lds_bytes<DK, CW, NT, EPI>(kMaxBlock)));
+    if (allowed != hipSuccess) return allowed;
     void* args[] = {const_cast<RecArgs*>(&a)};
-    return hipLaunchKernel(
-        reinterpret_cast<const void*>(&recurrent_kernel<Tin, DK, DV, NT, CW, NT_STORE, NT_LOAD, PRO, EPI, NARROW>),
-        dim3(a.B * a.Hv * (DV / CW)), dim3(NT), args, lds, stream);
+    return hipLaunchKernel(k, dim3(a.B * a.Hv * (DV / CW)), dim3(NT), args, lds, stream);
 }
 
 // Verify blocks at d = 128 on the narrow layout, with or without either fusion.

@@ -139,7 +139,8 @@ def test_decode_fused(shape, dtype, B, steps, pro, epi):
 
 
 @pytest.mark.parametrize("pro,epi", FUSIONS)
-@pytest.mark.parametrize("shape,dtype,B,T", [(gi.TINY, "f32", 2, 5), (SMALL128, "bf16", 4, 4)])
+@pytest.mark.parametrize("shape,dtype,B,T", [(gi.TINY, "f32", 2, 5), (SMALL128, "bf16", 4, 4),
+                                             (SMALL128, "bf16", 2, 16)])   # the widest block: 64 KB+ of LDS
 def test_verify_fused(shape, dtype, B, T, pro, epi):
     _say(f"verify_ex {shape} {dtype} B={B} T={T} prologue={pro} epilogue={epi}")
     inp = fused_inputs(shape, B, T, 52, dtype, pro, epi)
