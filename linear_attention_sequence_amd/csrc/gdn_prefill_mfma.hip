@@ -371,34 +371,9 @@ __global__ __launch_bounds__(256) void front_kernel(PrefillArgs a, Ws ws) {
     for (int j = 0; j < TT / 2; ++j) buf[(th * (TT / 2) + j) * (D + 1) + cpos] = y[j];
     }
     __syncthreads();
-    // per-token sum of squares: thread (token tid % TT, channel part tid / TT)
-    // reads its part column-wise (lanes run along tokens: conflict-free)
-    constexpr int NPART = 256 / TT, PW = D / NPART;
-    __shared__ float s_part[NPART][TT];
-    __shared__ float s_scale[TT];
-    {
-        const int t = tid % TT, qq = tid / TT;
-        float ss = 0.f;
-#pragma unroll 8
-        for (int cc = 0; cc < PW; ++cc) {
-            const float v = buf[t * (D + 1) + qq * PW + cc];
-            ss = __fmaf_rn(v, v, ss);
-        }
-        s_part[qq][t] = ss;
-    }
-    __syncthreads();
-    if (tid < TT) {
-        float r = 1.f;
-        float ss = 0.f;
-#pragma unroll
-        for (int q = 0; q < NPART; ++q) ss += s_part[q][tid];
-        if (a.use_l2) r = 1.0f / sqrtf(ss + a.eps);
-        if (is_q) r *= 1.0f / sqrtf(static_cast<float>(D));
-        s_scale[tid] = r;
-    }
-    __syncthreads();
     // 16 lanes per token, 8 channels (16 bytes) per lane: a wave stores 4 tokens
-    // per instruction, 16 tokens in all
+    // per instruction, 16 tokens in all. A token's sum of squares is formed from its
+    // 16 lanes' partials by a DPP tree that leaves the same total in every lane.
     {
         const int tq = lane >> 4, j = lane & 15;
         _Float16* base = is_q ? ws.qh + u * D : ws.kh + (u - a.Hk) * D;
@@ -406,10 +381,20 @@ __global__ __launch_bounds__(256) void front_kernel(PrefillArgs a, Ws ws) {
 #pragma unroll
         for (int i = 0; i < TT / 16; ++i) {
             const int t = wave * (TT / 4) + 4 * i + tq;
-            const float r = s_scale[t];
+            float x[8];
+            float ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                x[e] = buf[t * (D + 1) + 8 * j + e];
+                ss = __fmaf_rn(x[e], x[e], ss);
+            }
+            ss = row16_sum(ss);
+            float r = 1.f;
+            if (a.use_l2) r = 1.0f / sqrtf(ss + a.eps);
+            if (is_q) r *= 1.0f / sqrtf(static_cast<float>(D));
             f16x8 v;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = static_cast<_Float16>(buf[t * (D + 1) + 8 * j + e] * r);
+            for (int e = 0; e < 8; ++e) v[e] = static_cast<_Float16>(x[e] * r);
             const size_t tok = static_cast<size_t>(row) * a.L + p0 + t;
             if (vec || s_n[t] >= 0) *reinterpret_cast<f16x8*>(base + tok * hs * D + 8 * j) = v;
         }
@@ -938,6 +923,23 @@ __device__ __forceinline__ void issue_stage(const PrefillArgs& a, const Ws& ws, 
 using plan::kSortMax;
 constexpr int kZeroTile = -(1 << 20);   // state-map tile exponent marking a tile that is exactly zero
 
+// Carried power-of-two scales: values held as x 2^-e with max|x 2^-e| kept inside
+// [2^kWinLo, 2^15), a window of fp16's range with room to spare at the top (the fp16
+// operands formed from them cannot overflow) and far enough above fp16's smallest
+// normal at the bottom that the values keep fp16's full relative precision.
+constexpr int kWinLo = 6;
+// Wave-uniform: some lane's largest magnitude reached 2^15, or no lane's reached 2^kWinLo.
+__device__ __forceinline__ bool outside_window(float lane_max) {
+    return __builtin_amdgcn_ballot_w64(lane_max >= 0x1p15f) != 0 ||
+           __builtin_amdgcn_ballot_w64(lane_max >= static_cast<float>(1 << kWinLo)) == 0;
+}
+// The exponent that puts the wave's largest magnitude (now at scale 2^-e) into
+// [2^14, 2^15), kept >= ref - 100 so that the products that move values between this
+// scale and the one of exponent ref stay inside fp32's range.
+__device__ __forceinline__ int rescaled_exponent(int e, float lane_max, int ref) {
+    return max(e + pow2_exponent(wave_max_nonneg(lane_max)), ref - 100);
+}
+
 // Sequence of rank r when the N packed sequences are ordered by decreasing length
 // (ties by index). Every thread ranks up to N / blockDim of them against all N.
 __device__ int sequence_of_rank(const PrefillArgs& a, int r) {
@@ -1236,6 +1238,20 @@ __global__ __launch_bounds__((NW + (LW ? NL : 0)) * 64) void carry_kernel(Prefil
             if (t < pnt) __builtin_nontemporal_store(y, reinterpret_cast<f32x4v*>(pob + t * ts + col0 + 4 * g));
         }
     };
+    // The state is carried as S~ = S 2^-eS and each chunk's Delta formed as Delta 2^-eD,
+    // with eS and eD kept from chunk to chunk while the largest magnitude stays inside
+    // [2^kWinLo, 2^15) (fp16's range with room to spare; a wave vote, no cross-lane
+    // maximum) and reset only when it leaves that window. Powers of two scale exactly,
+    // so these are the products of per-chunk scaling, without a multiply per element
+    // and a reduction per chunk on the state's path.
+    int eS = pow2_exponent(wave_max_nonneg(smax)), eD = 0;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) S[mt][nt][e] = ldexpf(S[mt][nt][e], -eS);
+    smax = ldexpf(smax, -eS);
     // The next chunk's stage is issued in three parts spread over this chunk's
     // phases (each part before the phase that would otherwise wait on the memory
     // pipeline), so that the vector-memory issue queue never backs up the MFMA work.
@@ -1267,9 +1283,18 @@ __global__ __launch_bounds__((NW + (LW ? NL : 0)) * 64) void carry_kernel(Prefil
         const float* cfr = cf + C;                                            // exp(Gam_last - Gam_t)
         const float egl = cf[2 * C], uscale = cf[2 * C + 1];
 
-        // S as B operands (k = rows of S), scaled into fp16 range
-        const int eS = pow2_exponent(wave_max_nonneg(smax));
-        const float sS = ldexpf(1.f, -eS), iS = ldexpf(1.f, eS);
+        // S~ as B operands (k = rows of S); back into the window first if it left it
+        if (outside_window(smax)) {
+            const int e2 = rescaled_exponent(eS, smax, eD);
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) S[mt][nt][e] = ldexpf(S[mt][nt][e], eS - e2);
+            eS = e2;
+        }
+        const float iS = ldexpf(1.f, eS);
         f16x8 sb[NTW][4];
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt)
@@ -1277,13 +1302,16 @@ __global__ __launch_bounds__((NW + (LW ? NL : 0)) * 64) void carry_kernel(Prefil
             for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    sb[nt][ks][e] = static_cast<_Float16>(S[2 * ks][nt][e] * sS);
-                    sb[nt][ks][4 + e] = static_cast<_Float16>(S[2 * ks + 1][nt][e] * sS);
+                    sb[nt][ks][e] = static_cast<_Float16>(S[2 * ks][nt][e]);
+                    sb[nt][ks][4 + e] = static_cast<_Float16>(S[2 * ks + 1][nt][e]);
                 }
 
-        // Delta = U - W S (rows past the end of the sequence are zero)
+        // Delta 2^-eD = U uscale 2^-eD - (W S~) 2^(eS - eD). Rows past the end of the
+        // sequence come out zero: W and U are zero there (zero keys, values and beta).
         float dl[4][NTW][4];
         float dmax = 0.f;
+        const float uD = ldexpf(uscale, -eD);
+        const int dS = eS - eD;
         if constexpr (BATCH) {
             f16x8 aw[4][4];
             _Float16 uh[4][NTW][4];
@@ -1313,9 +1341,8 @@ __global__ __launch_bounds__((NW + (LW ? NL : 0)) * 64) void carry_kernel(Prefil
                 for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const int t = 16 * mt + 4 * g + e;
                         const float u = static_cast<float>(uh[mt][nt][e]);
-                        const float d = (t < ntc) ? __fmaf_rn(u, uscale, -iS * acc[nt][e]) : 0.f;
+                        const float d = __fmaf_rn(u, uD, -ldexpf(acc[nt][e], dS));
                         dl[mt][nt][e] = d;
                         dmax = fmaxf(dmax, fabsf(d));
                     }
@@ -1338,14 +1365,25 @@ __global__ __launch_bounds__((NW + (LW ? NL : 0)) * 64) void carry_kernel(Prefil
                     for (int e = 0; e < 4; ++e) {
                         const int t = 16 * mt + 4 * g + e;
                         const float u = static_cast<float>(lds_u1(Ul, lcol0 + 16 * nt + r16, t));
-                        const float d = (t < ntc) ? __fmaf_rn(u, uscale, -iS * acc[nt][e]) : 0.f;
+                        const float d = __fmaf_rn(u, uD, -ldexpf(acc[nt][e], dS));
                         dl[mt][nt][e] = d;
                         dmax = fmaxf(dmax, fabsf(d));
                     }
             }
         }
-        const int eD = pow2_exponent(wave_max_nonneg(dmax));
-        const float sD = ldexpf(1.f, -eD), iD = ldexpf(1.f, eD);
+        if (outside_window(dmax)) {   // Delta back into the window
+            int eu;
+            frexpf(uscale, &eu);
+            const int e2 = rescaled_exponent(eD, dmax, max(eS, eu));
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) dl[mt][nt][e] = ldexpf(dl[mt][nt][e], eD - e2);
+            eD = e2;
+        }
+        const float iD = ldexpf(1.f, eD);
         f16x8 db[NTW][2], dp[NTW][2];   // Delta and diag(exp(Gam_last - Gam)) Delta as B operands (k = token)
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt)
@@ -1355,7 +1393,7 @@ __global__ __launch_bounds__((NW + (LW ? NL : 0)) * 64) void carry_kernel(Prefil
                 for (int e = 0; e < 8; ++e) {
                     const int mt = 2 * ks + (e >> 2), ee = e & 3;
                     const int t = 16 * mt + 4 * g + ee;
-                    const float v = dl[mt][nt][ee] * sD;
+                    const float v = dl[mt][nt][ee];
                     db[nt][ks][e] = static_cast<_Float16>(v);
                     dp[nt][ks][e] = static_cast<_Float16>(v * cfr[t]);
                 }
@@ -1456,7 +1494,8 @@ __global__ __launch_bounds__((NW + (LW ? NL : 0)) * 64) void carry_kernel(Prefil
         if (!LW && more)
             issue_stage<CPW, NW, ST_KT>(a, ws, id + 1, tok0 + C, ntn, h, hk, ucol0, sb_, wave, lane);
 
-        // S = exp(Gam_last) S + K^T diag(exp(Gam_last - Gam)) Delta; max|S| for the next chunk
+        // S~ = exp(Gam_last) S~ + 2^(eD - eS) K^T diag(exp(Gam_last - Gam)) Delta 2^-eD;
+        // max|S~| of this lane for the next chunk's window check
         smax = 0.f;
         f16x8 ak[8][2];
         if constexpr (BATCH) {
@@ -1481,11 +1520,19 @@ __global__ __launch_bounds__((NW + (LW ? NL : 0)) * 64) void carry_kernel(Prefil
             for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    S[mt][nt][e] = __fmaf_rn(egl, S[mt][nt][e], iD * acc[nt][e]);
+                    S[mt][nt][e] = __fmaf_rn(egl, S[mt][nt][e], ldexpf(acc[nt][e], eD - eS));
                     smax = fmaxf(smax, fabsf(S[mt][nt][e]));
                 }
         }
     }
+    // back to S itself
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) S[mt][nt][e] = ldexpf(S[mt][nt][e], eS);
+    smax = ldexpf(smax, eS);
     if constexpr (NORM) {
         if (outs && ce > cb) {
             __syncthreads();                                 // every wave's sums of the last chunk

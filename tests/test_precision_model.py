@@ -52,9 +52,28 @@ def _scaled(rnd):
     return f
 
 
-def chunked_rounded(q, k, v, g, b, S0, rnd, C=64):
+def _exp_for(x, top):
+    """Exponent e with max|x 2^-e| in [2^(top - 1), 2^top) (0 for an all-zero x)."""
+    m = float(np.max(np.abs(x))) if np.size(x) else 0.0
+    return math.frexp(m)[1] - top if m > 0.0 else 0
+
+
+def chunked_rounded(q, k, v, g, b, S0, rnd, C=64, state_top=None):
     """o [L, dv] and the final state of one V head, chunk by chunk, every product operand
-    passed through rnd (q, k unit-norm and T, P, W bounded: the scale is a no-op for them)."""
+    passed through rnd (q, k unit-norm and T, P, W bounded: the scale is a no-op for them).
+
+    With state_top set (and rnd the plain narrow rounding), the state and Delta operands
+    are rounded at the scale that puts their largest magnitude in [2^(state_top - 1),
+    2^state_top) instead, both Delta operands (Delta and its decay-weighted copy) at
+    Delta's scale: the carry kernel keeps these scales anywhere in a window of fp16's
+    range rather than at its top."""
+    if state_top is None:
+        rs = rd = rnd
+    else:
+        def rs(x):
+            e = _exp_for(x, state_top)
+            return rnd(x * 2.0 ** -e) * 2.0 ** e
+
     L = q.shape[0]
     S = S0.copy()
     O = np.zeros((L, v.shape[1]))
@@ -72,10 +91,16 @@ def chunked_rounded(q, k, v, g, b, S0, rnd, C=64):
         W = _f32(rnd(T) @ rnd(np.exp(gam)[:, None] * Bt[:, None] * K))
         U = _f32(rnd(T) @ rnd(Bt[:, None] * V))
         P = np.exp(np.where(incl, diff, -np.inf)) * (Qr @ Kr.T)
-        Sr = rnd(S)
+        Sr = rs(S)
         Delta = _f32(rnd(U) - rnd(W) @ Sr)
-        O[sl] = _f32(np.exp(gam)[:, None] * (Qr @ Sr) + rnd(P) @ rnd(Delta))
-        S = _f32(math.exp(gam[-1]) * S + Kr.T @ rnd(np.exp(gam[-1] - gam)[:, None] * Delta))
+        wD = np.exp(gam[-1] - gam)[:, None] * Delta
+        if state_top is None:
+            Dr, wDr = rnd(Delta), rnd(wD)
+        else:
+            e = _exp_for(Delta, state_top)
+            Dr, wDr = rnd(Delta * 2.0 ** -e) * 2.0 ** e, rnd(wD * 2.0 ** -e) * 2.0 ** e
+        O[sl] = _f32(np.exp(gam)[:, None] * (Qr @ Sr) + rnd(P) @ Dr)
+        S = _f32(math.exp(gam[-1]) * S + Kr.T @ wDr)
     return O, S
 
 
@@ -131,3 +156,17 @@ def test_bf16_operands_miss_the_budget(cases):
         O, S = chunked_rounded(q, k, v, g, b, S0, _scaled(_bf16))
         worst = max(worst, _err(O, o_ref), _err(S, S_ref))
     assert worst > BUDGET, worst
+
+
+def test_fp16_operands_anywhere_in_the_carried_window(cases):
+    """The carry keeps the state's and Delta's power-of-two scales from chunk to chunk while
+    their largest magnitude stays in [2^6, 2^15): with it at the bottom of that window the
+    fp16 operands give the same error as with it at the top (fp16's relative precision
+    does not depend on the scale until values fall below its smallest normal, 2^-14)."""
+    for name, (q, k, v, g, b, S0, o_ref, S_ref) in cases.items():
+        Ot, St = chunked_rounded(q, k, v, g, b, S0, _fp16, state_top=15)
+        Ol, Sl = chunked_rounded(q, k, v, g, b, S0, _fp16, state_top=7)
+        et, el = (_err(Ot, o_ref), _err(St, S_ref)), (_err(Ol, o_ref), _err(Sl, S_ref))
+        assert max(el) <= BUDGET / 2, (name, el)
+        for x, y in zip(el, et):
+            assert abs(x - y) <= 0.01 * y, (name, el, et)
