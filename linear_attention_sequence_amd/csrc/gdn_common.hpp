@@ -43,17 +43,6 @@ __device__ __forceinline__ float wave_sum_uniform(float x) {
     return (r0 + r1) + (r2 + r3);
 }
 
-// Sum over each row of 16 lanes; every lane of the row receives the same total
-// (pairs within quads, then the quads of each half row, then the two half rows:
-// every step adds two equal partial sums in either order, which gives the same bits).
-__device__ __forceinline__ float row16_sum(float x) {
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));  // row_half_mirror
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));  // row_mirror
-    return x;
-}
-
 // Depthwise causal conv of one channel at one position followed by SiLU:
 // silu(sum_j w[j] * win[j]) where win[K-1] is the current token. The sum is
 // taken in tap order with explicit fused multiply-adds.

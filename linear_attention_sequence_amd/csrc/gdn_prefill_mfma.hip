@@ -153,6 +153,17 @@ __device__ __forceinline__ float fast_silu(float x) {
     return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));   // v_exp_f32, v_rcp_f32
 }
 
+// Sum over each row of 16 lanes; every lane of the row receives the same total
+// (pairs within quads, then the quads of each half row, then the two half rows:
+// every step adds two equal partial sums in either order, which gives the same bits).
+__device__ __forceinline__ float row16_sum(float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));  // row_half_mirror
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));  // row_mirror
+    return x;
+}
+
 // ---- steps 1-4 ------------------------------------------------------------------
 template <typename Tin>
 __global__ __launch_bounds__(256) void front_kernel(PrefillArgs a, Ws ws) {
