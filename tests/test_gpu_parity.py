@@ -151,6 +151,43 @@ def test_prefill_long_memory(L):
     assert rel_err(got["S"], ref["S"]) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("packed", [False, True], ids=["segmented", "one_chain"])
+def test_prefill_magnitude_swings(packed):
+    """The carry keeps the state's and Delta's power-of-two scales from chunk to chunk and
+    moves them only when a value leaves a window of fp16's range. Here the values jump by
+    up to 2^40 from one chunk to the next and the decay switches between strong and
+    weak, so both scales move in both directions many times; every chunk's outputs must
+    still meet the budget against that chunk's own largest output, i.e. keep their relative
+    precision at every magnitude. Segmented (pass 1 whole-head, pass 2 half-head
+    workgroups) and as one packed sequence (a single chain)."""
+    shape, dtype = SMALL128, "bf16"
+    L, C = 1300, 64
+    _say(f"prefill magnitude swings packed={packed}")
+    inp = layer_inputs(shape, 1, L, 23, dtype, s0_std=100.0, conv_std=1.0)
+    shifts = [0, 20, -20, 40, -40, 0, 12, -12, 30, -30, 5, -5, 0, 24, -24, 0, 40, 0, -40, 8, 0]
+    gates = [1.0, 0.01, 10.0, 0.01, 1.0, 10.0, 0.01, 0.01, 1.0, 10.0, 0.01]
+    x = inp["qkv"].astype(np.float64)
+    g = inp["gate"].astype(np.float64)
+    v0 = 2 * shape.Hk * shape.dk                      # first value channel
+    for c in range(0, (L + C - 1) // C):
+        sl = slice(c * C, min((c + 1) * C, L))
+        x[:, v0:, sl] *= 2.0 ** shifts[c % len(shifts)]
+        g[:, sl, :] *= gates[c % len(gates)]
+    inp["qkv"] = gi.round_to(x, dtype)                # powers of two: exact in bf16
+    inp["gate"] = gi.round_to(g, dtype)
+    cu = [0, L] if packed else None
+    got = run_prefill(shape, dtype, inp, cu=cu)
+    ref = oracle.gdn_forward(oparams(shape), inp["qkv"], inp["gate"], inp["beta"], inp["w"],
+                             inp["conv0"], inp["S0"], cu_seqlens=None if cu is None else np.asarray(cu, np.int32))
+    o = got["o"].double().cpu().numpy()
+    worst = 0.0
+    for c in range(0, (L + C - 1) // C):
+        sl = slice(c * C, min((c + 1) * C, L))
+        worst = max(worst, rel_err(o[:, sl], ref["o"][:, sl]))
+    assert worst <= TOL[dtype], worst
+    assert rel_err(got["S"], ref["S"]) <= TOL[dtype]
+
+
 # ---------------------------------------------------------------------------
 # decode and verify, small
 # ---------------------------------------------------------------------------
