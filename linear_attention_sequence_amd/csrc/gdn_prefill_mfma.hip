@@ -7,9 +7,10 @@
 // v_mfma_f32_16x16x32_f16 (fp16 operands, fp32 accumulation); the state S,
 // the triangular solve and every accumulation stay fp32. Operands whose scale
 // is set by the data (the state S, the values v, U and the deltas) are brought
-// into fp16's range with a power-of-two scale chosen per wave or per chunk
-// (exact to apply and to undo); q and k are unit-norm and P, W are bounded by
-// them.
+// into fp16's range with a power-of-two scale (exact to apply and to undo):
+// chosen per chunk for v and U, and for S and the deltas per wave, kept from
+// chunk to chunk while their maxima stay inside a window of fp16's range; q and
+// k are unit-norm and P, W are bounded by them.
 //
 //   front_kernel   steps 1-4 for the q and k channels on a (32-token,
 //                  128-channel) tile: coalesced channel-major loads, conv + SiLU,
