@@ -1254,8 +1254,8 @@ __global__ __launch_bounds__((NW + (LW ? NL : 0)) * 64) void carry_kernel(Prefil
     // with eS and eD kept from chunk to chunk while the largest magnitude stays inside
     // [2^kWinLo, 2^15) (fp16's range with room to spare; a wave vote, no cross-lane
     // maximum) and reset only when it leaves that window. Powers of two scale exactly,
-    // so these are the products of per-chunk scaling, without a multiply per element
-    // and a reduction per chunk on the state's path.
+    // so the results are those of scaling every chunk afresh, without its multiply per
+    // element and its cross-lane reduction per chunk on the state's path.
     int eS = pow2_exponent(wave_max_nonneg(smax)), eD = 0;
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
