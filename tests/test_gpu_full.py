@@ -90,6 +90,24 @@ def test_prefill_L4096():
     assert np.array_equal(cout.float().cpu().numpy(), ref["conv_out"])
 
 
+def test_prefill_L16384():
+    """Four times the 4096-token prompt: the segmented carry with about 50 chunks per
+    segment and the workspace at that size; every head against the oracle."""
+    seed, L = gi.WORKLOADS[2].seed + 1, 4 * gi.PREFILL_L
+    print(f"prefill full L={L}", flush=True)
+    x = gi.qkv(SH, 1, L, seed, "bf16")
+    g = gi.gate(SH, 1, L, seed, "bf16")
+    b = gi.beta(SH, 1, L, seed, "bf16")
+    w = gi.conv_weight(SH, seed, "bf16")
+    o, S, cout = _prefill(x, g, b, w, 1)
+    ref = oracle.gdn_forward(oparams(SH), x, g, b, w, np.zeros((1, SH.D, 3)), np.zeros((1, SH.Hv, 128, 128)))
+    assert not torch.isnan(o).any()
+    for h in range(SH.Hv):
+        assert rel_err(o[0, :, h], ref["o"][0, :, h]) <= TOL["bf16"], h
+        assert rel_err(S[0, h], ref["S"][0, h]) <= TOL["bf16"], h
+    assert np.array_equal(cout.float().cpu().numpy(), ref["conv_out"])
+
+
 def test_ragged_prefill_8_sequences():
     seed = gi.WORKLOADS[3].seed
     lens = gi.seq_lens(gi.RAGGED_N, gi.RAGGED_LO, gi.RAGGED_HI, seed)

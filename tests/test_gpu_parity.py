@@ -188,6 +188,31 @@ def test_prefill_magnitude_swings(packed):
     assert rel_err(got["S"], ref["S"]) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("packed", [False, True], ids=["segmented", "one_chain"])
+@pytest.mark.parametrize("case", ["no_decay_full_write", "total_forgetting"])
+def test_prefill_degenerate_gates(case, packed):
+    """The gate's two extremes: g = 0 with beta = 1 (no decay, every write at full strength:
+    the state maps never fade and each key's value is recalled exactly after its write),
+    and g = -60 per token (the state forgets everything between two tokens: every decay
+    factor across a token underflows, the state maps are exactly zero and each output
+    depends on its own token only)."""
+    shape, dtype, L = SMALL128, "bf16", 1300
+    _say(f"prefill degenerate gates {case} packed={packed}")
+    inp = layer_inputs(shape, 1, L, 24, dtype, s0_std=0.1, conv_std=1.0)
+    if case == "no_decay_full_write":
+        inp["gate"] = np.zeros_like(inp["gate"])
+        inp["beta"] = gi.round_to(np.ones(inp["beta"].shape), dtype)
+    else:
+        inp["gate"] = gi.round_to(np.full(inp["gate"].shape, -60.0), dtype)
+    cu = [0, L] if packed else None
+    got = run_prefill(shape, dtype, inp, cu=cu)
+    ref = oracle.gdn_forward(oparams(shape), inp["qkv"], inp["gate"], inp["beta"], inp["w"],
+                             inp["conv0"], inp["S0"], cu_seqlens=None if cu is None else np.asarray(cu, np.int32))
+    assert not torch.isnan(got["o"]).any()
+    assert rel_err(got["o"], ref["o"]) <= TOL[dtype]
+    assert rel_err(got["S"], ref["S"]) <= TOL[dtype]
+
+
 # ---------------------------------------------------------------------------
 # decode and verify, small
 # ---------------------------------------------------------------------------
