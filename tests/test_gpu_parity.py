@@ -247,6 +247,35 @@ def test_decode_small(shape, dtype, B, steps):
     assert np.array_equal(cs.float().cpu().numpy(), ref["conv_out"])
 
 
+@pytest.mark.parametrize("case", ["no_decay_full_write", "total_forgetting"])
+def test_decode_and_verify_degenerate_gates(case):
+    """The gate's extremes on the recurrent kernel: g = 0 with beta = 1, and g = -60 (the
+    carried state is wiped between tokens), as decode steps and as a verify block whose
+    snapshots are checked against the oracle's states after each token."""
+    shape, dtype, B, steps = SMALL128, "bf16", 3, 12
+    _say(f"decode/verify degenerate gates {case}")
+    inp = layer_inputs(shape, B, steps, 25, dtype, s0_std=0.5, conv_std=1.0)
+    if case == "no_decay_full_write":
+        inp["gate"] = np.zeros_like(inp["gate"])
+        inp["beta"] = gi.round_to(np.ones(inp["beta"].shape), dtype)
+    else:
+        inp["gate"] = gi.round_to(np.full(inp["gate"].shape, -60.0), dtype)
+    o, S, cs = _decode_steps(shape, dtype, inp, steps)
+    ref = oracle.gdn_forward(oparams(shape), inp["qkv"], inp["gate"], inp["beta"], inp["w"],
+                             inp["conv0"], inp["S0"])
+    assert rel_err(o, ref["o"]) <= TOL[dtype]
+    assert rel_err(S, ref["S"]) <= TOL[dtype]
+    T = 4
+    blk = {k: (v[:, :, :T] if k == "qkv" else v[:, :T]) if k in ("qkv", "gate", "beta") else v for k, v in inp.items()}
+    snap, ov = _verify(shape, dtype, blk, dev(inp["S0"]), dev(inp["conv0"], dtype), T)
+    torch.cuda.synchronize()
+    for t in range(T):
+        r = oracle.gdn_forward(oparams(shape), inp["qkv"][:, :, :t + 1], inp["gate"][:, :t + 1], inp["beta"][:, :t + 1],
+                               inp["w"], inp["conv0"], inp["S0"])
+        assert rel_err(snap[:, t], r["S"]) <= TOL[dtype], t
+        assert rel_err(ov[:, t], r["o"][:, t]) <= TOL[dtype], t
+
+
 def _verify(shape, dtype, inp, S_in, cs, T):
     p = params(shape, dtype)
     B = inp["qkv"].shape[0]
