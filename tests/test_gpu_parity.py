@@ -361,8 +361,11 @@ def test_gqa_mapping_probe_exact():
 # ---------------------------------------------------------------------------
 # bit-exact GPU invariants
 # ---------------------------------------------------------------------------
-def test_verify_snapshots_equal_decode_steps_bitexact():
-    shape, dtype, B, T = SMALL128, "bf16", 5, 6
+@pytest.mark.parametrize("T", [1, 6, 16])
+def test_verify_snapshots_equal_decode_steps_bitexact(T):
+    """A verify block of width T (1: the decode layout; 6 and 16, the widest: the narrow
+    layout) gives the decode steps' outputs and states bit for bit."""
+    shape, dtype, B = SMALL128, "bf16", 5
     inp = layer_inputs(shape, B, T, 41, dtype, s0_std=0.1, conv_std=1.0)
     S0 = dev(inp["S0"])
     snap, o_v = _verify(shape, dtype, inp, S0, dev(inp["conv0"], dtype), T)
