@@ -221,3 +221,28 @@ def test_null_fusion_is_the_plain_call_bitexact():
     for other in outs[1:]:
         for a, b in zip(outs[0], other):
             assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("path", ["decode", "verify", "prefill"])
+def test_fusions_at_saturating_inputs(path):
+    """Raw gate/beta projections and gates z twenty times the usual spread (|x| up to about
+    80): softplus and the sigmoids saturate, beta is nearly 0 or 1, some tokens' decay
+    wipes the state and silu(z) is nearly z or 0. The prologue and epilogue must follow the
+    oracle there too (MFMA prefill at 1300 tokens: the segmented carry)."""
+    shape, dtype = SMALL128, "bf16"
+    B, L = {"decode": (3, 10), "verify": (4, 8), "prefill": (1, 1300)}[path]
+    _say(f"fusions at saturating inputs: {path}")
+    inp = fused_inputs(shape, B, L, 56, dtype, True, True)
+    for k in ("a", "b", "z"):
+        inp[k] = gi.round_to(20.0 * inp[k].astype(np.float64), dtype)
+    ref = reference(shape, inp)
+    if path == "decode":
+        o, S, _ = run_decode(shape, dtype, inp, L)
+    elif path == "verify":
+        o, snap = run_verify(shape, dtype, inp, L)
+        S = snap[:, -1]
+    else:
+        o, S, _ = run_prefill(shape, dtype, inp)
+    assert not torch.isnan(o).any()
+    assert rel_err(o, ref["o"]) <= TOL[dtype]
+    assert rel_err(S, ref["S"]) <= TOL[dtype]
