@@ -202,6 +202,13 @@ def pin_closed_forms():
     for t in range(7):
         assert _rel(snap[t], math.exp(Gam[t]) * S0) < 1e-14
         assert _rel(o[t], math.exp(Gam[t]) * (q[t] @ S0)) < 1e-13
+    # (5) total forgetting (exp(g) underflows to exactly 0): every token starts from the
+    # zero state whatever came before, so S_t = beta_t k_t v_t^T and o_t = beta_t (k_t.q_t) v_t
+    q, k, v, _, b, S0 = _rand_core(rng, 5, dk, dv)
+    o, S, snap = oracle.delta_rule(q, k, v, np.full(5, -1.0e4), b, S0, snapshots=True)
+    for t in range(5):
+        assert _rel(snap[t], b[t] * np.outer(k[t], v[t])) < 1e-14
+        assert _rel(o[t], b[t] * float(k[t] @ q[t]) * v[t]) < 1e-13
 
 
 def pin_lms_and_norm_bound():
