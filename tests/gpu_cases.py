@@ -58,14 +58,14 @@ def layer_inputs(shape: gi.Shape, B: int, L: int, seed: int, dtype: str, N=None,
     )
 
 
-def run_prefill(shape, dtype, inp, cu=None, qkv_offset=0):
+def run_prefill(shape, dtype, inp, cu=None, qkv_offset=0, o_fill=0.0):
     """qkv_offset > 0 places qkv that many elements into a larger buffer (so its address
-    is only element-aligned)."""
+    is only element-aligned); o starts filled with o_fill."""
     p = params(shape, dtype)
     B, D, L = inp["qkv"].shape
     N = inp["S0"].shape[0]
     S = dev(inp["S0"])
-    o = torch.zeros((B, L, shape.Hv, shape.dv), dtype=torch.float32, device="cuda")
+    o = torch.full((B, L, shape.Hv, shape.dv), o_fill, dtype=torch.float32, device="cuda")
     cout = torch.zeros_like(dev(inp["conv0"], dtype))
     ws = gdn.prefill_workspace(p, B, L, N)
     x = dev(inp["qkv"], dtype)

@@ -134,6 +134,65 @@ def test_prefill_ragged_many_sequences():
     assert np.array_equal(got["conv_out"].float().cpu().numpy(), ref["conv_out"])
 
 
+@pytest.mark.parametrize("shape,L,cu_given,cu_read", [
+    (SMALL128, 260, [-5, 70, 200, 300], [0, 70, 200, 260]),
+    (SMALL128, 230, [0, 70, 200, 150, 150], [0, 70, 200, 200, 200]),
+    (gi.QWEN, 1050, [0, 900, 1000, 950, 950], [0, 900, 1000, 1000, 1000]),
+], ids=["clamped_to_0_and_L", "decreasing_pairs", "decreasing_pairs_full_heads"])
+def test_prefill_cu_seqlens_clamped_with_canary(shape, L, cu_given, cu_read):
+    """cu_seqlens entries outside [0, L] are clamped and a decreasing pair is an empty
+    sequence: the call equals the oracle on the clamped table, the tokens no sequence
+    owns keep the NaN o was filled with, and an empty sequence keeps its state bit for
+    bit. The last case runs the full head shape, a 15-chunk chain per head split over
+    two workgroups."""
+    dtype = "bf16"
+    N = len(cu_given) - 1
+    _say(f"prefill cu_seqlens {cu_given} over L={L}, {shape}")
+    inp = layer_inputs(shape, 1, L, 23, dtype, N=N, s0_std=0.1, conv_std=1.0)
+    got = run_prefill(shape, dtype, inp, cu=np.asarray(cu_given, np.int32), o_fill=float("nan"))
+    n_in = cu_read[-1]
+    cut = dict(inp, qkv=inp["qkv"][:, :, :n_in], gate=inp["gate"][:, :n_in],
+               beta=inp["beta"][:, :n_in])
+    ref = oracle.gdn_forward(oparams(shape), cut["qkv"], cut["gate"], cut["beta"], cut["w"],
+                             cut["conv0"], cut["S0"], cu_seqlens=np.asarray(cu_read, np.int32))
+    assert bool(torch.isfinite(got["o"][:, :n_in]).all())
+    assert rel_err(got["o"][:, :n_in], ref["o"]) <= TOL[dtype]
+    assert bool(torch.isnan(got["o"][:, n_in:]).all())
+    assert rel_err(got["S"], ref["S"]) <= TOL[dtype]
+    S0 = torch.from_numpy(inp["S0"])
+    for n in range(N):
+        if cu_read[n + 1] == cu_read[n]:
+            assert torch.equal(got["S"][n].cpu(), S0[n]), f"empty sequence {n} changed its state"
+    assert np.array_equal(got["conv_out"].float().cpu().numpy(), ref["conv_out"])
+
+
+def test_prefill_packed_thousands_of_sequences():
+    """5000 packed sequences of 0-3 tokens with a 130-token one every 500: more than the
+    front kernel's cu_seqlens table in LDS holds (it then searches the table in memory)
+    and more than the carry ranks by length (it then takes them in order). Tokens past
+    the last sequence keep the NaN o was filled with; empty sequences keep their state
+    bit for bit."""
+    shape, dtype = gi.Shape(Hk=1, Hv=2, dk=128, dv=128, K=4), "bf16"
+    lens = gi.seq_lens(5000, 0, 3, 24)
+    lens[::500] = 130
+    cu = gi.cu_seqlens(lens)
+    n_in = int(cu[-1])
+    L = n_in + 40
+    _say(f"prefill, {len(lens)} packed sequences over {n_in} of {L} tokens")
+    inp = layer_inputs(shape, 1, L, 24, dtype, N=len(lens), s0_std=0.1, conv_std=1.0)
+    got = run_prefill(shape, dtype, inp, cu=cu, o_fill=float("nan"))
+    ref = oracle.gdn_forward(oparams(shape), inp["qkv"][:, :, :n_in], inp["gate"][:, :n_in],
+                             inp["beta"][:, :n_in], inp["w"], inp["conv0"], inp["S0"], cu_seqlens=cu)
+    assert bool(torch.isfinite(got["o"][:, :n_in]).all())
+    assert rel_err(got["o"][:, :n_in], ref["o"]) <= TOL[dtype]
+    assert bool(torch.isnan(got["o"][:, n_in:]).all())
+    assert rel_err(got["S"], ref["S"]) <= TOL[dtype]
+    empty = torch.from_numpy(np.flatnonzero(lens == 0))
+    assert len(empty) > 0
+    assert torch.equal(got["S"].cpu()[empty], torch.from_numpy(inp["S0"])[empty])
+    assert np.array_equal(got["conv_out"].float().cpu().numpy(), ref["conv_out"])
+
+
 @pytest.mark.parametrize("L", [512, 2000], ids=["one_chain", "eight_segments"])
 def test_prefill_long_memory(L):
     """Weak decay (gate scaled by 0.01) so early errors do not fade; beta near 1. At 2000

@@ -38,9 +38,10 @@ def _block(shape, dtype, B, T, blk, base):
     return inp
 
 
-def _run_chain(shape, dtype, B, widths):
+def _run_chain(shape, dtype, B, widths, accept=None):
     """Run the copying chain and the zero-copy chain side by side over blocks of the
-    given widths; check both against the oracle and against each other."""
+    given widths; check both against the oracle and against each other. accept(blk, T)
+    gives the accepted lengths of a block (default: drawn uniformly from 0..T-1)."""
     p = params(shape, dtype)
     op = oparams(shape)
     base = layer_inputs(shape, B, 1, 61, dtype, s0_std=0.1, conv_std=1.0)
@@ -67,7 +68,7 @@ def _run_chain(shape, dtype, B, widths):
             nxt = torch.empty_like(snap_a)
             gdn.gdn_verify_block_slots(p, None, x, g, b, w, cs_b, snap_b, acc_prev, nxt, o_b)
             snap_b = nxt
-        acc = gi.accept_len(B, T, 61 + blk)
+        acc = gi.accept_len(B, T, 61 + blk) if accept is None else accept(blk, T)
         acc_d = dev(acc)
         S_new, c_new = torch.empty_like(S_a), torch.empty_like(cs_a)
         gdn.gdn_verify_commit(p, acc_d, x, cs_a, snap_a, c_new, S_new)
@@ -97,6 +98,36 @@ def test_verify_width_zero_copy_chain(T):
 def test_verify_width_tiny_f32(T):
     _say(f"verify width {T}, zero-copy chain, tiny fp32")
     _run_chain(gi.TINY_GQA, "f32", 2, [T, T, T, T])
+
+
+@pytest.mark.parametrize("T", [2, 16])
+def test_verify_accept_extremes(T):
+    """Every block accepts nothing for some rows (length 0: the state after the first
+    token) and everything for others (length T-1), rotating over the rows."""
+    _say(f"verify width {T}, accept lengths 0 and T-1")
+    pattern = np.array([0, T - 1, T - 1, 0], np.int32)
+    _run_chain(SMALL128, "bf16", 4, [T, T, T, T], accept=lambda blk, T: np.roll(pattern, blk))
+
+
+def test_verify_commit_clamps_accept_len():
+    """accept_len outside [0, T-1] is clamped: the commit equals the one with the
+    clamped lengths, bit for bit, for the state and the conv window."""
+    shape, dtype, B, T = SMALL128, "bf16", 4, 3
+    p = params(shape, dtype)
+    inp = layer_inputs(shape, B, T, 64, dtype, s0_std=0.1, conv_std=1.0)
+    x, g, b, w, cs = (dev(inp[k], dtype) for k in ("qkv", "gate", "beta", "w", "conv0"))
+    snap = torch.empty((B, T, shape.Hv, shape.dk, shape.dv), device="cuda")
+    o = torch.empty((B, T, shape.Hv, shape.dv), device="cuda")
+    gdn.gdn_verify_block(p, x, g, b, w, cs, dev(inp["S0"]), snap, o)
+    outs = []
+    for acc in ([-3, 0, 2, 9], [0, 0, 2, 2]):
+        S_new, c_new = torch.full_like(snap[:, 0], float("nan")), torch.empty_like(cs)
+        gdn.gdn_verify_commit(p, dev(np.array(acc, np.int32)), x, cs, snap, c_new, S_new)
+        outs.append((S_new, c_new))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0])
+    assert torch.equal(outs[0][1], outs[1][1])
+    assert torch.equal(outs[1][0], snap[torch.arange(B), torch.tensor([0, 0, 2, 2])])
 
 
 def test_verify_mixed_widths():
