@@ -454,8 +454,8 @@ def bench_verify(args, torch, gdn, gi, commit=False, rnd=None):
 # prefill (L = 4096) and ragged prefill (8 sequences)
 # ---------------------------------------------------------------------------
 PREFILL_FLOP_PER_TOKEN_HEAD = 163840   # bf16-MFMA-shaped work of the chunked form, C = 64, d = 128
-PREFILL_SOURCES = ["gdn_prefill_mfma.hip", "gdn_prefill_plan.hpp", "gdn_prefill.hip", "gdn_common.hpp", "gdn_mfma.hpp",
-                   "gdn_api.cpp"]
+PREFILL_SOURCES = ["gdn_prefill_mfma.hip", "gdn_prefill_plan.hpp", "gdn_packed.hpp", "gdn_prefill.hip", "gdn_common.hpp",
+                   "gdn_mfma.hpp", "gdn_api.cpp"]
 
 
 def prefill_bytes(sh, L, N, fused):

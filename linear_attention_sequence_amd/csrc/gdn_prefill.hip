@@ -29,6 +29,7 @@
 //                         what lets the sequential part split over slices.
 #include "gdn_common.hpp"
 #include "gdn_launch.hpp"
+#include "gdn_packed.hpp"
 
 namespace gdn {
 
@@ -44,6 +45,7 @@ struct PrefillWs {
     float* U;     // [Ttot, Hv, d]
     float* gam;   // [Ttot, Hv]      cumulative log-decay inside the chunk
     float* P;     // [NCmax, Hv, C, C]
+    int* cbase;   // [N + 1] packed prompts: first chunk slot of each sequence (write_chunk_bases)
     int nc_max;   // chunk slots of P
     size_t bytes;
 };
@@ -72,6 +74,7 @@ static PrefillWs ws_layout(void* base, int B, int L, int N, int Hk, int Hv, int 
     w.U = take(Ttot * Hv * d);
     w.gam = take(Ttot * Hv);
     w.P = take(nc * Hv * C * C);
+    w.cbase = ragged ? reinterpret_cast<int*>(take(static_cast<size_t>(N) + 1)) : nullptr;
     w.nc_max = static_cast<int>(nc);
     w.bytes = off;
     return w;
@@ -109,6 +112,9 @@ __global__ __launch_bounds__(256) void prefill_front_kernel(PrefillArgs a, Prefi
     const Tin* x = static_cast<const Tin*>(a.qkv) + (static_cast<size_t>(row) * a.D + ch0) * a.L;
     const Tin* w = static_cast<const Tin*>(a.w);
     const Tin* cin = static_cast<const Tin*>(a.conv_in);
+    // packed prompts: the first workgroup writes the chunk slot table of the chunk and
+    // carry kernels
+    if (a.cu != nullptr && blockIdx.x == 0) write_chunk_bases(a.N, a.L, a.cu, a.chunk, ws.nc_max, ws.cbase);
 
     if (threadIdx.x < TT) {
         const int p = p0 + threadIdx.x;
@@ -176,16 +182,20 @@ __global__ __launch_bounds__(256) void prefill_front_kernel(PrefillArgs a, Prefi
     }
 }
 
-// Locate chunk `id` of the launch: sequence n and chunk index inside it.
-__device__ __forceinline__ bool find_chunk(int id, const PrefillArgs& a, int* n_out, int* c_out, Seg* seg) {
-    int acc = 0;
-    for (int n = 0; n < a.N; ++n) {
-        const Seg s = segment_of(n, a.L, a.cu);
-        const int nc = chunks_of(s, a.chunk);
-        if (id < acc + nc) { *n_out = n; *c_out = id - acc; *seg = s; return true; }
-        acc += nc;
+// Locate chunk slot `id` of the launch: sequence n and chunk index inside it (rows of
+// equal length unpacked, the table of first slots packed).
+__device__ __forceinline__ bool find_chunk(int id, const PrefillArgs& a, const PrefillWs& ws, int* n_out,
+                                           int* c_out, Seg* seg) {
+    if (a.cu == nullptr) {
+        const int per = (a.L + a.chunk - 1) / a.chunk;
+        if (per == 0 || id >= a.N * per) return false;
+        *n_out = id / per;
+        *c_out = id - *n_out * per;
+    } else if (!chunk_slot(id, a.N, ws.cbase, n_out, c_out)) {
+        return false;
     }
-    return false;
+    *seg = segment_of(*n_out, a.L, a.cu);
+    return *c_out >= 0 && *c_out < chunks_of(*seg, a.chunk);   // (always, from the table the front kernel wrote)
 }
 
 // ---- chunk phase: Gam, A, T, W, U, P ---------------------------------------------
@@ -198,7 +208,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, Prefi
     const int id = blockIdx.x / a.Hv;
     int n, c;
     Seg seg;
-    if (id >= ws.nc_max || !find_chunk(id, a, &n, &c, &seg)) return;
+    if (id >= ws.nc_max || !find_chunk(id, a, ws, &n, &c, &seg)) return;
     const int f = a.Hv / a.Hk, hk = h / f;
     const int nt = min(C, seg.len - c * C);
     const size_t tok0 = static_cast<size_t>(seg.row) * a.L + seg.start + static_cast<size_t>(c) * C;
@@ -284,8 +294,8 @@ __global__ __launch_bounds__(256) void prefill_carry_kernel(PrefillArgs a, Prefi
     const int f = a.Hv / a.Hk, hk = h / f;
     const int tid = threadIdx.x;
     const Seg seg = segment_of(n, a.L, a.cu);
-    int base = 0;  // global id of this sequence's first chunk
-    for (int m = 0; m < n; ++m) base += chunks_of(segment_of(m, a.L, a.cu), C);
+    // chunk slot of this sequence's first chunk
+    const int base = a.cu != nullptr ? min(max(ws.cbase[n], 0), ws.nc_max) : n * ((a.L + C - 1) / C);
     const int nchunks = chunks_of(seg, C);
 
     float* Sg = a.S + (static_cast<size_t>(n) * a.Hv + h) * DK * DV + j0;
@@ -384,12 +394,15 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, int in_dtype, hipStream
     {
         const long long blocks = static_cast<long long>(a.B) * ((a.L + kFrontTile - 1) / kFrontTile) * (2 * a.Hk + a.Hv);
         void* args[] = {const_cast<PrefillArgs*>(&a), &ws};
-        if (blocks > 0) {
-            e = hipLaunchKernel(reinterpret_cast<const void*>(&prefill_front_kernel<Tin, D>),
-                                dim3(static_cast<unsigned>(blocks)), dim3(256), args, 0, stream);
-            if (e != hipSuccess) return e;
+        if (blocks == 0) {   // no tokens: every state stays as it is, and the conv windows are copied
+            ConvArgs ca{a.B, a.L, a.D, a.N, a.qkv, a.w, a.conv_in, a.conv_out, nullptr, a.cu};
+            return launch_conv_state(ca, in_dtype, stream);
         }
+        e = hipLaunchKernel(reinterpret_cast<const void*>(&prefill_front_kernel<Tin, D>),
+                            dim3(static_cast<unsigned>(blocks)), dim3(256), args, 0, stream);
+        if (e != hipSuccess) return e;
     }
+    // (the front kernel wrote the chunk slot table of packed prompts that the next kernels read)
     {
         const long long blocks = static_cast<long long>(nc) * a.Hv;
         void* args[] = {const_cast<PrefillArgs*>(&a), &ws};

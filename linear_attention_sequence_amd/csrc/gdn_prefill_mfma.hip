@@ -44,6 +44,7 @@
 #include "gdn_common.hpp"
 #include "gdn_launch.hpp"
 #include "gdn_mfma.hpp"
+#include "gdn_packed.hpp"
 #include "gdn_prefill_plan.hpp"
 
 namespace gdn {
@@ -75,6 +76,7 @@ struct Ws {
     _Float16* P;    // [NC, Hv, C, C] keys in k order
     _Float16* KT;   // [NC, Hk, D, C] keys of the chunk, transposed, tokens in k order
     float* coef;    // [NC, Hv, COEF]: exp(Gam_t), exp(Gam_last - Gam_t), exp(Gam_last), 2^uexp
+    int* cbase;     // [N + 1] packed prompts: first chunk slot of each sequence (write_chunk_bases)
     // segmented carry (see carry_kernel): the chunks of a sequence split into nseg segments
     float* Sent;    // [N, Hv, D, D] entry state of segment 1
     _Float16* Mhl;  // [nseg - 2, N, Hv, 2, D, D] state maps of segments 1 .. nseg - 2 (S_end = M S_entry + R):
@@ -99,6 +101,7 @@ static Ws layout(void* base, int B, int L, int N, int Hk, int Hv, bool ragged) {
     w.P = static_cast<_Float16*>(at(l.P, l.n_P));
     w.KT = static_cast<_Float16*>(at(l.KT, l.n_KT));
     w.coef = static_cast<float*>(at(l.coef, l.n_coef));
+    w.cbase = static_cast<int*>(at(l.cbase, l.n_cbase));
     w.Sent = static_cast<float*>(at(l.Sent, l.n_Sent));
     w.Mhl = static_cast<_Float16*>(at(l.Mhl, l.n_Mhl));
     w.Mexp = static_cast<int*>(at(l.Mexp, l.n_Mexp));
@@ -112,15 +115,20 @@ static Ws layout(void* base, int B, int L, int N, int Hk, int Hv, bool ragged) {
 
 __device__ __forceinline__ int chunks_of(const Seg& s) { return (s.len + C - 1) / C; }
 
-__device__ __forceinline__ bool find_chunk(int id, const PrefillArgs& a, int* n_out, int* c_out, Seg* seg) {
-    int acc = 0;
-    for (int n = 0; n < a.N; ++n) {
-        const Seg s = segment_of(n, a.L, a.cu);
-        const int nc = chunks_of(s);
-        if (id < acc + nc) { *n_out = n; *c_out = id - acc; *seg = s; return true; }
-        acc += nc;
+// Sequence n of chunk slot id and the chunk's index c inside it: rows of equal length
+// unpacked, the table of first slots (write_chunk_bases) packed.
+__device__ __forceinline__ bool find_chunk(int id, const PrefillArgs& a, const Ws& ws, int* n_out, int* c_out,
+                                           Seg* seg) {
+    if (a.cu == nullptr) {
+        const int per = plan::chunks_of_len(a.L);
+        if (per == 0 || id >= a.N * per) return false;
+        *n_out = id / per;
+        *c_out = id - *n_out * per;
+    } else if (!chunk_slot(id, a.N, ws.cbase, n_out, c_out)) {
+        return false;
     }
-    return false;
+    *seg = segment_of(*n_out, a.L, a.cu);
+    return *c_out >= 0 && *c_out < chunks_of(*seg);   // (always, from the table the front kernel wrote)
 }
 
 // Sequence owning token p of a row (clamped cu_seqlens), or -1.
@@ -183,6 +191,9 @@ __global__ __launch_bounds__(256) void front_kernel(PrefillArgs a, Ws ws) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const Tin* x = static_cast<const Tin*>(a.qkv) + (static_cast<size_t>(row) * a.D + ch0) * a.L;
     const bool is_q = u < a.Hk;
+    // packed prompts: the first workgroup writes the chunk slot table of the chunk and
+    // carry kernels
+    if (a.cu != nullptr && blockIdx.x == 0) write_chunk_bases(a.N, a.L, a.cu, C, ws.nc_max, ws.cbase);
 
     // Interior tiles of unpacked bf16 rows whose length is a multiple of 8 (so that every
     // 8-token group is 16-byte aligned): each lane loads 8 tokens of a channel and the 4
@@ -366,12 +377,15 @@ __global__ __launch_bounds__(256) void front_kernel(PrefillArgs a, Ws ws) {
             }
         }
         if (a.cu != nullptr && tile == 0 && row == 0) {        // empty sequences keep their state
-            for (int n = 0; n < a.N; ++n) {
-                if (segment_of(n, a.L, a.cu).len != 0) continue;
-                const size_t base = (static_cast<size_t>(n) * a.D + ch0 + c) * (kConvK - 1);
-                if (th == 0) {
+            for (int n0 = 0; n0 < a.N; n0 += 64) {             // 64 sequences a round, one per lane
+                const int nl = n0 + lane;
+                const bool empty = nl < a.N && segment_of(nl, a.L, a.cu).len == 0;
+                for (unsigned long long em = __ballot(empty); em != 0; em &= em - 1) {
+                    const size_t base = (static_cast<size_t>(n0 + __builtin_ctzll(em)) * a.D + ch0 + c) * (kConvK - 1);
+                    if (th == 0) {
 #pragma unroll
-                    for (int j = 0; j < kConvK - 1; ++j) co[base + j] = cin[base + j];
+                        for (int j = 0; j < kConvK - 1; ++j) co[base + j] = cin[base + j];
+                    }
                 }
             }
         }
@@ -468,15 +482,18 @@ __global__ __launch_bounds__(256, 4) void chunk_kernel(PrefillArgs a, Ws ws) {
     Seg seg;
     if (id == 0 && a.cu != nullptr && threadIdx.x < D) {   // empty sequences keep the value channels' conv state
         const int ch = 2 * a.Hk * D + h * D + threadIdx.x;
-        for (int m = 0; m < a.N; ++m) {
-            if (segment_of(m, a.L, a.cu).len != 0) continue;
-            const size_t cb = (static_cast<size_t>(m) * a.D + ch) * (kConvK - 1);
+        for (int m0 = 0; m0 < a.N; m0 += 64) {             // 64 sequences a round, one per lane
+            const int ml = m0 + (threadIdx.x & 63);
+            const bool empty = ml < a.N && segment_of(ml, a.L, a.cu).len == 0;
+            for (unsigned long long em = __ballot(empty); em != 0; em &= em - 1) {
+                const size_t cb = (static_cast<size_t>(m0 + __builtin_ctzll(em)) * a.D + ch) * (kConvK - 1);
 #pragma unroll
-            for (int j = 0; j < kConvK - 1; ++j)
-                static_cast<Tin*>(a.conv_out)[cb + j] = static_cast<const Tin*>(a.conv_in)[cb + j];
+                for (int j = 0; j < kConvK - 1; ++j)
+                    static_cast<Tin*>(a.conv_out)[cb + j] = static_cast<const Tin*>(a.conv_in)[cb + j];
+            }
         }
     }
-    if (id >= ws.nc_max || !find_chunk(id, a, &n, &c, &seg)) return;
+    if (id >= ws.nc_max || !find_chunk(id, a, ws, &n, &c, &seg)) return;
     const int nt = min(C, seg.len - c * C);
     const size_t tok0 = static_cast<size_t>(seg.row) * a.L + seg.start + static_cast<size_t>(c) * C;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1017,8 +1034,8 @@ __global__ __launch_bounds__((NW + (LW ? NL : 0)) * 64) void carry_kernel(Prefil
     const int lcol0 = wave * 16 * NTW;                   // first column of this wave, inside the workgroup
     const int col0 = ucol0 + lcol0;
     const Seg seg = segment_of(n, a.L, a.cu);
-    int base = 0;
-    for (int m = 0; m < n; ++m) base += chunks_of(segment_of(m, a.L, a.cu));
+    const int base = a.cu != nullptr ? min(max(ws.cbase[n], 0), ws.nc_max)   // first chunk slot
+                                     : n * plan::chunks_of_len(a.L);
     int nch = chunks_of(seg);
     if (base + nch > ws.nc_max) nch = ws.nc_max - base;   // only malformed cu_seqlens get here
     if (nch <= 0) return;
@@ -1652,6 +1669,11 @@ static hipError_t launch_mfma_t(const PrefillArgs& a, int in_dtype, hipStream_t 
                             dim3(256), args, 0, stream);
         if (e != hipSuccess) return e;
     }
+    if (fblocks == 0) {   // no tokens: every state stays as it is, and the conv windows are copied
+        ConvArgs ca{a.B, a.L, a.D, a.N, a.qkv, a.w, a.conv_in, a.conv_out, nullptr, a.cu};
+        return launch_conv_state(ca, in_dtype, stream);
+    }
+    // (the front kernel wrote the chunk slot table of packed prompts that the next kernels read)
     const long long cblocks = static_cast<long long>(ws.nc_max) * a.Hv;
     if (cblocks > 0) {
         e = hipLaunchKernel(reinterpret_cast<const void*>(&pf2::chunk_kernel<Tin>), dim3(static_cast<unsigned>(cblocks)),
@@ -1677,9 +1699,7 @@ static hipError_t launch_mfma_t(const PrefillArgs& a, int in_dtype, hipStream_t 
         else e = launch_carry<kWholeNTW, kWholeNW>(argp, cp.l[i].units, stream);
         if (e != hipSuccess) return e;
     }
-    if (fblocks > 0) return hipSuccess;   // the front kernel wrote the conv state
-    ConvArgs ca{a.B, a.L, a.D, a.N, a.qkv, a.w, a.conv_in, a.conv_out, nullptr, a.cu};
-    return launch_conv_state(ca, in_dtype, stream);
+    return hipSuccess;   // the front and chunk kernels wrote the conv state
 }
 
 // Runs the gated RMSNorm of gdn_prefill_ex too when a.fu.z is set (fused into the carry).

@@ -82,8 +82,8 @@ constexpr size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(25
 // Byte offsets of the workspace regions (from a 256-byte aligned base) and their sizes
 // in elements of their types.
 struct Layout {
-    size_t qh, kh, W, U, P, KT, coef, Sent, Mhl, Mexp, Rseg, bytes;
-    size_t n_qh, n_kh, n_W, n_U, n_P, n_KT, n_coef, n_Sent, n_Mhl, n_Mexp, n_Rseg;
+    size_t qh, kh, W, U, P, KT, coef, cbase, Sent, Mhl, Mexp, Rseg, bytes;
+    size_t n_qh, n_kh, n_W, n_U, n_P, n_KT, n_coef, n_cbase, n_Sent, n_Mhl, n_Mexp, n_Rseg;
     int nc_max, nseg;
 };
 
@@ -99,6 +99,9 @@ constexpr Layout layout(int B, int L, int N, int Hk, int Hv, bool ragged) {
     w.n_P = nc * Hv * C * C;   w.P = off;    off = align256(off + w.n_P * 2);
     w.n_KT = nc * Hk * D * C;  w.KT = off;   off = align256(off + w.n_KT * 2);
     w.n_coef = nc * Hv * COEF; w.coef = off; off = align256(off + w.n_coef * 4);
+    if (ragged) {              // packed prompts: each sequence's first chunk slot, and the total
+        w.n_cbase = static_cast<size_t>(N) + 1; w.cbase = off; off = align256(off + w.n_cbase * 4);
+    }
     w.nseg = segments(B, L, N, Hv, ragged, kLayoutCUs);
     if (w.nseg > 1) {
         const size_t tiles = static_cast<size_t>(N) * Hv * D * D;

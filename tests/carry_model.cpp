@@ -131,6 +131,51 @@ size_t check_map_geometry(int NW, int BYTES) {
     return top;
 }
 
+// The first chunk slot of sequence n as the kernels take it: n times the chunks per row
+// unpacked; packed, the table the front kernel writes (64-bit prefix sums of the chunk
+// counts, clamped to the slot count), whose entries n and n + 1 lie inside its region
+// and which, for sequences that fit, equals the plain sum over the sequences before.
+std::vector<int> slot_table(const Config& c, const Layout& lay) {
+    std::vector<int> t(static_cast<size_t>(c.N) + 1);
+    long long run = 0;
+    for (int n = 0; n <= c.N; ++n) {
+        t[n] = static_cast<int>(std::min(run, static_cast<long long>(lay.nc_max)));
+        if (n < c.N) run += chunks_of_len(c.lens[n]);
+    }
+    return t;
+}
+
+int first_slot(const Config& c, const Layout& lay, const std::vector<int>& t, int n) {
+    if (!c.ragged) return n * chunks_of_len(c.L);
+    REQUIRE(static_cast<size_t>(n) + 1 < lay.n_cbase && lay.cbase + lay.n_cbase * 4 <= lay.bytes);
+    long long sum = 0;
+    for (int m = 0; m < n; ++m) sum += chunks_of_len(c.lens[m]);
+    REQUIRE(sum >= lay.nc_max || t[n] == sum);
+    return t[n];
+}
+
+// The chunk kernel's lookup of slot id: the sequence and its chunk index (binary search
+// of the table for packed prompts), or false for a slot no sequence fills.
+bool slot_owner(const Config& c, const std::vector<int>& t, int id, int* n_out, int* c_out) {
+    if (!c.ragged) {
+        const int per = chunks_of_len(c.L);
+        if (per == 0 || id >= c.N * per) return false;
+        *n_out = id / per;
+        *c_out = id - *n_out * per;
+        return true;
+    }
+    int lo = 0, hi = c.N - 1, n = -1;
+    while (lo <= hi) {
+        const int mid = (lo + hi) >> 1;
+        REQUIRE(mid >= 0 && mid <= c.N);
+        if (t[mid] <= id) { n = mid; lo = mid + 1; } else { hi = mid - 1; }
+    }
+    if (n < 0 || id >= t[n + 1]) return false;
+    *n_out = n;
+    *c_out = id - t[n];
+    return true;
+}
+
 void model_launch(const Config& c, const Layout& lay, int nseg, const CarryLaunch& cl, bool norm) {
     // the launcher's choice: half-head workgroups with one loader wave, two in the second pass
     const WG wg = cl.half ? WG{4, 1, true, cl.pass == 2 ? 2 : 1} : WG{8, 1, false, 1};
@@ -152,6 +197,7 @@ void model_launch(const Config& c, const Layout& lay, int nseg, const CarryLaunc
     const size_t S_elems = tiles, o_elems = static_cast<size_t>(c.B) * c.L * c.Hv * D;
     std::vector<int> covered(static_cast<size_t>(NK) * NS * nh, 0);
     const bool sort = c.ragged && c.N <= kSortMax;
+    const std::vector<int> table = c.ragged ? slot_table(c, lay) : std::vector<int>();
     for (long long blk = 0; blk < blocks; ++blk) {
         const CarryUnit un = carry_unit(static_cast<int>(blk), NK * NS, c.N, c.Hk, c.Hv);
         REQUIRE(un.slice >= 0 && un.slice < NK * NS && un.n >= 0 && un.n < c.N && un.h >= 0 && un.h < c.Hv);
@@ -160,8 +206,7 @@ void model_launch(const Config& c, const Layout& lay, int nseg, const CarryLaunc
         int n = un.n;
         if (sort) n = sort_rank_sequence(c, n);
         const int f = c.Hv / c.Hk, hk = h / f;
-        int base = 0;
-        for (int m = 0; m < n; ++m) base += chunks_of_len(c.lens[m]);
+        const int base = first_slot(c, lay, table, n);
         int nch = chunks_of_len(c.lens[n]);
         if (base + nch > lay.nc_max) nch = lay.nc_max - base;
         if (nch <= 0) continue;   // the whole workgroup returns before any barrier
@@ -350,6 +395,21 @@ void model(const Config& c, bool norm) {
             ++seen[static_cast<size_t>(u.id) * c.Hv + u.h];
         }
         for (int v : seen) REQUIRE(v == 1);
+        // every slot that a sequence fills names that sequence and one of its chunks, and
+        // every chunk of every sequence has exactly one slot
+        const std::vector<int> t = c.ragged ? slot_table(c, lay) : std::vector<int>();
+        std::vector<int> owned(static_cast<size_t>(c.N) * (chunks_of_len(c.L) + 1), 0);
+        std::vector<long long> first(static_cast<size_t>(c.N) + 1, 0);
+        for (int n = 0; n < c.N; ++n) first[n + 1] = first[n] + chunks_of_len(c.lens[n]);
+        for (int id = 0; id < lay.nc_max; ++id) {
+            int n = -1, cc = -1;
+            if (!slot_owner(c, t, id, &n, &cc)) { REQUIRE(id >= first[c.N]); continue; }
+            REQUIRE(n >= 0 && n < c.N && cc >= 0 && cc < chunks_of_len(c.lens[n]) && first[n] + cc == id);
+            ++owned[static_cast<size_t>(n) * (chunks_of_len(c.L) + 1) + cc];
+        }
+        for (int n = 0; n < c.N; ++n)
+            for (int cc = 0; cc < chunks_of_len(c.lens[n]); ++cc)
+                REQUIRE(owned[static_cast<size_t>(n) * (chunks_of_len(c.L) + 1) + cc] == 1);
     }
     for (int i = 0; i < cp.count; ++i) model_launch(c, lay, cp.nseg, cp.l[i], norm);
     if (!norm) check_value_loads(c);
