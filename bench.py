@@ -29,8 +29,8 @@ each with its own median, spread and roofline. --no-extras skips them.
 
 Other workloads as the main line (--workload verify | prefill | ragged | commit
 | decode_fused | prefill_fused | ragged_fused | spec_round_copy |
-spec_round_slots; --verify-t sets the verify block width) print the same kind of
-JSON line.
+spec_round_slots | packed_short, 512 prompts of 64 tokens packed in one prefill call;
+--verify-t sets the verify block width) print the same kind of JSON line.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
 """
@@ -468,11 +468,18 @@ def prefill_bytes(sh, L, N, fused):
     return n
 
 
-def bench_prefill(args, torch, gdn, gi, ragged=False, fused=False):
+SHORT_N, SHORT_LEN = 512, 64   # many short prompts packed in one call
+
+
+def bench_prefill(args, torch, gdn, gi, ragged=False, fused=False, short=False):
     sh = gi.QWEN
-    w_ = gi.WORKLOADS[3 if ragged else 2]
+    w_ = gi.WORKLOADS[3 if ragged or short else 2]
     seed = w_.seed
-    if ragged:
+    if short:   # the ragged workload's inputs, cut into SHORT_N sequences of SHORT_LEN tokens
+        cu_np = gi.cu_seqlens(np.full(SHORT_N, SHORT_LEN))
+        L, N = SHORT_N * SHORT_LEN, SHORT_N
+        ragged = True
+    elif ragged:
         lens = gi.seq_lens(gi.RAGGED_N, gi.RAGGED_LO, gi.RAGGED_HI, seed)
         cu_np = gi.cu_seqlens(lens)
         L, N = int(cu_np[-1]), gi.RAGGED_N
@@ -512,7 +519,7 @@ def bench_prefill(args, torch, gdn, gi, ragged=False, fused=False):
     achieved = flops / (t["median_us"] * 1e-6) / 1e12
     nbytes = prefill_bytes(sh, L, N, fused)
     cname = ("ragged_prefill_8seqs_d128" if ragged else "prefill_L4096_d128") + ("_fused" if fused else "")
-    c = counters(cname, source_digest(PREFILL_SOURCES))
+    c = None if short else counters(cname, source_digest(PREFILL_SOURCES))
     roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": achieved / BF16_PEAK_TFLOPS, "traffic": traffic_from_counters(c),
             "kernel": "gdn_prefill (all kernels of one call)",
@@ -523,7 +530,8 @@ def bench_prefill(args, torch, gdn, gi, ragged=False, fused=False):
     return {
         "metric": METRIC, "value": L * args.steps / wall, "unit": "tokens/s",
         "ms_per_step": 1e3 * wall / args.steps,
-        "config": {"workload": w_.name + ("+gate_beta_prologue+gated_rmsnorm_epilogue" if fused else ""),
+        "config": {"workload": (f"packed prefill, {SHORT_N} sequences of {SHORT_LEN} tokens" if short else w_.name)
+                   + ("+gate_beta_prologue+gated_rmsnorm_epilogue" if fused else ""),
                    "L_total": L, "N": N, "Hk": sh.Hk, "Hv": sh.Hv, "dk": sh.dk,
                    "dv": sh.dv, "chunk": 64, "cache": f"{reps} input replicas"},
         "dtype": "f32",
@@ -538,7 +546,7 @@ def bench_prefill(args, torch, gdn, gi, ragged=False, fused=False):
 # region, and decode's first repetition after a 1.6 ms warm-up ran about 3% slow.
 DEFAULT_STEPS = {"decode": (256, 256), "decode_fused": (256, 256), "verify": (50, 40), "commit": (50, 100),
                  "prefill": (60, 200), "ragged": (20, 40), "prefill_fused": (60, 200), "ragged_fused": (20, 40),
-                 "spec_round_copy": (50, 30), "spec_round_slots": (50, 40)}
+                 "spec_round_copy": (50, 30), "spec_round_slots": (50, 40), "packed_short": (20, 30)}
 EXTRAS = ("prefill", "ragged", "verify", "commit")
 
 
@@ -551,7 +559,8 @@ def bench_fn(name):
             "prefill_fused": lambda a, t, g, i: bench_prefill(a, t, g, i, fused=True),
             "spec_round_copy": lambda a, t, g, i: bench_verify(a, t, g, i, rnd="copy"),
             "spec_round_slots": lambda a, t, g, i: bench_verify(a, t, g, i, rnd="slots"),
-            "ragged_fused": lambda a, t, g, i: bench_prefill(a, t, g, i, ragged=True, fused=True)}[name]
+            "ragged_fused": lambda a, t, g, i: bench_prefill(a, t, g, i, ragged=True, fused=True),
+            "packed_short": lambda a, t, g, i: bench_prefill(a, t, g, i, short=True)}[name]
 
 
 def with_measured(res, ceil):

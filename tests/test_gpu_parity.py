@@ -193,15 +193,18 @@ def test_prefill_packed_thousands_of_sequences():
     assert np.array_equal(got["conv_out"].float().cpu().numpy(), ref["conv_out"])
 
 
-@pytest.mark.parametrize("L", [512, 2000], ids=["one_chain", "eight_segments"])
-def test_prefill_long_memory(L):
+@pytest.mark.parametrize("L,scale", [(512, 0.01), (2000, 0.01), (65536, 0.001)],
+                         ids=["one_chain", "eight_segments", "long_context_L65536"])
+def test_prefill_long_memory(L, scale):
     """Weak decay (gate scaled by 0.01) so early errors do not fade; beta near 1. At 2000
     tokens the carry runs in 8 segments, whose state maps then stay far from zero and whose
-    entry states are chained through up to 6 maps."""
+    entry states are chained through up to 6 maps. The 65,536-token prompt (1,024 chunks,
+    8 segments of about 130) has its gates scaled by 0.001: a memory of about a thousand
+    tokens."""
     shape, dtype = SMALL128, "bf16"
-    _say(f"long memory L={L}")
+    _say(f"long memory L={L} gate scale {scale}")
     inp = layer_inputs(shape, 1, L, 13, dtype, s0_std=0.1, conv_std=1.0)
-    inp["gate"] = gi.round_to(0.01 * inp["gate"].astype(np.float64), dtype)
+    inp["gate"] = gi.round_to(scale * inp["gate"].astype(np.float64), dtype)
     inp["beta"] = gi.round_to(0.5 + 0.5 * inp["beta"].astype(np.float64), dtype)
     got = run_prefill(shape, dtype, inp)
     ref = oracle.gdn_forward(oparams(shape), inp["qkv"], inp["gate"], inp["beta"], inp["w"],
