@@ -67,7 +67,7 @@ typedef enum {
     GDN_ERR_DTYPE = 3,        /* in_dtype is not a gdn_dtype */
     GDN_ERR_UNSUPPORTED = 4,  /* a valid configuration outside the supported set */
     GDN_ERR_ALIAS = 5,        /* two buffers that must not overlap do */
-    GDN_ERR_WORKSPACE = 6,    /* workspace NULL or smaller than gdn_prefill_workspace_size() */
+    GDN_ERR_WORKSPACE = 6,    /* workspace NULL or smaller than the call needs */
     GDN_ERR_LAUNCH = 7,       /* the HIP runtime refused a kernel launch */
     GDN_ERR_ALIGN = 8,        /* a tensor pointer is not 16-byte aligned (workspace: 256) */
     GDN_ERR_TOO_LARGE = 9     /* gdn_prefill_ex_noalloc: the call needs more than its static scratch */
@@ -219,8 +219,8 @@ gdn_status gdn_verify_block_slots(const gdn_params* p, const gdn_fusion* fusion,
  * gdn_prefill_workspace_size — bytes of device workspace gdn_prefill needs for
  * these sizes and p->in_dtype (bf16 inputs at head dim 128 take the MFMA path,
  * whose workspace is smaller than the fp32 path's); an upper bound that holds
- * whatever cu_seqlens contains. Returns 0 when the arguments are invalid or
- * unsupported.
+ * whatever cu_seqlens contains, and with or without the fusions of gdn_prefill_ex.
+ * Returns 0 when the arguments are invalid or unsupported.
  */
 size_t gdn_prefill_workspace_size(const gdn_params* p, int32_t B, int32_t L, int32_t N,
                                   int32_t chunk);
@@ -239,8 +239,11 @@ size_t gdn_prefill_workspace_size(const gdn_params* p, int32_t B, int32_t L, int
  *   o              [B, L, Hv, dv]     fp32 (tokens outside every sequence untouched)
  *   cu_seqlens     as for gdn_conv1d_silu (NULL: N == B sequences of length L)
  *   chunk          chunk length (64)
- *   workspace      device memory of at least gdn_prefill_workspace_size() bytes,
- *                  256-byte aligned; its contents on entry do not matter.
+ *   workspace      device memory, 256-byte aligned, of workspace_bytes bytes:
+ *                  gdn_prefill_workspace_size() always suffices; a call given fewer
+ *                  bytes than its own layout needs (which depends on cu_seqlens and,
+ *                  for gdn_prefill_ex, on the fusions) returns GDN_ERR_WORKSPACE. Its
+ *                  contents on entry do not matter.
  */
 gdn_status gdn_prefill(const gdn_params* p, int32_t B, int32_t L, const void* qkv,
                        const void* gate, const void* beta, const void* conv_weight,
@@ -277,10 +280,11 @@ gdn_status gdn_prefill_ex(const gdn_params* p, const gdn_fusion* fusion, int32_t
  * (no hipMalloc, hipFree or allocating library routine); the array's address is looked
  * up once per device (hipGetSymbolAddress, on the first call made with that device
  * current) and the device holds the array until the process ends.
- *   Limit: a call whose gdn_prefill_workspace_size() exceeds 134217728 bytes returns
- *   GDN_ERR_TOO_LARGE and enqueues nothing (with bf16 inputs about 3,500 tokens at
- *   16 K / 32 V heads of dimension 128; gdn_prefill_workspace_size gives the exact
- *   need).
+ *   Limit: a call whose own workspace (for its packing and fusion; at most
+ *   gdn_prefill_workspace_size()) exceeds 134217728 bytes returns GDN_ERR_TOO_LARGE and
+ *   enqueues nothing: with bf16 inputs at 16 K / 32 V heads of dimension 128, one
+ *   prompt of up to 3,584 tokens, or 3,200 with the gated RMSNorm epilogue (whose
+ *   carry runs in more segments).
  *   Sharing: every call on one device uses that device's one array. Calls that can run
  *   at the same time on one device (different streams, or different host threads) race
  *   on it and must be serialised by the caller; calls on one stream run in order and

@@ -3,6 +3,7 @@
 // contract of each call.
 #include "gdn.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <hip/hip_runtime.h>
@@ -285,12 +286,17 @@ static gdn_status prefill_check_sizes(const gdn_params* p, int32_t B, int32_t L,
 
 size_t gdn_prefill_workspace_size(const gdn_params* p, int32_t B, int32_t L, int32_t N,
                                   int32_t chunk) {
-    // valid for either packing: with cu_seqlens (B == 1) or without (N == B)
+    // valid for either packing, with cu_seqlens (B == 1) or without (N == B), and with or
+    // without the gated RMSNorm epilogue: the largest of those layouts
     if (prefill_check_sizes(p, B, L, N, chunk, B == 1) != GDN_OK &&
         prefill_check_sizes(p, B, L, N, chunk, false) != GDN_OK)
         return 0;
-    return gdn::prefill_workspace_bytes(B, L, N, p->num_k_heads, p->num_v_heads, p->head_k_dim, chunk,
-                                        p->in_dtype);
+    size_t most = 0;
+    for (const bool ragged : {false, true})
+        for (const bool norm : {false, true})
+            most = std::max(most, gdn::prefill_workspace_bytes(B, L, N, p->num_k_heads, p->num_v_heads,
+                                                               p->head_k_dim, chunk, p->in_dtype, ragged, norm));
+    return most;
 }
 
 gdn_status gdn_prefill(const gdn_params* p, int32_t B, int32_t L, const void* qkv,
@@ -322,8 +328,8 @@ gdn_status gdn_prefill_ex(const gdn_params* p, const gdn_fusion* fusion, int32_t
         !conv_state_out || !S)
         return GDN_ERR_NULL;
     if (!aligned(S, 16) || (o && !aligned(o, 16))) return GDN_ERR_ALIGN;
-    const size_t need = gdn::prefill_workspace_bytes(B, L, N, p->num_k_heads, p->num_v_heads,
-                                                     p->head_k_dim, chunk, p->in_dtype);
+    const size_t need = gdn::prefill_workspace_bytes(B, L, N, p->num_k_heads, p->num_v_heads, p->head_k_dim,
+                                                     chunk, p->in_dtype, ragged, fu.z != nullptr);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return GDN_ERR_WORKSPACE;
     if (need > 0 && !aligned(workspace, 256)) return GDN_ERR_ALIGN;
     const long long D = dimD(p);
@@ -354,3 +360,18 @@ gdn_status gdn_prefill_ex(const gdn_params* p, const gdn_fusion* fusion, int32_t
 }
 
 }  // extern "C"
+
+namespace gdn {
+
+// The workspace one prefill call needs, for its own packing and fusion (at most what
+// gdn_prefill_workspace_size reports), or 0 for arguments that gdn_prefill_ex rejects
+// before it looks at the workspace.
+size_t prefill_call_workspace_bytes(const gdn_params* p, const gdn_fusion* fusion, int B, int L, int N, int chunk,
+                                    bool ragged) {
+    Fusion fu;
+    if (prefill_check_sizes(p, B, L, N, chunk, ragged) != GDN_OK || fusion_of(fusion, &fu) != GDN_OK) return 0;
+    return prefill_workspace_bytes(B, L, N, p->num_k_heads, p->num_v_heads, p->head_k_dim, chunk, p->in_dtype,
+                                   ragged, fu.z != nullptr);
+}
+
+}  // namespace gdn

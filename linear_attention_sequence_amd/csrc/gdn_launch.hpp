@@ -79,9 +79,12 @@ hipError_t launch_recurrent(const RecArgs& a, int in_dtype, int d, hipStream_t s
 hipError_t launch_commit(const CommitArgs& a, int in_dtype, int d, hipStream_t stream);
 hipError_t launch_conv1d_silu(const ConvArgs& a, int in_dtype, hipStream_t stream);
 hipError_t launch_conv_state(const ConvArgs& a, int in_dtype, hipStream_t stream);
-size_t prefill_workspace_bytes(int B, int L, int N, int Hk, int Hv, int d, int chunk, int in_dtype);
+// workspace of a prefill call with (ragged) or without cu_seqlens, with (norm) or without
+// the gated RMSNorm epilogue
+size_t prefill_workspace_bytes(int B, int L, int N, int Hk, int Hv, int d, int chunk, int in_dtype, bool ragged,
+                               bool norm);
 hipError_t launch_prefill(const PrefillArgs& a, int in_dtype, int d, hipStream_t stream);
-size_t prefill_mfma_workspace_bytes(int B, int L, int N, int Hk, int Hv);
+size_t prefill_mfma_workspace_bytes(int B, int L, int N, int Hk, int Hv, bool ragged, bool norm);
 hipError_t launch_prefill_mfma(const PrefillArgs& a, int in_dtype, hipStream_t stream);
 // gated RMSNorm of o in place over the tokens of every sequence (prefill epilogue)
 hipError_t launch_prefill_epilogue(const PrefillArgs& a, int in_dtype, int d, hipStream_t stream);

@@ -38,6 +38,13 @@ gdn_status scratch_of_current_device(void** out) {
 
 }  // namespace
 
+namespace gdn {
+// (gdn_api.cpp) the workspace of one prefill call, for its own packing and fusion; 0 for
+// arguments that gdn_prefill_ex rejects
+size_t prefill_call_workspace_bytes(const gdn_params* p, const gdn_fusion* fusion, int B, int L, int N, int chunk,
+                                    bool ragged);
+}  // namespace gdn
+
 extern "C" gdn_status gdn_prefill_ex_noalloc(const gdn_params* p, const gdn_fusion* fusion, int32_t B,
                                              int32_t L, const void* qkv, const void* gate,
                                              const void* beta, const void* conv_weight,
@@ -45,7 +52,7 @@ extern "C" gdn_status gdn_prefill_ex_noalloc(const gdn_params* p, const gdn_fusi
                                              float* S, float* o, const int32_t* cu_seqlens,
                                              int32_t N, int32_t chunk, void* stream) {
     // 0 for arguments gdn_prefill_ex rejects: it reports them itself below
-    const size_t need = gdn_prefill_workspace_size(p, B, L, N, chunk);
+    const size_t need = gdn::prefill_call_workspace_bytes(p, fusion, B, L, N, chunk, cu_seqlens != nullptr);
     if (need > kScratchBytes) return GDN_ERR_TOO_LARGE;
     void* ws = nullptr;
     if (need > 0) {

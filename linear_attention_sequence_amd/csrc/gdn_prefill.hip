@@ -80,13 +80,12 @@ static PrefillWs ws_layout(void* base, int B, int L, int N, int Hk, int Hv, int 
     return w;
 }
 
-size_t prefill_workspace_bytes(int B, int L, int N, int Hk, int Hv, int d, int chunk, int in_dtype) {
-    // the layout of the path the call takes (MFMA for bf16 inputs at d = 128, else the
-    // fp32 path), sized for the ragged layout and the plain one
-    if (d == 128 && in_dtype == 1) return prefill_mfma_workspace_bytes(B, L, N, Hk, Hv);
-    const size_t a = ws_layout(nullptr, B, L, N, Hk, Hv, d, chunk, true).bytes;
-    const size_t b = ws_layout(nullptr, B, L, N, Hk, Hv, d, chunk, false).bytes;
-    return a > b ? a : b;
+size_t prefill_workspace_bytes(int B, int L, int N, int Hk, int Hv, int d, int chunk, int in_dtype, bool ragged,
+                               bool norm) {
+    // the layout of the path the call takes: MFMA for bf16 inputs at d = 128, else the
+    // fp32 path (whose gated RMSNorm is a pass over o that needs no workspace)
+    if (d == 128 && in_dtype == 1) return prefill_mfma_workspace_bytes(B, L, N, Hk, Hv, ragged, norm);
+    return ws_layout(nullptr, B, L, N, Hk, Hv, d, chunk, ragged).bytes;
 }
 
 // Number of chunks of sequence n.

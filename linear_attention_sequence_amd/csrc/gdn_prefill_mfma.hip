@@ -89,8 +89,8 @@ struct Ws {
     size_t bytes;
 };
 
-static Ws layout(void* base, int B, int L, int N, int Hk, int Hv, bool ragged) {
-    const plan::Layout l = plan::layout(B, L, N, Hk, Hv, ragged);
+static Ws layout(void* base, int B, int L, int N, int Hk, int Hv, bool ragged, bool whole) {
+    const plan::Layout l = plan::layout(B, L, N, Hk, Hv, ragged, whole);
     char* b = static_cast<char*>(base);
     auto at = [&](size_t off, size_t n) -> void* { return (b != nullptr && n > 0) ? b + off : nullptr; };
     Ws w;
@@ -1616,10 +1616,8 @@ __global__ __launch_bounds__((NW + (LW ? NL : 0)) * 64) void carry_kernel(Prefil
 
 }  // namespace pf2
 
-size_t prefill_mfma_workspace_bytes(int B, int L, int N, int Hk, int Hv) {
-    const size_t a = pf2::layout(nullptr, B, L, N, Hk, Hv, true).bytes;
-    const size_t b = pf2::layout(nullptr, B, L, N, Hk, Hv, false).bytes;
-    return a > b ? a : b;
+size_t prefill_mfma_workspace_bytes(int B, int L, int N, int Hk, int Hv, bool ragged, bool norm) {
+    return pf2::layout(nullptr, B, L, N, Hk, Hv, ragged, norm).bytes;
 }
 
 // Whole-head carry workgroups: 8 waves of one 16-column tile each (two waves per
@@ -1658,9 +1656,10 @@ static hipError_t launch_carry(void** args, long long heads, hipStream_t stream)
 template <typename Tin>
 static hipError_t launch_mfma_t(const PrefillArgs& a, int in_dtype, hipStream_t stream) {
     const bool ragged = a.cu != nullptr;
-    pf2::Ws ws = pf2::layout(a.ws, a.B, a.L, a.N, a.Hk, a.Hv, ragged);
+    const bool norm = a.fu.z != nullptr;   // the gated RMSNorm fused into the carry's output store
+    pf2::Ws ws = pf2::layout(a.ws, a.B, a.L, a.N, a.Hk, a.Hv, ragged, norm);
     const int cus = device_cu_count();
-    ws.nseg = plan::carry_plan(a.B, a.L, a.N, a.Hv, ragged, cus).nseg;   // within the workspace's
+    ws.nseg = plan::carry_plan(a.B, a.L, a.N, a.Hv, ragged, cus, norm).nseg;   // within the workspace's
     void* args[] = {const_cast<PrefillArgs*>(&a), &ws};
     hipError_t e;
     const long long fblocks = static_cast<long long>(a.B) * ((a.L + pf2::TT - 1) / pf2::TT) * (2 * a.Hk);
@@ -1683,7 +1682,6 @@ static hipError_t launch_mfma_t(const PrefillArgs& a, int in_dtype, hipStream_t 
     // carry launches (plan::carry_plan: whole-head or half-head workgroups, one pass or
     // the two of the segmented carry); with the gated RMSNorm fused into the output
     // store, whole-head workgroups only
-    const bool norm = a.fu.z != nullptr;
     const plan::CarryPlan cp = plan::carry_plan(a.B, a.L, a.N, a.Hv, ragged, cus, norm);
     for (int i = 0; i < cp.count; ++i) {
         pf2::Ws wp = ws;

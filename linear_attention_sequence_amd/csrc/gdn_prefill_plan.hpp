@@ -41,10 +41,12 @@ constexpr long long lmin(long long a, long long b) { return a < b ? a : b; }
 
 // ---- segments of the carry ---------------------------------------------------------
 // Unpacked prompts whose heads leave the CUs idle run the carry in segments. Its second
-// pass runs 2 (nseg - 1) half-head workgroups per head and its first 2 nseg - 3
-// whole-head ones, each pass in one round of the CUs; a segment averages at least
+// pass runs 2 (nseg - 1) half-head workgroups per head (nseg - 1 whole-head ones when
+// the gated RMSNorm is fused into the output store: `whole`), sized to about one round
+// of the CUs, and its first 2 nseg - 3 whole-head ones; a segment averages at least
 // kMinSegChunks chunks, and nseg >= 3 (with two segments the two passes are one chain
-// cut in two).
+// cut in two). With `whole` the first pass may take two rounds: at L = 4096 eight
+// segments (first pass 416 workgroups, second 224) beat five (224 and 128) by 4 us.
 constexpr int kMaxSeg = 8;
 constexpr int kMinSegChunks = 4;
 constexpr int kLayoutCUs = 256;   // the workspace is sized for this many CUs at most
@@ -58,10 +60,10 @@ constexpr int max_chunks(int B, int L, int N, bool ragged) {
     return ragged ? chunks_of_len(L) + N : B * chunks_of_len(L);
 }
 
-constexpr int segments(int B, int L, int N, int Hv, bool ragged, int cus) {
+constexpr int segments(int B, int L, int N, int Hv, bool ragged, int cus, bool whole = false) {
     if (ragged || B != N || N <= 0 || Hv <= 0) return 1;
     const long long heads = static_cast<long long>(N) * Hv;
-    long long ks = cus / (2 * heads) + 1;
+    long long ks = cus / ((whole ? 1 : 2) * heads) + 1;
     ks = lmin(ks, kMaxSeg);
     ks = lmin(ks, chunks_of_len(L) / kMinSegChunks);
     return ks >= 3 ? static_cast<int>(ks) : 1;
@@ -87,7 +89,8 @@ struct Layout {
     int nc_max, nseg;
 };
 
-constexpr Layout layout(int B, int L, int N, int Hk, int Hv, bool ragged) {
+// `whole`: the layout of a call with the gated RMSNorm fused (its own segment count).
+constexpr Layout layout(int B, int L, int N, int Hk, int Hv, bool ragged, bool whole) {
     Layout w{};
     const size_t T = static_cast<size_t>(B) * L;
     const size_t nc = static_cast<size_t>(max_chunks(B, L, N, ragged));
@@ -102,7 +105,7 @@ constexpr Layout layout(int B, int L, int N, int Hk, int Hv, bool ragged) {
     if (ragged) {              // packed prompts: each sequence's first chunk slot, and the total
         w.n_cbase = static_cast<size_t>(N) + 1; w.cbase = off; off = align256(off + w.n_cbase * 4);
     }
-    w.nseg = segments(B, L, N, Hv, ragged, kLayoutCUs);
+    w.nseg = segments(B, L, N, Hv, ragged, kLayoutCUs, whole);
     if (w.nseg > 1) {
         const size_t tiles = static_cast<size_t>(N) * Hv * D * D;
         const size_t mid = static_cast<size_t>(w.nseg - 2);
@@ -213,7 +216,7 @@ struct CarryLaunch {
 struct CarryPlan { int nseg, count; CarryLaunch l[2]; };
 constexpr CarryPlan carry_plan(int B, int L, int N, int Hv, bool ragged, int cus, bool whole = false) {
     CarryPlan p{};
-    p.nseg = imin(segments(B, L, N, Hv, ragged, kLayoutCUs), segments(B, L, N, Hv, ragged, cus));
+    p.nseg = imin(segments(B, L, N, Hv, ragged, kLayoutCUs, whole), segments(B, L, N, Hv, ragged, cus, whole));
     const long long heads = static_cast<long long>(N) * Hv;
     if (heads <= 0) return p;
     if (p.nseg > 1) {

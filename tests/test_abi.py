@@ -169,14 +169,22 @@ def test_prefill_validation(lib):
     assert prefill(chunk=0) == SHAPE
     assert prefill(N=2) == SHAPE
     assert prefill(ws=None) == WS
-    assert prefill(ws_bytes=need - 1) == WS
+    assert prefill(ws_bytes=1) == WS
     assert prefill(ws=ctypes.c_void_p(0x7f0000000010 + 12 * 0x100000000)) == ALIGN
     assert prefill(o=A(7)) == ALIAS
     assert prefill(ws=A(8)) == ALIAS
     assert prefill(B=2, N=2, cu=A(11)) == SHAPE
-    # the bound for (B = 1, L, N = 1) serves the call either unpacked or through
-    # cu_seqlens: one byte less is refused both ways
-    assert prefill(N=1, cu=A(11), ws_bytes=need - 1) == WS
+    # the bound for (B = 1, L, N = 1) serves the call unpacked or through cu_seqlens, with or
+    # without the gated RMSNorm: it is the need of the largest of those layouts (unpacked
+    # with the norm, whose carry runs in more segments), one byte less is refused for that
+    # call and is still enough for the others
+    def fused(ws_bytes):
+        return lib.gdn_prefill_ex(p, F(z=A(13), w=A(14)), 1, 4096, A(1), A(2), A(3), A(4), A(5), A(6), A(7),
+                                  A(8), None, 1, 64, A(12), ws_bytes, None)
+    assert fused(need - 1) == WS
+    assert fused(need) != WS
+    assert prefill(ws_bytes=need - 1) != WS
+    assert prefill(N=1, cu=A(11), ws_bytes=need - 1) != WS
     assert lib.gdn_prefill_workspace_size(p, 1, 4096, 8, 64) > 0
     assert prefill(N=0, cu=A(11)) == OK
 
