@@ -193,6 +193,35 @@ def test_prefill_packed_thousands_of_sequences():
     assert np.array_equal(got["conv_out"].float().cpu().numpy(), ref["conv_out"])
 
 
+def test_prefill_packed_cost_grows_linearly_with_sequences():
+    """Eight times as many packed sequences (of 4 tokens each) cost about eight times as
+    much, not 64 times: no kernel spends time per workgroup on every sequence before its
+    own (such a scan made 4,096 sequences cost 24 times what 512 did)."""
+    shape, dtype = SMALL128, "bf16"
+    p = params(shape, dtype)
+    times = {}
+    for N in (512, 4096):
+        L = 4 * N
+        cu = dev(gi.cu_seqlens(np.full(N, 4)))
+        inp = layer_inputs(shape, 1, L, 25, dtype, N=N)
+        x, g, b, w, c0 = (dev(inp[k], dtype) for k in ("qkv", "gate", "beta", "w", "conv0"))
+        c1, S = torch.empty_like(c0), dev(inp["S0"])
+        o = torch.empty((1, L, shape.Hv, shape.dv), device="cuda")
+        ws = gdn.prefill_workspace(p, 1, L, N)
+        call = lambda: gdn.gdn_prefill(p, x, g, b, w, c0, c1, S, o, ws, cu_seqlens=cu)
+        for _ in range(2):
+            call()
+        st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        st.record()
+        for _ in range(3):
+            call()
+        en.record()
+        torch.cuda.synchronize()
+        times[N] = st.elapsed_time(en) / 3
+        _say(f"prefill, {N} packed sequences of 4 tokens: {1e3 * times[N]:.0f} us per call")
+    assert times[4096] < 16 * times[512], times
+
+
 @pytest.mark.parametrize("L,scale", [(512, 0.01), (2000, 0.01), (65536, 0.001)],
                          ids=["one_chain", "eight_segments", "long_context_L65536"])
 def test_prefill_long_memory(L, scale):
