@@ -409,11 +409,16 @@ def test_verify_commit_chain(shape, dtype, B, blocks, T):
         S, cs = S_new, c_new
 
 
-def test_gqa_mapping_probe_exact():
+@pytest.mark.parametrize("Hk,Hv,dtype", [(4, 16, "f32"), (4, 16, "bf16"), (2, 16, "bf16")],
+                         ids=["f4_fp32_path", "f4_mfma_path", "f8_mfma_path"])
+def test_gqa_mapping_probe_exact(Hk, Hv, dtype):
     """One token from a zero state, identity conv, beta = 1, gate = 0: o_h = (k.q) v_h
     with k, q from K head h // f. K head j's key makes angle theta_j with its query, so
-    round(o_h / v_h) read back as an integer must name h // f for every h, exactly."""
-    shape, dtype = gi.Shape(Hk=4, Hv=16, dk=128, dv=128), "f32"
+    round(o_h / v_h) read back as an integer must name h // f for every h, exactly. GQA
+    factors 4 and 8, through the fp32 prefill and the MFMA one (bf16 inputs: every probe
+    value is exact in bf16)."""
+    shape = gi.Shape(Hk=Hk, Hv=Hv, dk=128, dv=128)
+    _say(f"GQA probe Hk={Hk} Hv={Hv} {dtype}")
     Hk, Hv, dk, dv, K, D = shape.Hk, shape.Hv, shape.dk, shape.dv, shape.K, shape.D
     x = np.zeros((1, D, 1), np.float32)
     for j in range(Hk):
@@ -442,8 +447,9 @@ def test_gqa_mapping_probe_exact():
     # decode and verify use their own indexing: same probe through both
     o_dec = torch.empty((1, 1, Hv, dv), device="cuda")
     S = torch.zeros((1, Hv, dk, dv), device="cuda")
-    cz = torch.zeros((1, D, K - 1), device="cuda")
-    gdn.gdn_decode_step(p, dev(x), dev(inp["gate"]), dev(inp["beta"]), dev(w), cz, torch.empty_like(cz), S, o_dec)
+    cz = dev(inp["conv0"], dtype)
+    gdn.gdn_decode_step(p, dev(x, dtype), dev(inp["gate"], dtype), dev(inp["beta"], dtype), dev(w, dtype), cz,
+                        torch.empty_like(cz), S, o_dec)
     torch.cuda.synchronize()
     assert np.array_equal(head_of(o_dec[0, 0, :, 0].double().cpu().numpy() * np.sqrt(dk) / silu1),
                           np.arange(Hv) // (Hv // Hk))

@@ -19,12 +19,14 @@ D64 = gi.Shape(Hk=2, Hv=4, dk=64, dv=64, K=4)
 NOGQA128 = gi.Shape(Hk=4, Hv=4, dk=128, dv=128, K=4)
 NOGQA16 = gi.Shape(Hk=3, Hv=3, dk=16, dv=16, K=4)
 SMALL128 = gi.Shape(Hk=2, Hv=4, dk=128, dv=128, K=4)
+GQA8 = gi.Shape(Hk=2, Hv=16, dk=128, dv=128, K=4)   # eight V heads per K head
 
 # (shape, input dtype, use_qk_l2norm)
 VARIANTS = [
     (D64, "bf16", True), (D64, "f32", True), (D64, "bf16", False),
     (NOGQA128, "bf16", True), (NOGQA128, "f32", True), (NOGQA16, "f32", True),
     (SMALL128, "bf16", False), (SMALL128, "f32", False), (gi.TINY_GQA, "f32", False),
+    (GQA8, "bf16", True),
 ]
 IDS = [f"{s.Hk}x{s.Hv}_d{s.dk}_{dt}_{'l2' if l2 else 'nol2'}" for s, dt, l2 in VARIANTS]
 
@@ -121,7 +123,8 @@ def test_prefill_variant(shape, dtype, use_l2):
 
 
 @pytest.mark.parametrize("shape,dtype,use_l2", [(D64, "bf16", True), (NOGQA128, "bf16", True),
-                                                 (SMALL128, "bf16", False)], ids=["d64", "nogqa128", "nol2_128"])
+                                                 (SMALL128, "bf16", False), (GQA8, "bf16", True)],
+                         ids=["d64", "nogqa128", "nol2_128", "gqa8"])
 def test_prefill_ragged_variant(shape, dtype, use_l2):
     lens = [70, 0, 130, 1, 64]
     cu = gi.cu_seqlens(lens)
@@ -129,6 +132,20 @@ def test_prefill_ragged_variant(shape, dtype, use_l2):
     o, S, cout = _prefill(shape, dtype, use_l2, inp, cu=cu)
     ref = oracle.gdn_forward(oparams(shape, use_l2), inp["qkv"], inp["gate"], inp["beta"], inp["w"],
                              inp["conv0"], inp["S0"], cu_seqlens=cu)
+    assert rel_err(o, ref["o"]) <= TOL[dtype]
+    assert rel_err(S, ref["S"]) <= TOL[dtype]
+    assert np.array_equal(cout.float().cpu().numpy(), ref["conv_out"])
+
+
+def test_prefill_gqa8_segmented():
+    """Eight V heads per K head on the MFMA path, one 1,300-token prompt: 16 heads, so the
+    carry runs in 5 segments."""
+    shape, dtype = GQA8, "bf16"
+    print("prefill GQA 8, segmented", flush=True)
+    inp = _inputs(shape, 1, 1300, 75, dtype, True)
+    o, S, cout = _prefill(shape, dtype, True, inp)
+    ref = oracle.gdn_forward(oparams(shape, True), inp["qkv"], inp["gate"], inp["beta"], inp["w"],
+                             inp["conv0"], inp["S0"])
     assert rel_err(o, ref["o"]) <= TOL[dtype]
     assert rel_err(S, ref["S"]) <= TOL[dtype]
     assert np.array_equal(cout.float().cpu().numpy(), ref["conv_out"])
