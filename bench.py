@@ -30,7 +30,8 @@ each with its own median, spread and roofline. --no-extras skips them.
 Other workloads as the main line (--workload verify | prefill | ragged | commit
 | decode_fused | prefill_fused | ragged_fused | spec_round_copy |
 spec_round_slots | packed_short, 512 prompts of 64 tokens packed in one prefill call;
---verify-t sets the verify block width) print the same kind of JSON line.
+--verify-t sets the verify block width, --prefill-rows and --prefill-len the prompts
+of prefill and prefill_fused) print the same kind of JSON line.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
 """
@@ -484,26 +485,30 @@ def bench_prefill(args, torch, gdn, gi, ragged=False, fused=False, short=False):
         cu_np = gi.cu_seqlens(lens)
         L, N = int(cu_np[-1]), gi.RAGGED_N
     else:
-        L, N = gi.PREFILL_L, 1
+        L, N = args.prefill_len, args.prefill_rows
+    B = 1 if ragged else N   # rows of the input: one packed row, or N unpacked rows of L tokens
+    standard = ragged or (B == 1 and L == gi.PREFILL_L)
     p = gdn.GdnParams(sh.Hk, sh.Hv, sh.dk, sh.dv, sh.K, True, 1e-6, gdn.GDN_BF16)
     dev = lambda a: torch.from_numpy(a).cuda().to(torch.bfloat16)
-    reps = 1 if ragged else 4   # 64 MiB of qkv per call: 4 replicas exceed the 256 MB cache
-    xs = [dev(gi.qkv(sh, 1, L, seed + 100 * r, "bf16")) for r in range(reps)]
+    # input replicas so that the calls read qkv cold: the 64 MiB of the 4096-token prompt
+    # takes 4 to exceed the 256 MB cache; larger inputs fewer
+    reps = 1 if ragged else max(1, min(4, (512 << 20) // (B * L * sh.D * 2)))
+    xs = [dev(gi.qkv(sh, B, L, seed + 100 * r, "bf16")) for r in range(reps)]
     if fused:   # raw a/b through the prologue, gated RMSNorm epilogue with z
-        g = dev(gi.a_raw(sh, 1, L, seed, "bf16"))
-        b = dev(gi.b_raw(sh, 1, L, seed, "bf16"))
+        g = dev(gi.a_raw(sh, B, L, seed, "bf16"))
+        b = dev(gi.b_raw(sh, B, L, seed, "bf16"))
         fus = gdn.GdnFusion(dev(gi.a_log(sh, seed, "bf16")), dev(gi.dt_bias(sh, seed, "bf16")),
-                            dev(gi.z_gate(sh, 1, L, seed, "bf16")), dev(gi.norm_weight(sh, seed, "bf16")), 1e-6)
+                            dev(gi.z_gate(sh, B, L, seed, "bf16")), dev(gi.norm_weight(sh, seed, "bf16")), 1e-6)
     else:
-        g = dev(gi.gate(sh, 1, L, seed, "bf16"))
-        b = dev(gi.beta(sh, 1, L, seed, "bf16"))
+        g = dev(gi.gate(sh, B, L, seed, "bf16"))
+        b = dev(gi.beta(sh, B, L, seed, "bf16"))
     w = dev(gi.conv_weight(sh, seed, "bf16"))
     c0 = torch.zeros((N, sh.D, sh.K - 1), device="cuda", dtype=torch.bfloat16)
     c_out = torch.empty_like(c0)
     S = torch.zeros((N, sh.Hv, sh.dk, sh.dv), device="cuda")
-    o = torch.empty((1, L, sh.Hv, sh.dv), device="cuda")
+    o = torch.empty((B, L, sh.Hv, sh.dv), device="cuda")
     cu = torch.from_numpy(cu_np).cuda() if ragged else None
-    ws = gdn.prefill_workspace(p, 1, L, N)
+    ws = gdn.prefill_workspace(p, B, L, N)
 
     def step(i):
         # the state is carried in place, so each call continues from the last one's
@@ -515,11 +520,11 @@ def bench_prefill(args, torch, gdn, gi, ragged=False, fused=False, short=False):
 
     wall, per = run_timed(torch, step, args.steps, args.warmup)
     t = summary(per)
-    flops = PREFILL_FLOP_PER_TOKEN_HEAD * L * sh.Hv
+    flops = PREFILL_FLOP_PER_TOKEN_HEAD * B * L * sh.Hv
     achieved = flops / (t["median_us"] * 1e-6) / 1e12
-    nbytes = prefill_bytes(sh, L, N, fused)
+    nbytes = prefill_bytes(sh, B * L, N, fused)
     cname = ("ragged_prefill_8seqs_d128" if ragged else "prefill_L4096_d128") + ("_fused" if fused else "")
-    c = None if short else counters(cname, source_digest(PREFILL_SOURCES))
+    c = counters(cname, source_digest(PREFILL_SOURCES)) if standard and not short else None
     roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": achieved / BF16_PEAK_TFLOPS, "traffic": traffic_from_counters(c),
             "kernel": "gdn_prefill (all kernels of one call)",
@@ -528,11 +533,12 @@ def bench_prefill(args, torch, gdn, gi, ragged=False, fused=False, short=False):
     if c is not None and "mfma_busy" in c:
         roof["mfma_busy"] = c["mfma_busy"]
     return {
-        "metric": METRIC, "value": L * args.steps / wall, "unit": "tokens/s",
+        "metric": METRIC, "value": B * L * args.steps / wall, "unit": "tokens/s",
         "ms_per_step": 1e3 * wall / args.steps,
-        "config": {"workload": (f"packed prefill, {SHORT_N} sequences of {SHORT_LEN} tokens" if short else w_.name)
+        "config": {"workload": (f"packed prefill, {SHORT_N} sequences of {SHORT_LEN} tokens" if short else
+                                w_.name if standard else f"prefill_B{B}_L{L}_Hk16_Hv32_d128_chunk64")
                    + ("+gate_beta_prologue+gated_rmsnorm_epilogue" if fused else ""),
-                   "L_total": L, "N": N, "Hk": sh.Hk, "Hv": sh.Hv, "dk": sh.dk,
+                   "L_total": B * L, "N": N, "Hk": sh.Hk, "Hv": sh.Hv, "dk": sh.dk,
                    "dv": sh.dv, "chunk": 64, "cache": f"{reps} input replicas"},
         "dtype": "f32",
         "timing": t,
@@ -586,6 +592,10 @@ def main():
     ap.add_argument("--workload", default="decode", choices=sorted(DEFAULT_STEPS))
     ap.add_argument("--verify-t", type=int, default=4,
                     help="verify/commit/spec_round_*: block width T (tokens per sequence per block)")
+    ap.add_argument("--prefill-rows", type=int, default=1,
+                    help="prefill/prefill_fused: unpacked rows (prompts) per call")
+    ap.add_argument("--prefill-len", type=int, default=4096,
+                    help="prefill/prefill_fused: tokens per row")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--no-extras", dest="extras", action="store_false",
                     help="skip the ceilings and the other workloads (profiling runs)")
