@@ -499,23 +499,29 @@ __global__ __launch_bounds__(256) void commit_kernel(CommitArgs a) {
     const int h = bh - b * a.Hv;
     int acc = a.accept[b];
     acc = acc < 0 ? 0 : (acc > a.T - 1 ? a.T - 1 : acc);
-    if (a.S_out != nullptr) {   // every load in flight before the (non-temporal) stores
+    if (a.S_out != nullptr) {   // in passes of four loads, then their four (non-temporal) stores
         const f32x4* src = reinterpret_cast<const f32x4*>(
             a.S_snap + ((static_cast<size_t>(b) * a.T + acc) * a.Hv + h) * DK * DV);
         f32x4* dst = reinterpret_cast<f32x4*>(a.S_out + static_cast<size_t>(bh) * DK * DV);
         constexpr int NV = DK * DV / 4;
         constexpr int PER = NV >= 256 ? NV / 256 : 1;
         static_assert(NV < 256 || NV % 256 == 0, "tile must split evenly over the workgroup");
-        f32x4 r[PER];
+        // (all 16 loads of a thread before any store: 2% slower on the 128 x 32 tiles of
+        // 64 KB, whose copy then holds 64 registers; passes of 2 or 8 lie in between)
+        constexpr int Q = PER < 4 ? PER : 4;
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int e = threadIdx.x + 256 * i;
-            if (e < NV) r[i] = src[e];
-        }
+        for (int i0 = 0; i0 < PER; i0 += Q) {
+            f32x4 r[Q];
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int e = threadIdx.x + 256 * i;
-            if (e < NV) __builtin_nontemporal_store(r[i], dst + e);
+            for (int i = 0; i < Q; ++i) {
+                const int e = threadIdx.x + 256 * (i0 + i);
+                if (e < NV) r[i] = src[e];
+            }
+#pragma unroll
+            for (int i = 0; i < Q; ++i) {
+                const int e = threadIdx.x + 256 * (i0 + i);
+                if (e < NV) __builtin_nontemporal_store(r[i], dst + e);
+            }
         }
     }
 
