@@ -609,7 +609,7 @@ __global__ __launch_bounds__(256, 4) void chunk_kernel(PrefillArgs a, Ws ws) {
     const int cv0 = 2 * a.Hk * D + h * D;                 // first channel of this V head
     const int pc = seg.start + c * C;                      // row position of the chunk's first token
     const uint16_t* xr = reinterpret_cast<const uint16_t*>(a.qkv) + static_cast<size_t>(seg.row) * a.D * a.L;
-    const bool vfast = c > 0 && nt == C && pc + C + 1 <= a.L && (reinterpret_cast<uintptr_t>(a.qkv) & 3) == 0;
+    const bool vfast = plan::value_fast(c, nt, pc, a.L) && (reinterpret_cast<uintptr_t>(a.qkv) & 3) == 0;
     u32x4a4 vlo[4];
     u32x2a4 vhi[4];
     uint2 wraw[4];                                         // conv taps of the item's channel

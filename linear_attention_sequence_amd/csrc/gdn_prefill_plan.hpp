@@ -39,6 +39,17 @@ static_assert(kidx(kpos(45)) == 45 && kpos(kidx(45)) == 45 && kpos(16) == 4 && k
 constexpr int imin(int a, int b) { return a < b ? a : b; }
 constexpr long long lmin(long long a, long long b) { return a < b ? a : b; }
 
+// ---- raw value loads of the chunk kernel --------------------------------------------
+// A chunk (not a sequence's first) whose C tokens are all present takes its values' 12 raw
+// positions per item in two vector loads, from p - 4 + par (p = the item's first token, par
+// = the parity of the item's element offset ch L + p - 4 inside the row, so that the loads
+// start on a 4-byte boundary); the loads then reach position pc + C - 1 + par of the
+// channel's row. With an even row length L the parity is that of the chunk's first
+// position pc for every channel; with an odd one it can be either.
+constexpr int value_load_parity_max(int L, int pc) { return (L & 1) != 0 ? 1 : (pc & 1); }
+constexpr bool value_fast(int c, int nt, int pc, int L) {
+    return c > 0 && nt == C && pc + C + value_load_parity_max(L, pc) <= L;
+}
 // ---- segments of the carry ---------------------------------------------------------
 // Unpacked prompts whose heads leave the CUs idle run the carry in segments. Its second
 // pass runs 2 (nseg - 1) half-head workgroups per head (nseg - 1 whole-head ones when

@@ -348,11 +348,13 @@ void check_value_loads(const Config& c) {
         for (int cc = 0; cc < nch; ++cc) {
             const int nt = imin(C, c.lens[n] - cc * C), pc = c.starts[n] + cc * C;
             REQUIRE(nt >= 1 && pc + nt <= c.L);
-            const bool vfast = cc > 0 && nt == C && pc + C + 1 <= c.L;
+            const bool vfast = value_fast(cc, nt, pc, c.L);
             for (int g8 = 0; g8 < 8; ++g8) {
                 const int p = pc + 8 * g8;
                 if (vfast) {
-                    for (int parity = 0; parity < 2; ++parity) {   // of (channel row offset + p - 4)
+                    for (int ch = 0; ch < 2; ++ch) {               // parities of (ch L + p - 4) over the channels
+                        const int parity = (ch * c.L + p - 4) & 1;
+                        REQUIRE(parity <= value_load_parity_max(c.L, pc));
                         const int q0 = p - 4 + parity;             // the loads start on a 4-byte boundary
                         REQUIRE(q0 >= 0 && q0 + 12 <= c.L);        // inside the channel's row
                         REQUIRE(q0 <= p - 3 && p + 8 <= q0 + 12);  // the windows of tokens p .. p + 7
