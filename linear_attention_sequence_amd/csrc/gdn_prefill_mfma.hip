@@ -195,12 +195,13 @@ __global__ __launch_bounds__(256) void front_kernel(PrefillArgs a, Ws ws) {
     // carry kernels
     if (a.cu != nullptr && blockIdx.x == 0) write_chunk_bases(a.N, a.L, a.cu, C, ws.nc_max, ws.cbase);
 
-    // Interior tiles of unpacked bf16 rows whose length is a multiple of 8 (so that every
-    // 8-token group is 16-byte aligned): each lane loads 8 tokens of a channel and the 4
-    // tokens before them in two vector loads and runs the conv in registers. Every window
-    // lies inside the row and no sequence ends in the tile, so there is no masking and no
-    // conv-state update.
-    const bool vec = sizeof(Tin) == 2 && a.cu == nullptr && a.L % 8 == 0 && p0 > 0 && p0 + TT < a.L &&
+    // Tiles after the first of unpacked bf16 rows whose length is a multiple of 8 (so that
+    // every 8-token group is 16-byte aligned): each lane loads 8 tokens of a channel and the
+    // 4 tokens before them in two vector loads and runs the conv in registers. Every window
+    // lies inside the row, so there is no masking; in the row's last tile (whose 32 tokens
+    // end the sequence) the lanes of the last 8 tokens also write the conv state, those
+    // tokens' last K - 1 raw inputs.
+    const bool vec = sizeof(Tin) == 2 && a.cu == nullptr && a.L % 8 == 0 && p0 > 0 && p0 + TT <= a.L &&
                      (reinterpret_cast<uintptr_t>(a.qkv) & 15) == 0 && (reinterpret_cast<uintptr_t>(a.w) & 7) == 0;
     if (vec) {
         static_assert(TT == 32 && D == 128, "4 lanes of 8 tokens per channel, 16 channels per instruction");
@@ -216,6 +217,17 @@ __global__ __launch_bounds__(256) void front_kernel(PrefillArgs a, Ws ws) {
             xr[i] = *reinterpret_cast<const uint4*>(xp);
             hr[i] = *reinterpret_cast<const uint2*>(xp - 4);
             wr[i] = *reinterpret_cast<const uint2*>(wb + static_cast<size_t>(ch0 + cc) * kConvK);
+        }
+        static_assert(kConvK == 4, "the conv state is tokens 5, 6 and 7 of the last 8-token group");
+        if (p0 + TT == a.L && g == 3) {   // sequence `row` ends at the tile's last token
+            uint16_t* co = static_cast<uint16_t*>(a.conv_out);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const size_t cb = (static_cast<size_t>(row) * a.D + ch0 + (wave * 2 + i) * 16 + lq) * (kConvK - 1);
+                co[cb + 0] = static_cast<uint16_t>(xr[i].z >> 16);
+                co[cb + 1] = static_cast<uint16_t>(xr[i].w & 0xffffu);
+                co[cb + 2] = static_cast<uint16_t>(xr[i].w >> 16);
+            }
         }
         const auto lo = [](unsigned v) { return __uint_as_float(v << 16); };
         const auto hi = [](unsigned v) { return __uint_as_float(v & 0xffff0000u); };
